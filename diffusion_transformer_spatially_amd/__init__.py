@@ -1,0 +1,248 @@
+"""Python binding of libsafe_attn (the spatially-adaptive DiT attention step on MI355X / gfx950).
+
+Argument marshalling only: torch tensors supply device pointers, shapes and the current HIP stream;
+every step of the computation runs in the library's HIP kernels.  Each function has the name and
+meaning of the C entry point it calls (see include/safe_attn.h).  There is no CPU fallback: if the
+library is not built, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsafe_attn.so")
+
+SAFE_DTYPE_BF16, SAFE_DTYPE_F32, SAFE_DTYPE_BOOL = 0, 1, 2
+SAFE_MAX_BATCH = 64
+EXPORTS = ("safe_attn_dense", "safe_attn_rows", "safe_mask_is_row_constant", "safe_pcsp_accumulate",
+           "safe_pcsp_partition", "safe_swcfg_combine", "safe_gather_rows", "safe_scatter_rows",
+           "safe_status_string", "safe_version")
+
+
+class SafeAttnError(RuntimeError):
+    def __init__(self, code: int, name: str, call: str):
+        super().__init__(f"{call} failed: {name} ({code})")
+        self.code = code
+        self.name = name
+
+
+class safe_attn_desc(ctypes.Structure):
+    _fields_ = [
+        ("dtype", ctypes.c_int32), ("B", ctypes.c_int32), ("H", ctypes.c_int32), ("N", ctypes.c_int32),
+        ("T", ctypes.c_int32), ("d", ctypes.c_int32),
+        ("q", ctypes.c_void_p), ("k_img", ctypes.c_void_p), ("v_img", ctypes.c_void_p),
+        ("k_txt", ctypes.c_void_p), ("v_txt", ctypes.c_void_p),
+        ("text_valid_len", ctypes.POINTER(ctypes.c_int32)),
+        ("scale", ctypes.c_float),
+        ("mask", ctypes.c_void_p), ("mask_dtype", ctypes.c_int32), ("mask_B", ctypes.c_int32),
+        ("mask_H", ctypes.c_int32), ("mask_cols", ctypes.c_int32),
+        ("out", ctypes.c_void_p), ("lse", ctypes.c_void_p), ("xattn_out", ctypes.c_void_p),
+        ("lse_img_out", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+
+
+def load(path: Optional[str] = None):
+    """Load the built library (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} is missing: build it with __graft_entry__.build() "
+                           "(python diffusion_transformer_spatially_amd/build.py)")
+    lib = ctypes.CDLL(p)
+    vp, i32, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
+    P = ctypes.POINTER
+    lib.safe_attn_dense.argtypes = [P(safe_attn_desc), vp]
+    lib.safe_attn_rows.argtypes = [P(safe_attn_desc), vp, i32, vp]
+    lib.safe_mask_is_row_constant.argtypes = [vp, i32, i32, i32, i32, i32, i32, P(i32), i32, vp, P(i32), vp, vp]
+    lib.safe_pcsp_accumulate.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, vp, i32, vp]
+    lib.safe_pcsp_partition.argtypes = [vp, i32, i32, vp, vp, vp, vp, vp]
+    lib.safe_swcfg_combine.argtypes = [vp, vp, i32, i32, i32, i32, f32, f32, vp, vp]
+    lib.safe_gather_rows.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, vp, vp]
+    lib.safe_scatter_rows.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, vp, vp]
+    for name in EXPORTS[:-2]:
+        getattr(lib, name).restype = i32
+    lib.safe_status_string.argtypes = [i32]
+    lib.safe_status_string.restype = ctypes.c_char_p
+    lib.safe_version.argtypes = []
+    lib.safe_version.restype = i32
+    _lib = lib
+    return lib
+
+
+def _check(code: int, call: str):
+    if code != 0:
+        raise SafeAttnError(code, load().safe_status_string(code).decode(), call)
+
+
+# ----------------------------------------------------------------------------- marshalling helpers
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a torch tensor")
+    if not t.is_cuda:
+        raise ValueError("tensor must live in GPU memory")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return SAFE_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return SAFE_DTYPE_F32
+    if t.dtype == torch.bool:
+        return SAFE_DTYPE_BOOL
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def _desc(q, k_img, v_img, k_txt, v_txt, text_valid_len: Sequence[int], out, scale, mask, lse, xattn_out,
+          lse_img_out):
+    B, H, N, d = q.shape
+    T = k_txt.shape[2] if k_txt is not None else 0
+    tv = (ctypes.c_int32 * max(1, len(text_valid_len)))(*[int(x) for x in text_valid_len])
+    if len(text_valid_len) != B:
+        raise ValueError("text_valid_len needs one entry per batch element")
+    for t in (k_img, v_img, out):
+        if tuple(t.shape) != (B, H, N, d) or t.dtype != q.dtype:
+            raise ValueError("q, k_img, v_img and out must share shape [B,H,N,d] and dtype")
+    if k_txt is not None and (tuple(k_txt.shape) != (B, H, T, d) or tuple(v_txt.shape) != (B, H, T, d)):
+        raise ValueError("k_txt and v_txt must be [B,H,T,d]")
+    D = safe_attn_desc()
+    D.dtype = _dtype_code(q)
+    D.B, D.H, D.N, D.T, D.d = B, H, N, T, d
+    D.q, D.k_img, D.v_img = _ptr(q), _ptr(k_img), _ptr(v_img)
+    D.k_txt, D.v_txt = _ptr(k_txt), _ptr(v_txt)
+    D.text_valid_len = ctypes.cast(tv, ctypes.POINTER(ctypes.c_int32))
+    D.scale = float(scale)
+    if mask is not None:
+        if mask.dim() != 4 or mask.shape[2] != N:
+            raise ValueError("mask must be [mask_B, mask_H, N, mask_cols]")
+        D.mask = _ptr(mask)
+        D.mask_dtype = _dtype_code(mask)
+        D.mask_B, D.mask_H, D.mask_cols = mask.shape[0], mask.shape[1], mask.shape[3]
+    D.out = _ptr(out)
+    D.lse = _ptr(lse)
+    D.xattn_out = _ptr(xattn_out)
+    D.lse_img_out = _ptr(lse_img_out)
+    return D, tv
+
+
+# ----------------------------------------------------------------------------- entry points
+def safe_attn_dense(q, k_img, v_img, k_txt, v_txt, text_valid_len, out, scale=0.0, mask=None, lse=None,
+                    xattn_out=None, lse_img_out=None, stream=None):
+    """Dense anchor step: all N image rows of `out` (safe_attn_dense)."""
+    D, _keep = _desc(q, k_img, v_img, k_txt, v_txt, text_valid_len, out, scale, mask, lse, xattn_out, lse_img_out)
+    _check(load().safe_attn_dense(ctypes.byref(D), _stream(stream)), "safe_attn_dense")
+    return out
+
+
+def safe_attn_rows(q, k_img, v_img, k_txt, v_txt, text_valid_len, rows, out, scale=0.0, mask=None, lse=None,
+                   xattn_out=None, lse_img_out=None, stream=None):
+    """Sensitive-row step: rows[] of `out` only, against the global keys (safe_attn_rows)."""
+    torch = _torch()
+    if rows.dtype != torch.int32 or rows.dim() != 1:
+        raise ValueError("rows must be a 1-D int32 tensor")
+    D, _keep = _desc(q, k_img, v_img, k_txt, v_txt, text_valid_len, out, scale, mask, lse, xattn_out, lse_img_out)
+    _check(load().safe_attn_rows(ctypes.byref(D), _ptr(rows), rows.numel(), _stream(stream)), "safe_attn_rows")
+    return out
+
+
+def safe_mask_is_row_constant(mask, N: int, T: int, text_valid_len, flag_ws, c_out=None, stream=None) -> bool:
+    """Exact elision check; synchronous (safe_mask_is_row_constant)."""
+    if mask.dim() != 4:
+        raise ValueError("mask must be [mask_B, mask_H, N, mask_cols]")
+    B = len(text_valid_len)
+    tv = (ctypes.c_int32 * B)(*[int(x) for x in text_valid_len])
+    res = ctypes.c_int32(0)
+    _check(load().safe_mask_is_row_constant(
+        _ptr(mask), _dtype_code(mask), mask.shape[0], mask.shape[1], N, mask.shape[3], T,
+        ctypes.cast(tv, ctypes.POINTER(ctypes.c_int32)), B, _ptr(flag_ws), ctypes.byref(res), _ptr(c_out),
+        _stream(stream)), "safe_mask_is_row_constant")
+    return bool(res.value)
+
+
+def safe_pcsp_accumulate(x, lse_img, Tv: int, c0: int, c1: int, scores, accumulate: bool, stream=None):
+    """scores (+)= per-token text-content attention mass summed over heads (safe_pcsp_accumulate)."""
+    H, N, T = x.shape
+    _check(load().safe_pcsp_accumulate(_ptr(x), _ptr(lse_img), H, N, T, Tv, c0, c1, _ptr(scores),
+                                       1 if accumulate else 0, _stream(stream)), "safe_pcsp_accumulate")
+    return scores
+
+
+def safe_pcsp_partition(scores, k: int, S, C, is_sens, s01=None, stream=None):
+    """Exact top-k partition of the scores (safe_pcsp_partition)."""
+    N = scores.numel()
+    _check(load().safe_pcsp_partition(_ptr(scores), N, k, _ptr(S), _ptr(C), _ptr(is_sens), _ptr(s01),
+                                      _stream(stream)), "safe_pcsp_partition")
+
+
+def safe_swcfg_combine(eps, s, side: int, g_ctx: float, g_sens: float, out, stream=None):
+    """Per-token guidance combine (safe_swcfg_combine)."""
+    _, C, Hl, Wl = eps.shape
+    _check(load().safe_swcfg_combine(_ptr(eps), _ptr(s), C, Hl, Wl, side, float(g_ctx), float(g_sens), _ptr(out),
+                                     _stream(stream)), "safe_swcfg_combine")
+    return out
+
+
+def safe_gather_rows(state, rows, packed, stream=None):
+    B, H, N, d = state.shape
+    _check(load().safe_gather_rows(_ptr(state), _ptr(rows), rows.numel(), B, H, N, d, _dtype_code(state),
+                                   _ptr(packed), _stream(stream)), "safe_gather_rows")
+    return packed
+
+
+def safe_scatter_rows(packed, rows, state, stream=None):
+    B, H, N, d = state.shape
+    _check(load().safe_scatter_rows(_ptr(packed), _ptr(rows), rows.numel(), B, H, N, d, _dtype_code(state),
+                                    _ptr(state), _stream(stream)), "safe_scatter_rows")
+    return state
+
+
+def safe_version() -> int:
+    return load().safe_version()
+
+
+# ----------------------------------------------------------------------------- elide-or-keep helper
+class MaskPolicy:
+    """Checks a supplied mask once (per tensor version) and drops it when it is provably redundant.
+
+    Mirrors the exact fast-path rewrite: a removable mask goes to the mask-free kernels, any other mask
+    is kept and applied exactly.
+    """
+
+    def __init__(self):
+        self._cache = {}
+        self._flag = None
+
+    def elide(self, mask, N: int, T: int, text_valid_len):
+        if mask is None:
+            return None
+        torch = _torch()
+        key = (mask.data_ptr(), mask._version, tuple(mask.shape), mask.dtype, tuple(int(t) for t in text_valid_len))
+        if key not in self._cache:
+            if self._flag is None or self._flag.device != mask.device:
+                self._flag = torch.empty(1, dtype=torch.int32, device=mask.device)
+            self._cache[key] = safe_mask_is_row_constant(mask, N, T, text_valid_len, self._flag)
+        return None if self._cache[key] else mask

@@ -1,0 +1,55 @@
+"""Build libsafe_attn.so (gfx950) in-tree with hipcc.
+
+Every HIP source under csrc/ is compiled to an object in _build/ (in parallel) and linked into
+diffusion_transformer_spatially_amd/libsafe_attn.so.  Packed fp32 VALU forms are disabled for the
+device code; the host pass warns that it does not know that target feature, which is harmless.
+"""
+from __future__ import annotations
+
+import concurrent.futures as cf
+import glob
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD = os.path.join(ROOT, "_build")
+LIB = os.path.join(PKG, "libsafe_attn.so")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+
+CFLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", f"-I{INCLUDE}", f"-I{CSRC}",
+          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wno-unused-command-line-argument"]
+
+
+def _run(cmd):
+    p = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    out = "\n".join(l for l in p.stdout.splitlines() if "not a recognized feature" not in l)
+    if p.returncode != 0:
+        raise RuntimeError(f"command failed ({p.returncode}): {' '.join(cmd)}\n{out}")
+    return out
+
+
+def build(verbose: bool = False, jobs: int = 8) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    sources = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    if not sources:
+        raise RuntimeError("no HIP sources found")
+    objs = [os.path.join(BUILD, os.path.basename(s)[:-4] + ".o") for s in sources]
+    with cf.ThreadPoolExecutor(max_workers=min(jobs, len(sources))) as ex:
+        futs = [ex.submit(_run, [HIPCC, *CFLAGS, "-c", s, "-o", o]) for s, o in zip(sources, objs)]
+        for f in futs:
+            out = f.result()
+            if verbose and out.strip():
+                print(out)
+    tmp = LIB + ".tmp"
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,196 @@
+// C ABI entry points: argument validation, dispatch to the gfx950 kernels, status mapping.
+// No allocation, no retained pointers; every launch goes to the caller's stream.
+#include <cmath>
+#include <cstring>
+
+#include "common.hpp"
+
+using namespace safe;
+
+namespace {
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+safe_status from_hip(hipError_t e) { return e == hipSuccess ? SAFE_OK : SAFE_ERR_HIP; }
+
+safe_status check_attn(const safe_attn_desc* d) {
+  if (d == nullptr) return SAFE_ERR_NULL;
+  if (d->dtype != SAFE_DTYPE_BF16 && d->dtype != SAFE_DTYPE_F32) return SAFE_ERR_DTYPE;
+  if (d->B < 1 || d->H < 1 || d->N < 1 || d->T < 0 || d->d < 1) return SAFE_ERR_SHAPE;
+  if (d->B > SAFE_MAX_BATCH) return SAFE_ERR_UNSUPPORTED;
+  if (d->d != 64) return SAFE_ERR_UNSUPPORTED;
+  if (d->q == nullptr || d->k_img == nullptr || d->v_img == nullptr || d->out == nullptr ||
+      d->text_valid_len == nullptr)
+    return SAFE_ERR_NULL;
+  int tmax = 0;
+  for (int b = 0; b < d->B; ++b) {
+    const int t = d->text_valid_len[b];
+    if (t < 0 || t > d->T) return SAFE_ERR_RANGE;
+    tmax = t > tmax ? t : tmax;
+  }
+  if (tmax > 0 && (d->k_txt == nullptr || d->v_txt == nullptr)) return SAFE_ERR_NULL;
+  if (!aligned16(d->q) || !aligned16(d->k_img) || !aligned16(d->v_img) || !aligned16(d->out)) return SAFE_ERR_ALIGN;
+  if (tmax > 0 && (!aligned16(d->k_txt) || !aligned16(d->v_txt))) return SAFE_ERR_ALIGN;
+  if (!std::isfinite(d->scale)) return SAFE_ERR_RANGE;
+  // 32-bit grid and index limits of the kernels
+  const double elems = static_cast<double>(d->B) * d->H * (static_cast<double>(d->N) + d->T) * d->d;
+  if (elems > 4.0e12) return SAFE_ERR_SHAPE;
+  if (d->mask != nullptr) {
+    if (d->mask_dtype != SAFE_DTYPE_F32 && d->mask_dtype != SAFE_DTYPE_BOOL) return SAFE_ERR_DTYPE;
+    if (!(d->mask_B == 1 || d->mask_B == d->B) || !(d->mask_H == 1 || d->mask_H == d->H)) return SAFE_ERR_SHAPE;
+    if (!(d->mask_cols == d->N || d->mask_cols == d->N + d->T)) return SAFE_ERR_SHAPE;
+    if (d->mask_dtype == SAFE_DTYPE_F32 && (reinterpret_cast<uintptr_t>(d->mask) & 3u) != 0) return SAFE_ERR_ALIGN;
+  }
+  return SAFE_OK;
+}
+
+AttnArgs make_args(const safe_attn_desc* d, const int32_t* rows, int R) {
+  AttnArgs a;
+  std::memset(&a, 0, sizeof a);
+  a.q = d->q;
+  a.k_img = d->k_img;
+  a.v_img = d->v_img;
+  a.k_txt = d->k_txt;
+  a.v_txt = d->v_txt;
+  a.out = d->out;
+  a.lse = d->lse;
+  a.xattn_out = d->xattn_out;
+  a.lse_img_out = d->lse_img_out;
+  a.rows = rows;
+  a.mask = d->mask;
+  a.mask_dtype = d->mask_dtype;
+  a.mask_B = d->mask_B;
+  a.mask_H = d->mask_H;
+  a.mask_cols = d->mask_cols;
+  a.B = d->B;
+  a.H = d->H;
+  a.N = d->N;
+  a.T = d->T;
+  a.R = R;
+  a.scale = d->scale == 0.f ? 1.0f / std::sqrt(static_cast<float>(d->d)) : d->scale;
+  for (int b = 0; b < d->B; ++b) a.tv[b] = d->text_valid_len[b];
+  return a;
+}
+
+safe_status run_attn(const safe_attn_desc* d, const int32_t* rows, int R, hipStream_t s) {
+  const AttnArgs a = make_args(d, rows, R);
+  if (R == 0) return SAFE_OK;
+  if (d->dtype == SAFE_DTYPE_BF16 && d->mask == nullptr) return from_hip(launch_attn_mfma_bf16(a, s));
+  return from_hip(launch_attn_generic(a, d->dtype, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+safe_status safe_attn_dense(const safe_attn_desc* desc, hipStream_t stream) {
+  const safe_status st = check_attn(desc);
+  if (st != SAFE_OK) return st;
+  return run_attn(desc, nullptr, desc->N, stream);
+}
+
+safe_status safe_attn_rows(const safe_attn_desc* desc, const int32_t* rows, int32_t k, hipStream_t stream) {
+  const safe_status st = check_attn(desc);
+  if (st != SAFE_OK) return st;
+  if (k < 0 || k > desc->N) return SAFE_ERR_RANGE;
+  if (k == 0) return SAFE_OK;
+  if (rows == nullptr) return SAFE_ERR_NULL;
+  return run_attn(desc, rows, k, stream);
+}
+
+safe_status safe_mask_is_row_constant(const void* mask, int32_t mask_dtype, int32_t mask_B, int32_t mask_H, int32_t N,
+                                      int32_t mask_cols, int32_t T, const int32_t* text_valid_len, int32_t B,
+                                      int32_t* flag_ws, int32_t* is_const, float* c_out, hipStream_t stream) {
+  if (mask == nullptr || text_valid_len == nullptr || flag_ws == nullptr || is_const == nullptr) return SAFE_ERR_NULL;
+  if (mask_dtype != SAFE_DTYPE_F32 && mask_dtype != SAFE_DTYPE_BOOL) return SAFE_ERR_DTYPE;
+  if (B < 1 || B > SAFE_MAX_BATCH || N < 1 || T < 0 || mask_H < 1) return SAFE_ERR_SHAPE;
+  if (!(mask_B == 1 || mask_B == B)) return SAFE_ERR_SHAPE;
+  if (!(mask_cols == N || mask_cols == N + T)) return SAFE_ERR_SHAPE;
+  for (int b = 0; b < B; ++b)
+    if (text_valid_len[b] < 0 || text_valid_len[b] > T) return SAFE_ERR_RANGE;
+  if (static_cast<double>(mask_H) * N > 2.0e9) return SAFE_ERR_SHAPE;
+  if (mask_dtype == SAFE_DTYPE_F32 && (reinterpret_cast<uintptr_t>(mask) & 3u) != 0) return SAFE_ERR_ALIGN;
+  if ((reinterpret_cast<uintptr_t>(flag_ws) & 3u) != 0) return SAFE_ERR_ALIGN;
+  hipError_t e = launch_mask_check(mask, mask_dtype, mask_B, mask_H, N, mask_cols, T, text_valid_len, B, flag_ws,
+                                   c_out, stream);
+  if (e != hipSuccess) return SAFE_ERR_HIP;
+  int32_t h = 0;
+  e = hipMemcpyAsync(&h, flag_ws, sizeof h, hipMemcpyDeviceToHost, stream);
+  if (e != hipSuccess) return SAFE_ERR_HIP;
+  e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return SAFE_ERR_HIP;
+  *is_const = h ? 1 : 0;
+  return SAFE_OK;
+}
+
+safe_status safe_pcsp_accumulate(const float* x, const float* lse_img, int32_t H, int32_t N, int32_t T, int32_t Tv,
+                                 int32_t c0, int32_t c1, float* scores, int32_t accumulate, hipStream_t stream) {
+  if (x == nullptr || scores == nullptr) return SAFE_ERR_NULL;
+  if (H < 1 || N < 1 || T < 1) return SAFE_ERR_SHAPE;
+  if (Tv < 0 || Tv > T || c0 < 0 || c0 > c1 || c1 > Tv) return SAFE_ERR_RANGE;
+  if (static_cast<double>(H) * 4 > 48.0 * 1024) return SAFE_ERR_UNSUPPORTED;  // LDS per workgroup
+  if ((reinterpret_cast<uintptr_t>(x) & 3u) != 0) return SAFE_ERR_ALIGN;
+  return from_hip(launch_pcsp_accumulate(x, lse_img, H, N, T, Tv, c0, c1, scores, accumulate, stream));
+}
+
+safe_status safe_pcsp_partition(const float* scores, int32_t N, int32_t k, int32_t* S, int32_t* C, uint8_t* is_sens,
+                                float* s01, hipStream_t stream) {
+  if (scores == nullptr || is_sens == nullptr) return SAFE_ERR_NULL;
+  if (N < 1 || N > (1 << 24)) return SAFE_ERR_SHAPE;
+  if (k < 0 || k > N) return SAFE_ERR_RANGE;
+  if ((k > 0 && S == nullptr) || (k < N && C == nullptr)) return SAFE_ERR_NULL;
+  return from_hip(launch_pcsp_partition(scores, N, k, S, C, is_sens, s01, stream));
+}
+
+safe_status safe_swcfg_combine(const float* eps, const float* s, int32_t C, int32_t Hl, int32_t Wl, int32_t side,
+                               float g_ctx, float g_sens, float* out, hipStream_t stream) {
+  if (eps == nullptr || s == nullptr || out == nullptr) return SAFE_ERR_NULL;
+  if (C < 1 || Hl < 1 || Wl < 1 || side < 1) return SAFE_ERR_SHAPE;
+  if (Hl % side != 0 || Wl % side != 0) return SAFE_ERR_SHAPE;
+  if (static_cast<double>(C) * Hl * Wl * 2 > 2.0e9) return SAFE_ERR_SHAPE;
+  return from_hip(launch_swcfg(eps, s, C, Hl, Wl, side, g_ctx, g_sens, out, stream));
+}
+
+static safe_status rows_copy(const void* src, const int32_t* rows, int32_t k, int32_t B, int32_t H, int32_t N,
+                             int32_t d, int32_t dtype, void* dst, bool scatter, hipStream_t stream) {
+  if (dtype != SAFE_DTYPE_BF16 && dtype != SAFE_DTYPE_F32) return SAFE_ERR_DTYPE;
+  if (B < 1 || H < 1 || N < 1 || d < 1) return SAFE_ERR_SHAPE;
+  if (k < 0 || k > N) return SAFE_ERR_RANGE;
+  if (k == 0) return SAFE_OK;
+  if (src == nullptr || dst == nullptr || rows == nullptr) return SAFE_ERR_NULL;
+  const int esize = dtype == SAFE_DTYPE_BF16 ? 2 : 4;
+  const int row_bytes = d * esize;
+  if (row_bytes % 16 != 0) return SAFE_ERR_UNSUPPORTED;
+  if (!aligned16(src) || !aligned16(dst)) return SAFE_ERR_ALIGN;
+  if (static_cast<double>(B) * H * k * (row_bytes / 16) > 4.0e9) return SAFE_ERR_SHAPE;
+  return from_hip(launch_rows_copy(src, dst, rows, k, B, H, N, row_bytes, scatter, stream));
+}
+
+safe_status safe_gather_rows(const void* state, const int32_t* rows, int32_t k, int32_t B, int32_t H, int32_t N,
+                             int32_t d, int32_t dtype, void* packed, hipStream_t stream) {
+  return rows_copy(state, rows, k, B, H, N, d, dtype, packed, false, stream);
+}
+
+safe_status safe_scatter_rows(const void* packed, const int32_t* rows, int32_t k, int32_t B, int32_t H, int32_t N,
+                              int32_t d, int32_t dtype, void* state, hipStream_t stream) {
+  return rows_copy(packed, rows, k, B, H, N, d, dtype, state, true, stream);
+}
+
+const char* safe_status_string(safe_status s) {
+  switch (s) {
+    case SAFE_OK: return "SAFE_OK";
+    case SAFE_ERR_NULL: return "SAFE_ERR_NULL";
+    case SAFE_ERR_SHAPE: return "SAFE_ERR_SHAPE";
+    case SAFE_ERR_DTYPE: return "SAFE_ERR_DTYPE";
+    case SAFE_ERR_RANGE: return "SAFE_ERR_RANGE";
+    case SAFE_ERR_WORKSPACE: return "SAFE_ERR_WORKSPACE";
+    case SAFE_ERR_UNSUPPORTED: return "SAFE_ERR_UNSUPPORTED";
+    case SAFE_ERR_HIP: return "SAFE_ERR_HIP";
+    case SAFE_ERR_ALIGN: return "SAFE_ERR_ALIGN";
+    default: return "SAFE_ERR_UNKNOWN";
+  }
+}
+
+int32_t safe_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,151 @@
+// General attention kernel on the vector ALUs: fp32 or bf16 storage, dense or sensitive rows,
+// optional kept additive mask (fp32 or bool), optional warmup emission.  It serves the fp32 path and
+// every kept-mask call; the mask-free bf16 hot path runs on the MFMA kernel instead.
+//
+// Semantics (SAFE-DiT technical summary, Methodology 1 and 3): one joint softmax per image query row
+// over the image keys then the valid text keys (padded text slots never enter), logits scaled by
+// `scale`, kept mask added; a fully masked row yields 0 and lse = -inf.
+//
+// Layout: one thread per query row (q and the 64 output accumulators in registers), 256 rows per
+// workgroup; 32-key tiles of K and V are staged in LDS as fp32 and read as broadcasts.
+#include "common.hpp"
+
+namespace safe {
+
+constexpr int kGenThreads = 256;
+constexpr int kGenD = 64;
+constexpr int kGenTile = 32;
+
+template <typename T>
+__device__ __forceinline__ float ld(const T* p, size_t i);
+template <>
+__device__ __forceinline__ float ld<float>(const float* p, size_t i) { return p[i]; }
+template <>
+__device__ __forceinline__ float ld<uint16_t>(const uint16_t* p, size_t i) { return bf16_to_f32(p[i]); }
+
+template <typename T>
+__device__ __forceinline__ void st(T* p, size_t i, float v);
+template <>
+__device__ __forceinline__ void st<float>(float* p, size_t i, float v) { p[i] = v; }
+template <>
+__device__ __forceinline__ void st<uint16_t>(uint16_t* p, size_t i, float v) { p[i] = f32_to_bf16_rne(v); }
+
+template <typename T, bool HAS_MASK>
+__global__ __launch_bounds__(kGenThreads) void k_attn_generic(AttnArgs a) {
+  __shared__ float ks[kGenTile][kGenD];
+  __shared__ float vs[kGenTile][kGenD];
+  const int nqb = (a.R + kGenThreads - 1) / kGenThreads;
+  const int bh = blockIdx.x / nqb;
+  const int qb = blockIdx.x - bh * nqb;
+  const int b = bh / a.H, h = bh - b * a.H;
+  const int r = qb * kGenThreads + threadIdx.x;
+  const bool active = r < a.R;
+  int row = active ? (a.rows ? a.rows[r] : r) : 0;
+  const bool valid_row = active && row >= 0 && row < a.N;
+  if (!valid_row) row = 0;
+  const int tv = a.tv[b];
+  const T* Q = static_cast<const T*>(a.q) + static_cast<size_t>(bh) * a.N * kGenD;
+  const T* KI = static_cast<const T*>(a.k_img) + static_cast<size_t>(bh) * a.N * kGenD;
+  const T* VI = static_cast<const T*>(a.v_img) + static_cast<size_t>(bh) * a.N * kGenD;
+  const T* KT = static_cast<const T*>(a.k_txt) + static_cast<size_t>(bh) * a.T * kGenD;
+  const T* VT = static_cast<const T*>(a.v_txt) + static_cast<size_t>(bh) * a.T * kGenD;
+
+  float q[kGenD], o[kGenD];
+#pragma unroll
+  for (int c = 0; c < kGenD; ++c) {
+    q[c] = ld(Q, static_cast<size_t>(row) * kGenD + c);
+    o[c] = 0.f;
+  }
+  // mask row pointer (fp32 entries or bool bytes)
+  const uint8_t* mrow = nullptr;
+  if (HAS_MASK) {
+    const int mb = a.mask_B == 1 ? 0 : b, mh = a.mask_H == 1 ? 0 : h;
+    const int esz = a.mask_dtype == SAFE_DTYPE_BOOL ? 1 : 4;
+    mrow = static_cast<const uint8_t*>(a.mask) +
+           ((static_cast<size_t>(mb) * a.mask_H + mh) * a.N + row) * static_cast<size_t>(a.mask_cols) * esz;
+  }
+  const bool emit = (a.xattn_out != nullptr || a.lse_img_out != nullptr) && b == 0;
+  const float c2 = a.scale * kLog2e;  // logits are tracked in log2 units
+  float m = -INFINITY, l = 0.f;
+  const int n_img_tiles = (a.N + kGenTile - 1) / kGenTile;
+  const int n_txt_tiles = (tv + kGenTile - 1) / kGenTile;
+  for (int t = 0; t < n_img_tiles + n_txt_tiles; ++t) {
+    const bool txt = t >= n_img_tiles;
+    const int j0 = txt ? (t - n_img_tiles) * kGenTile : t * kGenTile;
+    const int nvalid = txt ? min(kGenTile, tv - j0) : min(kGenTile, a.N - j0);
+    const T* Ksrc = txt ? KT : KI;
+    const T* Vsrc = txt ? VT : VI;
+    __syncthreads();
+    for (int e = threadIdx.x; e < kGenTile * kGenD; e += kGenThreads) {
+      const int jj = e / kGenD, c = e - jj * kGenD;
+      const bool ok = jj < nvalid;
+      ks[jj][c] = ok ? ld(Ksrc, static_cast<size_t>(j0 + jj) * kGenD + c) : 0.f;
+      vs[jj][c] = ok ? ld(Vsrc, static_cast<size_t>(j0 + jj) * kGenD + c) : 0.f;
+    }
+    __syncthreads();
+    // logits of this tile, in log2 units, mask included
+    float s[kGenTile];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int jj = 0; jj < kGenTile; ++jj) {
+      float acc = 0.f;
+#pragma unroll
+      for (int c = 0; c < kGenD; ++c) acc = fmaf(q[c], ks[jj][c], acc);
+      float z = acc * a.scale;  // natural-log logit
+      if (HAS_MASK) {
+        const int col = (txt ? a.N : 0) + j0 + jj;
+        float mv = 0.f;
+        if (jj < nvalid && (!txt || a.mask_cols != a.N)) {
+          if (a.mask_dtype == SAFE_DTYPE_BOOL) mv = mrow[col] ? 0.f : -INFINITY;
+          else mv = reinterpret_cast<const float*>(mrow)[col];
+        }
+        z += mv;
+      }
+      if (emit && txt && a.xattn_out != nullptr && valid_row && jj < nvalid)
+        a.xattn_out[(static_cast<size_t>(h) * a.N + row) * a.T + j0 + jj] = z;
+      s[jj] = jj < nvalid ? z * kLog2e : -INFINITY;
+      tmax = fmaxf(tmax, s[jj]);
+    }
+    const float mnew = fmaxf(m, tmax);
+    if (mnew != -INFINITY) {
+      const float alpha = exp2f(m - mnew);
+      l *= alpha;
+#pragma unroll
+      for (int c = 0; c < kGenD; ++c) o[c] *= alpha;
+#pragma unroll
+      for (int jj = 0; jj < kGenTile; ++jj) {
+        const float p = exp2f(s[jj] - mnew);
+        l += p;
+#pragma unroll
+        for (int c = 0; c < kGenD; ++c) o[c] = fmaf(p, vs[jj][c], o[c]);
+      }
+      m = mnew;
+    }
+    if (emit && t == n_img_tiles - 1 && a.lse_img_out != nullptr && valid_row)
+      a.lse_img_out[static_cast<size_t>(h) * a.N + row] = (l > 0.f) ? (m + log2f(l)) * kLn2 : -INFINITY;
+  }
+  (void)c2;
+  if (!valid_row) return;
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  T* O = static_cast<T*>(a.out) + static_cast<size_t>(bh) * a.N * kGenD;
+#pragma unroll
+  for (int c = 0; c < kGenD; ++c) st(O, static_cast<size_t>(row) * kGenD + c, o[c] * inv);
+  if (a.lse != nullptr)
+    a.lse[static_cast<size_t>(bh) * a.N + row] = (l > 0.f) ? (m + log2f(l)) * kLn2 : -INFINITY;
+}
+
+hipError_t launch_attn_generic(const AttnArgs& a, int dtype, hipStream_t s) {
+  const int nqb = (a.R + kGenThreads - 1) / kGenThreads;
+  const uint32_t grid = static_cast<uint32_t>(a.B) * a.H * nqb;
+  const bool mask = a.mask != nullptr;
+  if (dtype == SAFE_DTYPE_F32) {
+    if (mask) k_attn_generic<float, true><<<grid, kGenThreads, 0, s>>>(a);
+    else k_attn_generic<float, false><<<grid, kGenThreads, 0, s>>>(a);
+  } else {
+    if (mask) k_attn_generic<uint16_t, true><<<grid, kGenThreads, 0, s>>>(a);
+    else k_attn_generic<uint16_t, false><<<grid, kGenThreads, 0, s>>>(a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace safe

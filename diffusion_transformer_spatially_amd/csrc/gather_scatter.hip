@@ -1,0 +1,44 @@
+// Row gather / scatter between the full-token cached state and a packed sensitive-row buffer
+// (SAFE-DiT technical summary, Methodology 3: only the S rows of the state change in an SRSU step).
+// Pure data movement: 16-byte vector copies, one lane per 16-byte chunk, HBM-bound.
+#include "common.hpp"
+
+namespace safe {
+
+template <bool SCATTER>
+__global__ __launch_bounds__(256) void k_rows_copy(const uint4* __restrict__ src, uint4* __restrict__ dst,
+                                                   const int32_t* __restrict__ rows, uint32_t k, uint32_t N,
+                                                   uint32_t cpr, uint32_t total) {
+  const uint32_t stride = gridDim.x * blockDim.x;
+  for (uint32_t c = blockIdx.x * blockDim.x + threadIdx.x; c < total; c += stride) {
+    const uint32_t part = c % cpr;
+    const uint32_t bhr = c / cpr;
+    const uint32_t r = bhr % k;
+    const uint32_t bh = bhr / k;
+    const int32_t row = rows[r];
+    if (row < 0 || static_cast<uint32_t>(row) >= N) continue;
+    const size_t sidx = (static_cast<size_t>(bh) * N + static_cast<uint32_t>(row)) * cpr + part;
+    if (SCATTER)
+      dst[sidx] = src[c];
+    else
+      dst[c] = src[sidx];
+  }
+}
+
+hipError_t launch_rows_copy(const void* src, void* dst, const int32_t* rows, int k, int B, int H, int N,
+                            int row_bytes, bool scatter, hipStream_t s) {
+  const uint32_t cpr = static_cast<uint32_t>(row_bytes / 16);
+  const uint32_t total = static_cast<uint32_t>(B) * H * static_cast<uint32_t>(k) * cpr;
+  if (total == 0) return hipSuccess;
+  uint32_t blocks = (total + 255) / 256;
+  if (blocks > 256 * 64) blocks = 256 * 64;
+  if (scatter)
+    k_rows_copy<true><<<blocks, 256, 0, s>>>(static_cast<const uint4*>(src), static_cast<uint4*>(dst), rows, k, N,
+                                             cpr, total);
+  else
+    k_rows_copy<false><<<blocks, 256, 0, s>>>(static_cast<const uint4*>(src), static_cast<uint4*>(dst), rows, k, N,
+                                              cpr, total);
+  return hipGetLastError();
+}
+
+}  // namespace safe

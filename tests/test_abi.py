@@ -1,0 +1,144 @@
+"""The C-ABI library: it loads, exports every declared entry point, and rejects bad arguments
+before launching anything (host-side checks; the CPU cases never reach a kernel)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import diffusion_transformer_spatially_amd as dts
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "safe_attn.h")
+
+OK, NULL, SHAPE, DTYPE, RANGE, WS, UNSUP, HIP, ALIGN = range(9)
+
+
+def _declared():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(safe_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_header_declares_the_binding_exports():
+    assert sorted(dts.EXPORTS) == _declared()
+
+
+def test_library_loads_and_exports_every_symbol():
+    lib = dts.load()
+    for name in _declared():
+        assert hasattr(lib, name), name
+    assert lib.safe_version() == 100
+    for code, name in [(0, b"SAFE_OK"), (2, b"SAFE_ERR_SHAPE"), (8, b"SAFE_ERR_ALIGN"), (99, b"SAFE_ERR_UNKNOWN")]:
+        assert lib.safe_status_string(code) == name
+
+
+def _cpu_only():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("host-validation cases use fake device addresses; run on a machine without a GPU")
+
+
+def _desc(**kw):
+    tv = (ctypes.c_int32 * 2)(77, 77)
+    D = dts.safe_attn_desc()
+    D.dtype, D.B, D.H, D.N, D.T, D.d = 0, 2, 4, 128, 256, 64
+    fake = 0x10000
+    D.q = D.k_img = D.v_img = D.k_txt = D.v_txt = D.out = fake
+    D.text_valid_len = ctypes.cast(tv, ctypes.POINTER(ctypes.c_int32))
+    for k, v in kw.items():
+        if k == "tv":
+            tv = (ctypes.c_int32 * len(v))(*v)
+            D.text_valid_len = ctypes.cast(tv, ctypes.POINTER(ctypes.c_int32))
+        else:
+            setattr(D, k, v)
+    return D, tv
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({"dtype": 5}, DTYPE), ({"B": 0}, SHAPE), ({"N": 0}, SHAPE), ({"T": -1}, SHAPE), ({"d": 32}, UNSUP),
+    ({"d": 128}, UNSUP), ({"B": 65}, UNSUP), ({"q": None}, NULL), ({"out": None}, NULL),
+    ({"tv": (77, 257)}, RANGE), ({"tv": (-1, 0)}, RANGE), ({"q": 0x10008}, ALIGN),
+    ({"mask": 0x20000, "mask_dtype": 0, "mask_B": 1, "mask_H": 1, "mask_cols": 128}, DTYPE),
+    ({"mask": 0x20000, "mask_dtype": 1, "mask_B": 3, "mask_H": 1, "mask_cols": 128}, SHAPE),
+    ({"mask": 0x20000, "mask_dtype": 1, "mask_B": 1, "mask_H": 1, "mask_cols": 200}, SHAPE),
+    ({"mask": 0x20002, "mask_dtype": 1, "mask_B": 1, "mask_H": 1, "mask_cols": 128}, ALIGN),
+    ({"scale": float("nan")}, RANGE),
+])
+def test_attention_validation(kw, code):
+    _cpu_only()
+    lib = dts.load()
+    D, _keep = _desc(**kw)
+    assert lib.safe_attn_dense(ctypes.byref(D), None) == code
+    assert lib.safe_attn_rows(ctypes.byref(D), 0x30000, 5, None) == code
+
+
+def test_rows_validation():
+    _cpu_only()
+    lib = dts.load()
+    D, _keep = _desc()
+    assert lib.safe_attn_rows(ctypes.byref(D), 0x30000, 129, None) == RANGE
+    assert lib.safe_attn_rows(ctypes.byref(D), 0x30000, -1, None) == RANGE
+    assert lib.safe_attn_rows(ctypes.byref(D), None, 3, None) == NULL
+    assert lib.safe_attn_rows(ctypes.byref(D), None, 0, None) == OK  # k = 0 is a no-op
+    assert lib.safe_attn_dense(None, None) == NULL
+
+
+def test_other_entry_validation():
+    _cpu_only()
+    lib = dts.load()
+    f = 0x10000
+    tv = (ctypes.c_int32 * 2)(3, 4)
+    tvp = ctypes.cast(tv, ctypes.POINTER(ctypes.c_int32))
+    res = ctypes.c_int32(-1)
+    chk = lambda *a: lib.safe_mask_is_row_constant(*a)
+    assert chk(None, 1, 1, 1, 8, 8, 4, tvp, 2, f, ctypes.byref(res), None, None) == NULL
+    assert chk(f, 7, 1, 1, 8, 8, 4, tvp, 2, f, ctypes.byref(res), None, None) == DTYPE
+    assert chk(f, 1, 3, 1, 8, 8, 4, tvp, 2, f, ctypes.byref(res), None, None) == SHAPE
+    assert chk(f, 1, 1, 1, 8, 9, 4, tvp, 2, f, ctypes.byref(res), None, None) == SHAPE
+    assert chk(f, 1, 1, 1, 8, 8, 3, tvp, 2, f, ctypes.byref(res), None, None) == RANGE
+    assert chk(f + 1, 1, 1, 1, 8, 8, 4, tvp, 2, f, ctypes.byref(res), None, None) == ALIGN
+    assert res.value == -1
+    acc = lib.safe_pcsp_accumulate
+    assert acc(None, None, 2, 8, 16, 4, 0, 4, f, 0, None) == NULL
+    assert acc(f, None, 2, 8, 16, 17, 0, 4, f, 0, None) == RANGE
+    assert acc(f, None, 2, 8, 16, 4, 3, 2, f, 0, None) == RANGE
+    assert acc(f, None, 2, 8, 16, 4, 0, 5, f, 0, None) == RANGE
+    assert acc(f, None, 0, 8, 16, 4, 0, 4, f, 0, None) == SHAPE
+    part = lib.safe_pcsp_partition
+    assert part(f, 10, 11, f, f, f, None, None) == RANGE
+    assert part(f, 0, 0, f, f, f, None, None) == SHAPE
+    assert part(f, 10, 3, None, f, f, None, None) == NULL
+    assert part(f, 10, 3, f, None, f, None, None) == NULL
+    assert part(f, 10, 3, f, f, None, None, None) == NULL
+    cfg = lib.safe_swcfg_combine
+    assert cfg(f, f, 16, 128, 128, 60, ctypes.c_float(3), ctypes.c_float(6), f, None) == SHAPE
+    assert cfg(None, f, 16, 128, 128, 64, ctypes.c_float(3), ctypes.c_float(6), f, None) == NULL
+    g = lib.safe_gather_rows
+    assert g(f, f, 5, 2, 2, 4, 64, 0, f, None) == RANGE
+    assert g(f, f, 2, 2, 2, 4, 64, 9, f, None) == DTYPE
+    assert g(f, f, 2, 2, 2, 4, 6, 0, f, None) == UNSUP
+    assert g(f + 8, f, 2, 2, 2, 4, 64, 0, f, None) == ALIGN
+    assert g(None, None, 0, 2, 2, 4, 64, 0, None, None) == OK
+    assert lib.safe_scatter_rows(f, None, 2, 2, 2, 4, 64, 1, f, None) == NULL
+
+
+@pytest.mark.gpu
+def test_gpu_errors_leave_outputs_untouched(lib):
+    import torch
+    q = torch.zeros((1, 2, 64, 64), dtype=torch.bfloat16, device="cuda")
+    kt = torch.zeros((1, 2, 8, 64), dtype=torch.bfloat16, device="cuda")
+    out = torch.full_like(q, 3.0)
+    with pytest.raises(dts.SafeAttnError) as e:
+        dts.safe_attn_dense(q, q, q, kt, kt, [9], out)
+    assert e.value.name == "SAFE_ERR_RANGE"
+    rows = torch.arange(65, dtype=torch.int32, device="cuda")
+    with pytest.raises(dts.SafeAttnError) as e:
+        dts.safe_attn_rows(q, q, q, kt, kt, [8], rows, out)
+    assert e.value.name == "SAFE_ERR_RANGE"
+    q32 = torch.zeros((1, 2, 64, 32), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(dts.SafeAttnError) as e:
+        dts.safe_attn_dense(q32, q32, q32, None, None, [0], q32)
+    assert e.value.name == "SAFE_ERR_UNSUPPORTED"
+    torch.cuda.synchronize()
+    assert torch.all(out == 3.0).item()

@@ -1,0 +1,144 @@
+"""GPU parity of SW-CFG, row gather/scatter and the mask-elision check."""
+import numpy as np
+import pytest
+
+import synthetic as syn
+from oracle import elision as OE
+from oracle import swcfg as OG
+from oracle import attention as OA
+from tests.gpu_util import CFG_REL, dev, host, torch
+
+pytestmark = pytest.mark.gpu
+
+
+# ------------------------------------------------------------------------------------------ SW-CFG
+def _cfg(lib, eps, s, side, gc, gs):
+    t = torch()
+    out = t.full(eps.shape[1:], np.nan, dtype=t.float32, device="cuda")
+    lib.safe_swcfg_combine(dev(eps), dev(s.astype(np.float32)), side, gc, gs, out)
+    t.cuda.synchronize()
+    return host(out).astype(np.float64)
+
+
+def _cfg_check(got, eps, s, side, gc, gs):
+    ref = OG.combine(eps, s, side, gc, gs)
+    e = eps.astype(np.float64)
+    g = OG.gamma(s, gc, gs)[OG.token_map(e.shape[2], e.shape[3], side)]
+    bound = CFG_REL * (np.abs(e[1]) + np.abs(g)[None] * np.abs(e[0] - e[1]))
+    assert np.all(np.abs(got - ref) <= bound + 1e-30)
+    assert np.linalg.norm(got - ref) <= CFG_REL * np.linalg.norm(ref)
+
+
+@pytest.mark.parametrize("name", ["srsu_1024", "traj_3072"])
+def test_swcfg_workloads(lib, name):
+    w = syn.WORKLOADS[name]
+    eps = syn.latent_eps(w)
+    s = np.random.default_rng(w.seed).random(w.N).astype(np.float32)
+    _cfg_check(_cfg(lib, eps, s, w.side, w.g_ctx, w.g_sens), eps, s.astype(np.float64), w.side, w.g_ctx, w.g_sens)
+
+
+@pytest.mark.parametrize("C,Hl,Wl,side", [(3, 6, 9, 3), (1, 5, 5, 5), (2, 8, 12, 4), (16, 128, 128, 64)])
+def test_swcfg_shapes_and_closed_forms(lib, C, Hl, Wl, side):
+    r = np.random.default_rng(C * Hl)
+    eps = r.standard_normal((2, C, Hl, Wl)).astype(np.float32)
+    s = r.random(side * side).astype(np.float32)
+    _cfg_check(_cfg(lib, eps, s, side, 3.0, 6.0), eps, s.astype(np.float64), side, 3.0, 6.0)
+    # gamma = 0 gives the unconditional branch exactly; equal scales are global CFG
+    assert np.array_equal(_cfg(lib, eps, s, side, 0.0, 0.0), eps[1].astype(np.float64))
+    got = _cfg(lib, eps, s, side, 4.5, 4.5)
+    _cfg_check(got, eps, np.zeros(side * side), side, 4.5, 4.5)
+
+
+# ------------------------------------------------------------------------------------ gather/scatter
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("k", [0, 1, 77, 300])
+def test_gather_scatter_bitwise(lib, dtype, k):
+    t = torch()
+    B, H, N, d = 2, 3, 300, 64
+    r = np.random.default_rng(k)
+    tdt = t.bfloat16 if dtype == "bf16" else t.float32
+    state = t.from_numpy(r.standard_normal((B, H, N, d)).astype(np.float32)).to(tdt).cuda()
+    rows = np.sort(r.choice(N, size=k, replace=False)).astype(np.int32)
+    rows_d = dev(rows)
+    packed = t.zeros((B, H, k, d), dtype=tdt, device="cuda")
+    lib.safe_gather_rows(state, rows_d, packed)
+    t.cuda.synchronize()
+    ref = state.float().cpu().numpy()
+    assert np.array_equal(packed.float().cpu().numpy(), OA.gather_rows(ref, rows))
+    canvas = t.full_like(state, 7.0)
+    lib.safe_scatter_rows(packed, rows_d, canvas)
+    t.cuda.synchronize()
+    expect = OA.scatter_rows(np.full(ref.shape, 7.0, dtype=np.float32), OA.gather_rows(ref, rows), rows)
+    assert np.array_equal(canvas.float().cpu().numpy(), expect)
+
+
+# ------------------------------------------------------------------------------------ mask check
+def _check(lib, mask: np.ndarray, N, T, tv, want_c=True):
+    t = torch()
+    flag = t.zeros(1, dtype=t.int32, device="cuda")
+    c = t.full((mask.shape[0] * mask.shape[1] * N,), 123.0, dtype=t.float32, device="cuda") if want_c else None
+    ok = lib.safe_mask_is_row_constant(dev(mask), N, T, tv, flag, c_out=c)
+    return ok, (host(c).astype(np.float64) if want_c else None)
+
+
+def _same(c_gpu, c_ref):
+    nan = np.isnan(c_ref)
+    return np.array_equal(np.isnan(c_gpu), nan) and np.array_equal(c_gpu[~nan], c_ref[~nan])
+
+
+def test_mask_check_random_small(lib):
+    r = np.random.default_rng(11)
+    N, T = 37, 9
+    for trial in range(60):
+        tv = tuple(int(x) for x in r.integers(0, T + 1, size=2))
+        cols = N if trial % 2 else N + T
+        mB, mH = int(r.integers(1, 3)), int(r.integers(1, 4))
+        if trial % 3 == 0:
+            m = r.random((mB, mH, N, cols)) < 0.995
+        else:
+            m = np.broadcast_to(r.integers(-2, 3, size=(mB, mH, N, 1)).astype(np.float32), (mB, mH, N, cols)).copy()
+            if trial % 3 == 1:
+                m[tuple(int(r.integers(0, s)) for s in m.shape)] = r.choice([np.nan, np.inf, -np.inf, 0.5, -0.0])
+        ok, c = _check(lib, m, N, T, tv)
+        rok, rc = OE.is_row_constant(m, N, T, tv)
+        assert ok == rok and _same(c, rc), trial
+        ok2, _ = _check(lib, m, N, T, tv, want_c=False)
+        assert ok2 == rok
+
+
+def test_mask_check_dense_1024_all_valid(lib):
+    w = syn.WORKLOADS["dense_1024"]
+    m = syn.mask_all_valid_bool(w.N, w.N)
+    assert _check(lib, m, w.N, w.T, w.tv, want_c=False)[0]
+    m[0, 0, 4095, 4095] = False
+    assert not _check(lib, m, w.N, w.T, w.tv, want_c=False)[0]
+    f = np.zeros((1, 1, w.N, w.N), dtype=np.float32)
+    f[0, 0, 17, 3] = -0.0
+    ok, c = _check(lib, f, w.N, w.T, w.tv)
+    assert ok and np.all(c == 0)
+    f[0, 0, 17, 3] = 1e-30
+    ok, c = _check(lib, f, w.N, w.T, w.tv)
+    assert not ok and np.isnan(c[17]) and np.sum(np.isnan(c)) == 1
+
+
+def test_mask_check_srsu_2560_all_valid(lib):
+    w = syn.WORKLOADS["srsu_2560"]
+    m = syn.mask_all_valid_bool(w.N, w.N)
+    assert _check(lib, m, w.N, w.T, w.tv, want_c=False)[0]
+    m[0, 0, 12345, 25599] = False
+    assert not _check(lib, m, w.N, w.T, w.tv, want_c=False)[0]
+
+
+def test_mask_check_unaligned_row_lengths(lib):
+    N, T = 29, 3
+    for cols in (N, N + T):
+        m = np.zeros((1, 2, N, cols), dtype=np.float32)
+        ok, c = _check(lib, m, N, T, (3,))
+        assert ok
+        m[0, 1, 28, cols - 1] = 2.0
+        ok, c = _check(lib, m, N, T, (3,))
+        assert not ok and np.isnan(c[N + 28])
+        mb = np.ones((1, 1, N, cols), dtype=np.bool_)
+        mb[0, 0, 3, cols - 1] = False
+        assert not _check(lib, mb, N, T, (3,))[0]
+        assert _check(lib, mb, N, T, (0,))[0] == (cols == N + T)

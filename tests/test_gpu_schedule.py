@@ -1,0 +1,64 @@
+"""The warmup / anchor / sensitive-row trajectory on the GPU against the oracle's schedule."""
+import numpy as np
+import pytest
+
+import synthetic as syn
+from oracle import schedule as OS
+from tests.gpu_util import assert_close, attn_tensors, dev, host, torch
+
+pytestmark = pytest.mark.gpu
+
+
+def _gpu_trajectory(lib, w, step_inputs, warm, state0):
+    t = torch()
+    sc = t.zeros(w.N, dtype=t.float32, device="cuda")
+    for i, (x, li) in enumerate(warm):
+        lib.safe_pcsp_accumulate(dev(x), dev(li), w.tv[0], 0, w.tv[0], sc, i > 0)
+    S = t.zeros(w.k, dtype=t.int32, device="cuda")
+    C = t.zeros(w.N - w.k, dtype=t.int32, device="cuda")
+    isn = t.zeros(w.N, dtype=t.uint8, device="cuda")
+    lib.safe_pcsp_partition(sc, w.k, S, C, isn)
+    state = t.from_numpy(state0).to(t.bfloat16).cuda()
+    snaps = []
+    for step, kind in enumerate(OS.plan(w.steps, w.anchor_every)):
+        q, ki, vi, kt, vt = step_inputs(step)
+        if kind == "dense":
+            lib.safe_attn_dense(q, ki, vi, kt, vt, w.tv, state)
+        else:
+            lib.safe_attn_rows(q, ki, vi, kt, vt, w.tv, S, state)
+        snaps.append(state.clone())
+    t.cuda.synchronize()
+    return state, host(S), snaps
+
+
+def test_small_trajectory_matches_oracle(lib):
+    w = syn.scaled(syn.WORKLOADS["traj_3072"], N=400, side=20, k=80, H=2, n_blobs=2, blob_sigma=3.0)
+    inputs = [syn.attention_inputs(w, step=s) for s in range(w.steps)]
+    warm = [(lambda d: (d["x"], d["lse_img"]))(syn.pcsp_logits(w, s)) for s in range(w.warmup_steps)]
+    state0 = syn.initial_state(w)
+    st, S, _ = _gpu_trajectory(lib, w, lambda s: attn_tensors(inputs[s], "bf16"), warm, state0)
+    ref, rS, _, kinds = OS.run(state0, warm, lambda s: tuple(inputs[s][n] for n in ("q", "k_img", "v_img", "k_txt", "v_txt")),
+                               w.k, w.steps, w.anchor_every, w.tv, 0, w.tv[0])
+    assert np.array_equal(S, rS)
+    assert_close(host(st), ref, "bf16", "trajectory")
+
+
+def test_full_size_trajectory_keeps_context_rows(lib):
+    """At 3072^2 (N = 36864): after 10 steps the context rows hold the last anchor's output bitwise."""
+    w = syn.WORKLOADS["traj_3072"]
+    t = torch()
+    g = t.Generator(device="cuda")
+
+    def step_inputs(step):
+        g.manual_seed(1000 + step)
+        mk = lambda n: (t.randn((w.B, w.H, n, w.d), generator=g, device="cuda") * w.std).to(t.bfloat16)
+        return mk(w.N), mk(w.N), mk(w.N), mk(w.T), mk(w.T)
+
+    warm = [(lambda d: (d["x"], d["lse_img"]))(syn.pcsp_logits(w, s)) for s in range(w.warmup_steps)]
+    state0 = np.zeros((w.B, w.H, w.N, w.d), dtype=np.float32)
+    st, S, snaps = _gpu_trajectory(lib, w, step_inputs, warm, state0)
+    C = t.as_tensor(np.setdiff1d(np.arange(w.N), S), device="cuda")
+    Sd = t.as_tensor(S.astype(np.int64), device="cuda")
+    assert t.equal(st[:, :, C], snaps[8][:, :, C])   # last anchor at step 8
+    assert t.equal(st[:, :, Sd], snaps[9][:, :, Sd])
+    assert not t.equal(snaps[9][:, :, Sd], snaps[8][:, :, Sd])
