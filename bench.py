@@ -1,0 +1,247 @@
+#!/usr/bin/env python3
+"""Benchmark of one pass of the spatially-adaptive DiT attention step on one MI355X.
+
+A step runs every stage of the hot path once over the 1024^2-latent workload (B = 2 cond/uncond,
+H = 24, d = 64, N = 4096 image tokens, T = 256 text slots with 77 valid, |S| = 1229):
+  elision check of the redundant all-valid image mask -> PCSP aggregation of the warmup
+  cross-attention logits -> exact top-|S| partition -> dense anchor attention (all rows) ->
+  sensitive-row attention (rows of S, scattered into the cached state) -> stand-alone gather and
+  scatter of the S rows -> SW-CFG on the 2x16x128x128 latent.
+Inputs are seeded synthetic tensors already resident in HBM.  The reported value is attention
+TFLOP/s over the whole step (dense + sensitive-row algorithmic flops, 4*rows*(N+Tv)*d per head,
+divided by the wall time of the whole step).
+
+Prints ONE JSON line.  --gpus above 1 exits with a message: this path runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="time budget of the oracle sample")
+    ap.add_argument("--no-large", action="store_true", help="skip the 2560^2 attention lines")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain 256 MiB device copy (for scaling HBM byte counters)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs the attention step on exactly one GPU; "
+              "--gpus above 1 is not supported (no multi-GPU path).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import diffusion_transformer_spatially_amd as dts
+    import synthetic as syn
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dts.load()
+    dev = torch.device("cuda:0")
+    w = syn.WORKLOADS["srsu_1024"]
+    B, H, N, T, d, k = w.B, w.H, w.N, w.T, w.d, w.k
+    Tv = w.tv[0]
+
+    # ---------------------------------------------------------------- inputs (seeded, resident in HBM)
+    inp = syn.attention_inputs(w)
+    bf = lambda n: torch.from_numpy(inp[n + "_bits"].view(np.int16)).view(torch.bfloat16).to(dev)
+    q, ki, vi, kt, vt = (bf(n) for n in ("q", "k_img", "v_img", "k_txt", "v_txt"))
+    x = syn.pcsp_logits(w)
+    xd = torch.from_numpy(x["x"]).to(dev)
+    lid = torch.from_numpy(x["lse_img"]).to(dev)
+    eps = torch.from_numpy(syn.latent_eps(w)).to(dev)
+    mask = torch.ones((1, 1, N, N), dtype=torch.bool, device=dev)
+    flag = torch.zeros(1, dtype=torch.int32, device=dev)
+    state = torch.zeros_like(q)
+    scores = torch.zeros(N, dtype=torch.float32, device=dev)
+    S = torch.zeros(k, dtype=torch.int32, device=dev)
+    C = torch.zeros(N - k, dtype=torch.int32, device=dev)
+    isn = torch.zeros(N, dtype=torch.uint8, device=dev)
+    s01 = torch.zeros(N, dtype=torch.float32, device=dev)
+    packed = torch.empty((B, H, k, d), dtype=torch.bfloat16, device=dev)
+    cfg_out = torch.empty(eps.shape[1:], dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+
+    stages = ["mask_check", "pcsp_accumulate", "pcsp_partition", "attn_dense", "attn_rows", "gather_rows",
+              "scatter_rows", "swcfg_combine"]
+    ev = {s: [] for s in stages}
+
+    def step(record: bool):
+        def mark(name, fn):
+            if record:
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                fn()
+                e1.record(stream)
+                ev[name].append((e0, e1))
+            else:
+                fn()
+        elided = []
+        mark("mask_check", lambda: elided.append(dts.safe_mask_is_row_constant(mask, N, T, w.tv, flag)))
+        m = None if elided[0] else mask
+        mark("pcsp_accumulate", lambda: dts.safe_pcsp_accumulate(xd, lid, Tv, 0, Tv, scores, False))
+        mark("pcsp_partition", lambda: dts.safe_pcsp_partition(scores, k, S, C, isn, s01))
+        mark("attn_dense", lambda: dts.safe_attn_dense(q, ki, vi, kt, vt, w.tv, state, mask=m))
+        mark("attn_rows", lambda: dts.safe_attn_rows(q, ki, vi, kt, vt, w.tv, S, state, mask=m))
+        mark("gather_rows", lambda: dts.safe_gather_rows(state, S, packed))
+        mark("scatter_rows", lambda: dts.safe_scatter_rows(packed, S, state))
+        mark("swcfg_combine", lambda: dts.safe_swcfg_combine(eps, s01, w.side, w.g_ctx, w.g_sens, cfg_out))
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = 1e3 * elapsed / args.steps
+    avg_ms = {s: float(np.mean([a.elapsed_time(b) for a, b in ev[s]])) for s in stages}
+
+    attn_flops = w.flops_dense + w.flops_rows
+    value = attn_flops / (ms_per_step * 1e-3) / 1e12
+
+    # algorithmic work per launch
+    dense_tf = w.flops_dense / (avg_ms["attn_dense"] * 1e-3) / 1e12
+    rows_tf = w.flops_rows / (avg_ms["attn_rows"] * 1e-3) / 1e12
+    pcsp_bytes = 4.0 * H * N * Tv + 4.0 * H * N + 4.0 * N
+    C_, Hl, Wl = w.latent
+    cfg_bytes = 3 * 4.0 * C_ * Hl * Wl + 4.0 * N
+    gs_bytes = 2 * 2.0 * B * H * k * d
+    mask_bytes = 1.0 * N * N
+    gbs = lambda b, ms: b / (ms * 1e-3) / 1e9
+    breakdown = {
+        "attn_dense": {"ms": avg_ms["attn_dense"], "tflops": dense_tf, "frac_mfma": dense_tf / MFMA_BF16_PEAK_TFLOPS},
+        "attn_rows": {"ms": avg_ms["attn_rows"], "tflops": rows_tf, "frac_mfma": rows_tf / MFMA_BF16_PEAK_TFLOPS},
+        "pcsp_accumulate": {"ms": avg_ms["pcsp_accumulate"], "gbs": gbs(pcsp_bytes, avg_ms["pcsp_accumulate"])},
+        "pcsp_partition": {"ms": avg_ms["pcsp_partition"]},
+        "swcfg_combine": {"ms": avg_ms["swcfg_combine"], "gbs": gbs(cfg_bytes, avg_ms["swcfg_combine"])},
+        "gather_rows": {"ms": avg_ms["gather_rows"], "gbs": gbs(gs_bytes, avg_ms["gather_rows"])},
+        "scatter_rows": {"ms": avg_ms["scatter_rows"], "gbs": gbs(gs_bytes, avg_ms["scatter_rows"])},
+        "mask_check": {"ms": avg_ms["mask_check"], "gbs": gbs(mask_bytes, avg_ms["mask_check"]),
+                       "note": "synchronous (host verdict), includes the device-to-host copy"},
+    }
+
+    result = {
+        "metric": "attention TFLOP/s + % bf16 MFMA peak (dense & |S|-row) at N=4096/25600",
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1)*0.125 Q/K/V, blob-biased cross-attention logits, N(0,1) latents)",
+        "config": {"workload": "srsu_1024: 1024^2 latent, B=2, H=24, d=64, N=4096, T=256 (Tv=77), |S|=1229, "
+                               "SW-CFG 2x16x128x128", "attention_flops_per_step": attn_flops},
+        "roofline": {"bound": "mfma", "achieved": dense_tf, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": dense_tf / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
+                     "kernel": "k_attn_mfma<false> (dense anchor attention)",
+                     "flops_per_launch": w.flops_dense, "avg_launch_ms": avg_ms["attn_dense"]},
+        "breakdown": breakdown,
+    }
+
+    # ---------------------------------------------------------------- 2560^2 attention (same kernels)
+    if not args.no_large:
+        wl = syn.WORKLOADS["srsu_2560"]
+        g = torch.Generator(device=dev)
+        g.manual_seed(wl.seed)
+        mk = lambda n: (torch.randn((wl.B, wl.H, n, wl.d), generator=g, device=dev) * wl.std).to(torch.bfloat16)
+        lq, lki, lvi, lkt, lvt = mk(wl.N), mk(wl.N), mk(wl.N), mk(wl.T), mk(wl.T)
+        lrows = torch.from_numpy(syn.random_rows(wl)).to(dev)
+        lout = torch.zeros_like(lq)
+        timing = {}
+        for name, fn in (("dense", lambda: dts.safe_attn_dense(lq, lki, lvi, lkt, lvt, wl.tv, lout)),
+                         ("rows", lambda: dts.safe_attn_rows(lq, lki, lvi, lkt, lvt, wl.tv, lrows, lout))):
+            fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            reps = 5
+            e0.record(stream)
+            for _ in range(reps):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            timing[name] = e0.elapsed_time(e1) / reps
+        tfd = wl.flops_dense / (timing["dense"] * 1e-3) / 1e12
+        tfr = wl.flops_rows / (timing["rows"] * 1e-3) / 1e12
+        result["attention_2560"] = {"workload": "srsu_2560: B=2, H=24, d=64, N=25600, Tv=120, |S|=5120",
+                                    "dense_ms": timing["dense"], "dense_tflops": tfd,
+                                    "dense_frac_mfma": tfd / MFMA_BF16_PEAK_TFLOPS,
+                                    "rows_ms": timing["rows"], "rows_tflops": tfr,
+                                    "rows_frac_mfma": tfr / MFMA_BF16_PEAK_TFLOPS}
+        del lq, lki, lvi, lkt, lvt, lout
+
+    if args.copy_calibration:
+        src = torch.empty(64 << 20, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        result["copy_calibration_bytes"] = {"read": src.numel() * 4, "write": dst.numel() * 4}
+
+    # ---------------------------------------------------------------- oracle on the host cores
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(w, inp, budget_s: float):
+    """The fp64 oracle as it stands, on a bounded sample of the same step's attention work."""
+    import numpy as np
+    from oracle import attention as OA
+
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas = 1
+    cores = len(os.sched_getaffinity(0))
+    rows = None  # every query row of each (b, h) visited
+    flops = 0.0
+    done = 0
+    t0 = time.perf_counter()
+    for b in range(w.B):
+        for h in range(w.H):
+            sl = lambda a: a[b:b + 1, h:h + 1]
+            OA.attention(sl(inp["q"]), sl(inp["k_img"]), sl(inp["v_img"]), sl(inp["k_txt"]), sl(inp["v_txt"]),
+                         (w.tv[b],), rows=rows)
+            flops += 4.0 * w.N * (w.N + w.tv[b]) * w.d
+            done += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+        if time.perf_counter() - t0 > budget_s:
+            break
+    el = time.perf_counter() - t0
+    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": min(cores, blas) if blas else cores,
+            "kind": "oracle",
+            "sample": f"fp64 numpy oracle dense attention (all {w.N} query rows) of {done} of the "
+                      f"{w.B * w.H} (b,h) heads of srsu_1024, stopped after a {budget_s:.0f} s budget ({el:.1f} s); "
+                      f"host affinity {cores} cores, BLAS threads {blas}"}
+
+
+if __name__ == "__main__":
+    main()

@@ -6,17 +6,23 @@
 // exactly: padded slots are never loaded), and writes the output rows into the full-token state.
 //
 // Shape of the work (d = 64):
-//  * a workgroup owns BM = 128 query rows of one (b,h): 4 waves x 32 rows;
+//  * a workgroup of 4 waves owns 4 * 32 * QB query rows of one (b,h); each wave owns QB blocks of 32
+//    rows, so every K / V operand read from LDS feeds QB matrix instructions;
 //  * keys stream in tiles of BN = 64 through double-buffered LDS (16-byte chunks XOR-swizzled by row);
-//  * per tile and wave: S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (keys are the M dimension, queries
-//    the N dimension), so every lane holds the 32 logits of one query row: lane L owns query L%32 and
-//    keys 16*(L/32) + r (r = 0..15) of each 32-key block thanks to a fixed permutation of the K rows
-//    fed to the MFMA;
-//  * fp32 online softmax in log2 units (scale*log2(e) folded into one FMA per logit, v_exp_f32),
-//    row max combined across the two lane halves with v_permlane32_swap, rescale of the output only
-//    when some row's max grew;
-//  * O^T += V^T P^T on the same MFMA: the P^T operand is the lane's own logits converted to bf16 (no
-//    data movement), the V^T operand is read from row-major LDS with ds_read_b64_tr_b16;
+//  * per tile: S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (keys are the M dimension, queries the N
+//    dimension), so every lane holds the 32 logits of one query row per block: lane L owns query
+//    L%32 and keys 16*(L/32) + r (r = 0..15) of each 32-key block, thanks to a fixed permutation of
+//    the K rows fed to the instruction;
+//  * fp32 online softmax in log2 units (scale*log2(e) folded into one FMA per logit, v_exp_f32); the
+//    row max is combined across the two lane halves with v_permlane32_swap; the output is rescaled
+//    only when some row's max grew; the row sum accumulates the bf16-rounded probabilities with
+//    v_dot2_f32_bf16, i.e. exactly the values the P V product uses (the fp32 probabilities when a
+//    log-sum-exp output is requested);
+//  * O^T += V^T P^T on the same instruction: the P^T operand is the lane's own probabilities (no data
+//    movement), the V^T operand is read from row-major LDS with ds_read_b64_tr_b16;
+//  * full image tiles run a loop without any masking; the ragged image tail and the text tiles run a
+//    separate path that masks keys past the valid count and, for the warmup emission, stores the
+//    text-block logits and the image-block log-sum-exp;
 //  * gathered rows: Q rows are loaded from rows[r] and outputs scattered to rows[r] in the epilogue.
 // The workgroup id is remapped so that the Q tiles of one (b,h) run on the same XCD and share K/V
 // in that XCD's L2.
@@ -34,9 +40,9 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) uint16_t lds_u16;
 
 constexpr int kD = 64;
-constexpr int kBM = 128;
 constexpr int kBN = 64;
 constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
 constexpr int kTileElems = kBN * kD;
 
 __device__ __forceinline__ float swap_halves(float x) {
@@ -46,8 +52,13 @@ __device__ __forceinline__ float swap_halves(float x) {
   return __uint_as_float(lane < 32 ? r[1] : r[0]);
 }
 
+// XOR swizzle of the 16-byte chunk index by key row: bits (1, 2, 4) of the row go to chunk bits
+// (2, 1, 0).  With 128-byte rows this spreads both LDS read patterns of a tile step -- 16-byte reads of
+// 16 permuted K rows, and transposing 8-byte reads of 4 consecutive V rows x 64 bytes -- over all 64
+// banks without conflicts.
+__device__ __forceinline__ int swz(int key) { return (((key >> 1) & 1) << 2) | (((key >> 2) & 1) << 1) | ((key >> 4) & 1); }
 // LDS element offset of (key row, 16-byte chunk) with the chunk XOR-swizzled by the row.
-__device__ __forceinline__ int lds_off(int key, int chunk) { return key * kD + ((chunk ^ (key & 7)) << 3); }
+__device__ __forceinline__ int lds_off(int key, int chunk) { return key * kD + ((chunk ^ swz(key)) << 3); }
 
 struct TileSrc {
   const uint16_t* k;
@@ -71,24 +82,24 @@ __device__ __forceinline__ TileSrc tile_src(const AttnArgs& a, size_t bh, int t,
   return s;
 }
 
-// Each thread moves 2 K chunks and 2 V chunks (16 B each) per tile; rows past nvalid become zeros.
-__device__ __forceinline__ void stage_load(uint4 (&r)[4], const TileSrc& s) {
+// Direct global -> LDS copies of one tile (no VGPR staging): each wave instruction writes 64
+// consecutive 16-byte LDS slots; slot p holds key row p/8, chunk (p%8) ^ swz(row) (the XOR swizzle), so
+// the global address of each lane is chosen to land its chunk in that slot.  Rows past nvalid are
+// clamped to the last valid row (never read out of bounds, never read padded text); the softmax
+// masks those keys to -inf and their probabilities are exactly 0.
+__device__ __forceinline__ void stage_issue(const TileSrc& s, uint16_t* kl, uint16_t* vl) {
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
-    const int ci = threadIdx.x + kThreads * u;
-    const int row = ci >> 3, c = ci & 7;
-    const bool ok = row < s.nvalid;
-    r[u] = ok ? *reinterpret_cast<const uint4*>(s.k + row * kD + c * 8) : make_uint4(0, 0, 0, 0);
-    r[2 + u] = ok ? *reinterpret_cast<const uint4*>(s.v + row * kD + c * 8) : make_uint4(0, 0, 0, 0);
-  }
-}
-__device__ __forceinline__ void stage_store(const uint4 (&r)[4], uint16_t* kl, uint16_t* vl) {
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int ci = threadIdx.x + kThreads * u;
-    const int row = ci >> 3, c = ci & 7;
-    *reinterpret_cast<uint4*>(kl + lds_off(row, c)) = r[u];
-    *reinterpret_cast<uint4*>(vl + lds_off(row, c)) = r[2 + u];
+    const int base = (u * kWaves + w) * 64;  // first slot of this wave instruction
+    const int p = base + lane;
+    const int row = p >> 3;
+    const int c = (p & 7) ^ swz(row);
+    const int srow = row < s.nvalid ? row : s.nvalid - 1;
+    __builtin_amdgcn_global_load_lds(static_cast<const void*>(s.k + srow * kD + c * 8),
+                                     (__attribute__((address_space(3))) void*)(kl + base * 8), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(static_cast<const void*>(s.v + srow * kD + c * 8),
+                                     (__attribute__((address_space(3))) void*)(vl + base * 8), 16, 0, 0);
   }
 }
 
@@ -97,9 +108,198 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-__global__ __launch_bounds__(kThreads) void k_attn_mfma(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][kTileElems];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][kTileElems];
+// Per-wave running state of QB query blocks.
+template <int QB>
+struct WaveState {
+  bf16x8 q[QB][4];   // Q^T operand: lane (q + 32g) holds Q[q][16ks + 8g .. +7]
+  f32x16 o[QB][2];   // O^T accumulators: lane holds query L%32, head dims db*32 + 8(r/4) + 4g + r%4
+  float m[QB];       // running row max (raw dot-product units)
+  float l[QB];       // running row sum of exp2((s - m) * c2), lane-half partial
+};
+
+// One 64-key tile: logits, online softmax, P V.  MASKED handles partial tiles (keys >= nvalid are
+// -inf) and the optional store of the tile's logits (text tiles of the warmup emission).
+template <int QB, bool MASKED, bool EXACT_SUM>
+__device__ __forceinline__ void tile_step(WaveState<QB>& st, const uint16_t* kl, const uint16_t* vl, int kperm,
+                                          int g, int li, int dc0, float c2, int nvalid, float* const (&xo)[QB],
+                                          float scale) {
+  // ---- S^T = K Q^T
+  f32x16 s[QB][2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    const int key = kb * 32 + kperm;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kl + lds_off(key, 2 * ks + g));
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        if (ks == 0)
+          s[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, st.q[qb][0], (f32x16){}, 0, 0, 0);
+        else
+          s[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, st.q[qb][ks], s[qb][kb], 0, 0, 0);
+      }
+    }
+  }
+  if (MASKED) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = kb * 32 + 16 * g + i;
+          s[qb][kb][i] = key < nvalid ? s[qb][kb][i] : -INFINITY;
+        }
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+      if (xo[qb] != nullptr) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = kb * 32 + 16 * g + i;
+            if (key < nvalid) xo[qb][key] = s[qb][kb][i] * scale;
+          }
+      }
+  }
+
+  // ---- online softmax in log2 units against the running max m.  The tile's probabilities are made
+  // with the current m first; only if a lane's partial tile sum exceeds 2^16 (some logit is more
+  // than 16 log2-units above m, always the case on the first tile where m = -inf, or a NaN) does the
+  // wave take the exact path: recompute S from the K tile still in LDS, take the tile max, rescale O
+  // and l, and remake P.  m itself stays the running max of logits seen, so probabilities are <= 2^16
+  // and nothing over- or underflows; the result is the same softmax up to rounding.
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  bf16x8 p[QB][2][2];
+  float tl[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const float mc = st.m[qb] * c2;
+    float tsum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int mm = 0; mm < 2; ++mm) {
+        uint32_t pk[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(s[qb][kb][8 * mm + 2 * e], c2, -mc));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(s[qb][kb][8 * mm + 2 * e + 1], c2, -mc));
+          pk[e] = pack_bf16x2(p0, p1);
+          if (EXACT_SUM)
+            tsum += p0 + p1;
+          else
+            tsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[e]), ones, tsum, false);
+        }
+        p[qb][kb][mm] = __builtin_bit_cast(bf16x8, (uint4){pk[0], pk[1], pk[2], pk[3]});
+      }
+    tl[qb] = tsum;
+  }
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    if (__any(!(tl[qb] <= 65536.f))) {
+      // exact path: S again (the tile is still in LDS), tile max, rescale, P again
+      f32x16 sx[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int key = kb * 32 + kperm;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kl + lds_off(key, 2 * ks + g));
+          sx[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, st.q[qb][ks], ks == 0 ? (f32x16){} : sx[kb], 0, 0, 0);
+        }
+      }
+      if (MASKED) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) sx[kb][i] = (kb * 32 + 16 * g + i) < nvalid ? sx[kb][i] : -INFINITY;
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sx[kb][i]);
+      mx = fmaxf(mx, swap_halves(mx));
+      const float mnew = fmaxf(st.m[qb], mx);
+      if (mnew > st.m[qb]) {
+        const float alpha = __builtin_amdgcn_exp2f((st.m[qb] - mnew) * c2);
+        st.l[qb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) st.o[qb][db][i] *= alpha;
+        st.m[qb] = mnew;
+      }
+      const float mc = st.m[qb] * c2;
+      float tsum = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int mm = 0; mm < 2; ++mm) {
+          uint32_t pk[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float p0 = __builtin_amdgcn_exp2f(fmaf(sx[kb][8 * mm + 2 * e], c2, -mc));
+            const float p1 = __builtin_amdgcn_exp2f(fmaf(sx[kb][8 * mm + 2 * e + 1], c2, -mc));
+            pk[e] = pack_bf16x2(p0, p1);
+            if (EXACT_SUM)
+              tsum += p0 + p1;
+            else
+              tsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[e]), ones, tsum, false);
+          }
+          p[qb][kb][mm] = __builtin_bit_cast(bf16x8, (uint4){pk[0], pk[1], pk[2], pk[3]});
+        }
+      tl[qb] = tsum;
+    }
+    st.l[qb] += tl[qb];
+  }
+
+  // ---- O^T += V^T P^T.  A operand: lane (dc + 32g) gets V[keys 16g+8mm .. +7][dc] via two
+  // transposing 4x16 reads; B operand: this lane's own probabilities for those keys.
+  lds_u16* vl3 = (lds_u16*)(vl);
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+    for (int mm = 0; mm < 2; ++mm) {
+      const int key = kb * 32 + 16 * g + 8 * mm + (li >> 2);
+#pragma unroll
+      for (int db = 0; db < 2; ++db) {
+        const int col = db * 32 + dc0 + 4 * (li & 3);
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vl3 + lds_off(key, col >> 3) + (col & 4)));
+        const s16x4 hi =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vl3 + lds_off(key + 4, col >> 3) + (col & 4)));
+        const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+          st.o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, p[qb][kb][mm], st.o[qb][db], 0, 0, 0);
+      }
+    }
+  }
+}
+
+template <int QB>
+__device__ __forceinline__ void store_lse_img(const AttnArgs& a, const WaveState<QB>& st, int h, const int (&row)[QB],
+                                              const bool (&valid)[QB], int g) {
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const float lt = st.l[qb] + swap_halves(st.l[qb]);
+    if (valid[qb] && g == 0)
+      a.lse_img_out[static_cast<size_t>(h) * a.N + row[qb]] = lt > 0.f ? st.m[qb] * a.scale + logf(lt) : -INFINITY;
+  }
+}
+
+template <bool GATHER, int QB, bool EXACT_SUM>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void k_attn_mfma(AttnArgs a) {
+  constexpr int kRowsW = 32 * QB;
+  constexpr int kBM = kWaves * kRowsW;
+  // Two LDS buffers as distinct objects: every read and every DMA target below names one of them
+  // statically, so the compiler can see that the prefetch into one never aliases reads of the other
+  // and does not wait for the prefetch before computing.
+  __shared__ __attribute__((aligned(16))) uint16_t k_a[kTileElems];
+  __shared__ __attribute__((aligned(16))) uint16_t v_a[kTileElems];
+  __shared__ __attribute__((aligned(16))) uint16_t k_b[kTileElems];
+  __shared__ __attribute__((aligned(16))) uint16_t v_b[kTileElems];
 
   const int nqt = (a.R + kBM - 1) / kBM;
   const uint32_t G = static_cast<uint32_t>(a.B) * a.H * nqt;
@@ -112,180 +312,143 @@ __global__ __launch_bounds__(kThreads) void k_attn_mfma(AttnArgs a) {
 
   const int w = threadIdx.x >> 6;
   const int L = threadIdx.x & 63;
-  const int qi = L & 31;   // query column of the MFMA tiles owned by this lane
-  const int g = L >> 5;    // lane half
+  const int qi = L & 31;  // query column of the MFMA tiles owned by this lane
+  const int g = L >> 5;   // lane half
   const int li = L & 15;
   const int dc0 = 16 * ((L >> 4) & 1);
 
-  const int r = qt * kBM + w * 32 + qi;
-  const bool active = r < a.R;
-  int row = active ? (a.rows ? a.rows[r] : r) : 0;
-  const bool valid_row = active && row >= 0 && row < a.N;
-  if (!valid_row) row = 0;
-
-  // Q^T operand: lane (q + 32g) holds Q[q][16ks + 8g .. +7]
-  bf16x8 qreg[4];
-  {
-    const bf16x8* qp = reinterpret_cast<const bf16x8*>(static_cast<const uint16_t*>(a.q) + (bh * a.N + row) * kD);
+  int row[QB];
+  bool valid[QB];
+  WaveState<QB> st;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) qreg[ks] = qp[2 * ks + g];
+  for (int qb = 0; qb < QB; ++qb) {
+    const int r = qt * kBM + w * kRowsW + qb * 32 + qi;
+    const bool active = r < a.R;
+    const int rr = active ? (GATHER ? a.rows[r] : r) : 0;
+    valid[qb] = active && rr >= 0 && rr < a.N;
+    row[qb] = valid[qb] ? rr : 0;
+    const bf16x8* qp =
+        reinterpret_cast<const bf16x8*>(static_cast<const uint16_t*>(a.q) + (bh * a.N + row[qb]) * kD);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) st.q[qb][ks] = qp[2 * ks + g];
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) st.o[qb][db][i] = 0.f;
+    st.m[qb] = -INFINITY;
+    st.l[qb] = 0.f;
   }
 
   const int n_img = (a.N + kBN - 1) / kBN;
+  const int n_full = a.N / kBN;  // image tiles with all 64 keys valid
   const int n_txt = (tv + kBN - 1) / kBN;
   const int ntiles = n_img + n_txt;
   const bool emit = b == 0 && (a.xattn_out != nullptr || a.lse_img_out != nullptr);
   const float c2 = a.scale * kLog2e;
-
-  f32x16 o[2];
-#pragma unroll
-  for (int db = 0; db < 2; ++db)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
-  float m = -INFINITY, l = 0.f;
-
-  uint4 st[4];
-  {
-    const TileSrc s0 = tile_src(a, bh, 0, n_img, tv);
-    stage_load(st, s0);
-    stage_store(st, k_lds[0], v_lds[0]);
-  }
-  __syncthreads();
-
   // K rows fed to the MFMA: A-row R reads key kb*32 + 16*((R>>2)&1) + 4*(R>>3) + (R&3), which makes
   // output register r of lane half g hold key 16*g + r.
   const int kperm = 16 * ((qi >> 2) & 1) + 4 * (qi >> 3) + (qi & 3);
 
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    const bool has_next = t + 1 < ntiles;
-    if (has_next) stage_load(st, tile_src(a, bh, t + 1, n_img, tv));
+  stage_issue(tile_src(a, bh, 0, n_img, tv), k_a, v_a);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
 
-    const uint16_t* kl = k_lds[buf];
+  float* const no_store[QB] = {};
+  // One tile: prefetch tile t+1 into the other buffer, compute on this one, then wait for the
+  // prefetch and synchronise.
+  auto full_tile = [&](int t, const uint16_t* ck, const uint16_t* cv, uint16_t* nk, uint16_t* nv) {
+    if (t + 1 < ntiles) stage_issue(tile_src(a, bh, t + 1, n_img, tv), nk, nv);
+    tile_step<QB, false, EXACT_SUM>(st, ck, cv, kperm, g, li, dc0, c2, kBN, no_store, a.scale);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  };
+  auto masked_tile = [&](int t, const uint16_t* ck, const uint16_t* cv, uint16_t* nk, uint16_t* nv) {
+    if (emit && t == n_img && a.lse_img_out != nullptr) store_lse_img(a, st, h, row, valid, g);
+    if (t + 1 < ntiles) stage_issue(tile_src(a, bh, t + 1, n_img, tv), nk, nv);
     const bool txt = t >= n_img;
     const int nvalid = txt ? min(kBN, tv - (t - n_img) * kBN) : min(kBN, a.N - t * kBN);
-
-    // ---- S^T = K Q^T
-    f32x16 s[2];
+    float* xo[QB];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
-      const int key = kb * 32 + kperm;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kl + lds_off(key, 2 * ks + g));
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[ks], s[kb], 0, 0, 0);
-      }
-    }
-    if (nvalid < kBN) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (kb * 32 + 16 * g + i >= nvalid) s[kb][i] = -INFINITY;
-    }
-    if (emit && txt && a.xattn_out != nullptr && valid_row) {
-      const int j0 = (t - n_img) * kBN;
-      float* xo = a.xattn_out + (static_cast<size_t>(h) * a.N + row) * a.T + j0;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (kb * 32 + 16 * g + i < nvalid) xo[kb * 32 + 16 * g + i] = s[kb][i] * a.scale;
-    }
-
-    // ---- online softmax (log2 units)
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-    mx = fmaxf(mx, swap_halves(mx));
-    const float mnew = fmaxf(m, mx);
-    if (__any(mnew > m)) {
-      const float alpha = __builtin_amdgcn_exp2f((m - mnew) * c2);
-      l *= alpha;
-#pragma unroll
-      for (int db = 0; db < 2; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
-      m = mnew;
-    }
-    const float mc = m * c2;
-    bf16x8 p[2][2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int mm = 0; mm < 2; ++mm) {
-        uint32_t pk[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * mm + 2 * e], c2, -mc));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * mm + 2 * e + 1], c2, -mc));
-          l += p0 + p1;
-          pk[e] = pack_bf16x2(p0, p1);
-        }
-        p[kb][mm] = __builtin_bit_cast(bf16x8, (uint4){pk[0], pk[1], pk[2], pk[3]});
-      }
-    }
-
-    if (emit && t == n_img - 1 && a.lse_img_out != nullptr) {
-      const float lt = l + swap_halves(l);
-      if (valid_row && g == 0)
-        a.lse_img_out[static_cast<size_t>(h) * a.N + row] = lt > 0.f ? m * a.scale + logf(lt) : -INFINITY;
-    }
-
-    // ---- O^T += V^T P^T  (A operand: lane (dc + 32g) gets V[keys 16g+8mm .. +7][dc] via two
-    // transposing 4x16 reads; B operand: this lane's own probabilities for those keys)
-    {
-      lds_u16* vl3 = (lds_u16*)(&v_lds[buf][0]);
-#pragma unroll
-      for (int db = 0; db < 2; ++db) {
-        const int col = db * 32 + dc0 + 4 * (li & 3);
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-          for (int mm = 0; mm < 2; ++mm) {
-            const int key = kb * 32 + 16 * g + 8 * mm + (li >> 2);
-            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vl3 + lds_off(key, col >> 3) + (col & 4)));
-            const s16x4 hi =
-                __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vl3 + lds_off(key + 4, col >> 3) + (col & 4)));
-            const s16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, both), p[kb][mm], o[db], 0, 0,
-                                                             0);
-          }
-        }
-      }
-    }
-
-    if (has_next) stage_store(st, k_lds[buf ^ 1], v_lds[buf ^ 1]);
+    for (int qb = 0; qb < QB; ++qb)
+      xo[qb] = (emit && txt && a.xattn_out != nullptr && valid[qb])
+                   ? a.xattn_out + (static_cast<size_t>(h) * a.N + row[qb]) * a.T + (t - n_img) * kBN
+                   : nullptr;
+    tile_step<QB, true, EXACT_SUM>(st, ck, cv, kperm, g, li, dc0, c2, nvalid, xo, a.scale);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-  }
+  };
 
-  // ---- epilogue: normalise, write the output row (scatter for gathered rows) and its lse
-  const float lt = l + swap_halves(l);
-  if (!valid_row) return;
-  const float inv = lt > 0.f ? 1.f / lt : 0.f;
-  uint16_t* orow = static_cast<uint16_t*>(a.out) + (bh * a.N + row) * kD;
+  int t = 0;
+  // ---- full image tiles, two per iteration (buffer a, then buffer b)
+  for (; t + 1 < n_full; t += 2) {
+    full_tile(t, k_a, v_a, k_b, v_b);
+    full_tile(t + 1, k_b, v_b, k_a, v_a);
+  }
+  if (t < n_full) {
+    full_tile(t, k_a, v_a, k_b, v_b);
+    ++t;
+  }
+  // ---- ragged image tail and text tiles (tile t sits in buffer a when t is even)
+  for (; t < ntiles; ++t) {
+    if ((t & 1) == 0)
+      masked_tile(t, k_a, v_a, k_b, v_b);
+    else
+      masked_tile(t, k_b, v_b, k_a, v_a);
+  }
+  if (emit && n_txt == 0 && a.lse_img_out != nullptr) store_lse_img(a, st, h, row, valid, g);
+
+  // ---- epilogue: normalise, write the output rows (scatter for gathered rows) and their lse
 #pragma unroll
-  for (int db = 0; db < 2; ++db)
+  for (int qb = 0; qb < QB; ++qb) {
+    const float lt = st.l[qb] + swap_halves(st.l[qb]);
+    if (!valid[qb]) continue;
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    uint16_t* orow = static_cast<uint16_t*>(a.out) + (bh * a.N + row[qb]) * kD;
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int dc = db * 32 + 8 * rr + 4 * g;
-      uint2 v;
-      v.x = pack_bf16x2(o[db][4 * rr + 0] * inv, o[db][4 * rr + 1] * inv);
-      v.y = pack_bf16x2(o[db][4 * rr + 2] * inv, o[db][4 * rr + 3] * inv);
-      *reinterpret_cast<uint2*>(orow + dc) = v;
-    }
-  if (a.lse != nullptr && g == 0) a.lse[bh * a.N + row] = lt > 0.f ? m * a.scale + logf(lt) : -INFINITY;
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int dc = db * 32 + 8 * rr + 4 * g;
+        uint2 v;
+        v.x = pack_bf16x2(st.o[qb][db][4 * rr + 0] * inv, st.o[qb][db][4 * rr + 1] * inv);
+        v.y = pack_bf16x2(st.o[qb][db][4 * rr + 2] * inv, st.o[qb][db][4 * rr + 3] * inv);
+        *reinterpret_cast<uint2*>(orow + dc) = v;
+      }
+    if (a.lse != nullptr && g == 0) a.lse[bh * a.N + row[qb]] = lt > 0.f ? st.m[qb] * a.scale + logf(lt) : -INFINITY;
+  }
+}
+
+template <bool GATHER, int QB, bool EXACT_SUM>
+static void launch(const AttnArgs& a, hipStream_t s) {
+  constexpr int kBM = kWaves * 32 * QB;
+  const int nqt = (a.R + kBM - 1) / kBM;
+  const uint32_t grid = static_cast<uint32_t>(a.B) * a.H * nqt;
+  k_attn_mfma<GATHER, QB, EXACT_SUM><<<grid, kThreads, 0, s>>>(a);
+}
+
+template <bool GATHER, int QB>
+static void launch_sum(const AttnArgs& a, hipStream_t s) {
+  // The row sum accumulates the bf16-rounded probabilities (v_dot2, exactly the values the P V
+  // product uses) unless a log-sum-exp output is requested; then it sums the fp32 probabilities so
+  // that lse / lse_img keep fp32 accuracy (they feed the sensitivity scores).
+  const bool exact = a.lse != nullptr || a.lse_img_out != nullptr;
+  if (exact) launch<GATHER, QB, true>(a, s);
+  else launch<GATHER, QB, false>(a, s);
 }
 
 hipError_t launch_attn_mfma_bf16(const AttnArgs& a, hipStream_t s) {
-  const int nqt = (a.R + kBM - 1) / kBM;
-  const uint32_t grid = static_cast<uint32_t>(a.B) * a.H * nqt;
-  if (grid == 0) return hipSuccess;
-  k_attn_mfma<<<grid, kThreads, 0, s>>>(a);
+  if (a.R == 0) return hipSuccess;
+  // Two query blocks per wave halve the LDS traffic per flop; one block per wave doubles the number
+  // of waves, which wins when the row count alone cannot fill the 1024 SIMDs about twice over.
+  const double waves_qb2 = static_cast<double>(a.B) * a.H * ((a.R + 63) / 64);
+  const bool qb2 = waves_qb2 >= 2048.0;
+  if (a.rows != nullptr) {
+    if (qb2) launch_sum<true, 2>(a, s);
+    else launch_sum<true, 1>(a, s);
+  } else {
+    if (qb2) launch_sum<false, 2>(a, s);
+    else launch_sum<false, 1>(a, s);
+  }
   return hipGetLastError();
 }
 

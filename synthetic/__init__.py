@@ -35,12 +35,12 @@ def rng_for(seed: int, role: str, step: int = 0) -> np.random.Generator:
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round-to-nearest-even fp32 -> bf16, returned as uint16 bit patterns (NaN stays NaN)."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    lsb = (u >> 16) & 1
-    r = ((u + 0x7FFF + lsb) >> 16).astype(np.uint16)
+    u = x.view(np.uint32)
+    # non-NaN patterns are at most 0xFF800000, so adding up to 0x8000 cannot wrap in uint32
+    r = ((u + (np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1)))) >> np.uint32(16)).astype(np.uint16)
     nan = np.isnan(x)
     if nan.any():
-        r = np.where(nan, ((u >> 16) | 0x40).astype(np.uint16), r)
+        r = np.where(nan, ((u >> np.uint32(16)) | np.uint32(0x40)).astype(np.uint16), r)
     return r
 
 

@@ -10,11 +10,11 @@ from tests.gpu_util import assert_close, attn_tensors, dev, err, host, torch
 pytestmark = pytest.mark.gpu
 
 
-def _run(lib, w, inp, rows=None, state=None, emission=False, mask=None):
+def _run(lib, w, inp, rows=None, state=None, emission=False, mask=None, want_lse=True):
     t = torch()
     q, ki, vi, kt, vt = attn_tensors(inp, w.dtype)
     out = t.from_numpy(state).to(q.dtype).cuda() if state is not None else t.zeros_like(q)
-    lse = t.full((w.B, w.H, w.N), float("nan"), dtype=t.float32, device="cuda")
+    lse = t.full((w.B, w.H, w.N), float("nan"), dtype=t.float32, device="cuda") if want_lse else None
     xo = t.full((w.H, w.N, w.T), float("nan"), dtype=t.float32, device="cuda") if emission else None
     li = t.full((w.H, w.N), float("nan"), dtype=t.float32, device="cuda") if emission else None
     if rows is None:
@@ -23,7 +23,7 @@ def _run(lib, w, inp, rows=None, state=None, emission=False, mask=None):
         lib.safe_attn_rows(q, ki, vi, kt, vt, w.tv, dev(rows.astype(np.int32)), out, mask=mask, lse=lse,
                            xattn_out=xo, lse_img_out=li)
     t.cuda.synchronize()
-    return host(out), host(lse), (host(xo) if emission else None), (host(li) if emission else None)
+    return host(out), (host(lse) if want_lse else None), (host(xo) if emission else None), (host(li) if emission else None)
 
 
 def _oracle(w, inp, rows=None, mask=None, emission=False):
@@ -101,15 +101,18 @@ SHAPES = [
 ]
 
 
+@pytest.mark.parametrize("want_lse", [True, False], ids=["lse", "nolse"])
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "B%dH%dN%dT%d" % s[:4])
-def test_bf16_dense_parity(lib, shape):
+def test_bf16_dense_parity(lib, shape, want_lse):
+    """Both row-sum forms: fp32 sum when lse is requested, bf16-probability sum otherwise."""
     B, H, N, T, tv = shape
     w = syn.scaled(syn.WORKLOADS["dense_1024"], B=B, H=H, N=N, T=T, tv=tv, side=1)
     inp = syn.attention_inputs(w)
-    o, lse, _, _ = _run(lib, w, inp)
+    o, lse, _, _ = _run(lib, w, inp, want_lse=want_lse)
     ro, rlse = _oracle(w, inp)
     assert_close(o, ro, "bf16", f"dense {shape}")
-    assert np.max(np.abs(lse - rlse)) < 1e-3
+    if want_lse:
+        assert np.max(np.abs(lse - rlse)) < 1e-4
 
 
 @pytest.mark.parametrize("k", [0, 1, 63, 64, 65, 129, 300])
@@ -118,14 +121,14 @@ def test_bf16_rows_parity_and_untouched_context(lib, k):
     inp = syn.attention_inputs(w)
     rows = syn.random_rows(w, k=k)
     state = syn.initial_state(w)
-    o, _, _, _ = _run(lib, w, inp, rows=rows, state=state)
+    o, _, _, _ = _run(lib, w, inp, rows=rows, state=state, want_lse=(k % 2 == 1))
     C = np.setdiff1d(np.arange(w.N), rows)
     assert np.array_equal(o[:, :, C], state[:, :, C].astype(np.float64))
     if k:
         ro, _ = _oracle(w, inp, rows=rows)
         assert_close(o[:, :, rows], ro, "bf16", f"rows k={k}")
     if k == w.N:
-        od, _, _, _ = _run(lib, w, inp)
+        od, _, _, _ = _run(lib, w, inp, want_lse=False)
         assert np.array_equal(o, od)
 
 
@@ -149,6 +152,8 @@ def test_bf16_closed_forms(lib):
     inp = syn.attention_inputs(w)
     one = np.full_like(inp["v_img_bits"], 0x3F80)  # 1.0
     ones = dict(inp, v_img_bits=one, v_txt_bits=np.full_like(inp["v_txt_bits"], 0x3F80))
+    o, _, _, _ = _run(lib, w, ones, want_lse=False)
+    assert np.max(np.abs(o - 1.0)) <= 1e-6  # the row sum uses the same bf16 probabilities as P V
     o, _, _, _ = _run(lib, w, ones)
     assert np.max(np.abs(o - 1.0)) <= 2e-2
     zq = dict(inp, q_bits=np.zeros_like(inp["q_bits"]))
