@@ -158,8 +158,9 @@ def main():
         "config": {"workload": "srsu_1024: 1024^2 latent, B=2, H=24, d=64, N=4096, T=256 (Tv=77), |S|=1229, "
                                "SW-CFG 2x16x128x128", "attention_flops_per_step": attn_flops},
         "roofline": {"bound": "mfma", "achieved": dense_tf, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": dense_tf / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
-                     "kernel": "k_attn_mfma<false> (dense anchor attention)",
+                     "frac": dense_tf / MFMA_BF16_PEAK_TFLOPS, "traffic": profiled_traffic(),
+                     "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE/WRITE_SIZE, copy-calibrated)",
+                     "kernel": "k_attn_mfma<false, 2, false> (dense anchor attention)",
                      "flops_per_launch": w.flops_dense, "avg_launch_ms": avg_ms["attn_dense"]},
         "breakdown": breakdown,
     }
@@ -207,6 +208,27 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def profiled_traffic():
+    """HBM bytes per launch of the dense attention kernel from the committed counter summary, or None
+    when the kernel source has changed since those counters were taken."""
+    import hashlib
+    prof = os.path.join(ROOT, "profiles", "attn_dense_1024.md")
+    if not os.path.exists(prof):
+        return None
+    fields = {}
+    for line in open(prof):
+        if ":" in line and line.strip().split(":")[0] in ("traffic_bytes_per_launch", "kernel_source_sha256"):
+            k, v = line.strip().split(":", 1)
+            fields[k] = v.strip()
+    h = hashlib.sha256()
+    for f in ("attn_mfma.hip", "common.hpp"):
+        with open(os.path.join(ROOT, "diffusion_transformer_spatially_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    if fields.get("kernel_source_sha256") != h.hexdigest() or "traffic_bytes_per_launch" not in fields:
+        return None
+    return float(fields["traffic_bytes_per_launch"])
 
 
 def cpu_baseline(w, inp, budget_s: float):
