@@ -92,12 +92,108 @@ __global__ __launch_bounds__(kPcspThreads) void k_pcsp_accumulate(const float* _
   }
 }
 
+// Batched form for Tv <= 64*TV4 with float4 rows: each 16-lane group issues the loads of up to JB
+// (head, token) rows at once (JB*TV4 float4 per lane in flight) and then reduces them from registers,
+// so HBM latency is paid once per batch instead of once per row.
+template <int TV4>
+__global__ __launch_bounds__(kPcspThreads) void k_pcsp_accumulate_b(const float* __restrict__ x,
+                                                                   const float* __restrict__ lse_img, int H, int N,
+                                                                   int T, int Tv, int c0, int c1,
+                                                                   float* __restrict__ scores, int accumulate) {
+  constexpr int JB = 4;
+  extern __shared__ float part[];  // [kPcspRows][H]
+  const int g = threadIdx.x >> 4;
+  const int lane = threadIdx.x & 15;
+  const int i0 = blockIdx.x * kPcspRows;
+  const int pairs = kPcspRows * H;
+  for (int pb = g; pb < pairs; pb += kPcspGroups * JB) {
+    float4 v[JB][TV4];
+#pragma unroll
+    for (int jj = 0; jj < JB; ++jj) {
+      const int p = pb + kPcspGroups * jj;
+      const int r = p / H, h = p - r * H, i = i0 + r;
+      const bool ok = p < pairs && i < N;
+      const float* row = x + (static_cast<size_t>(ok ? h : 0) * N + (ok ? i : 0)) * T;
+#pragma unroll
+      for (int c = 0; c < TV4; ++c) {
+        const int t = lane * 4 + 64 * c;
+        v[jj][c] = (ok && t < Tv) ? *reinterpret_cast<const float4*>(row + t)
+                                  : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+      }
+    }
+#pragma unroll
+    for (int jj = 0; jj < JB; ++jj) {
+      const int p = pb + kPcspGroups * jj;
+      if (p >= pairs) break;
+      const int r = p / H, h = p - r * H, i = i0 + r;
+      float contrib = 0.f;
+      if (i < N) {
+        float e[TV4 * 4];
+#pragma unroll
+        for (int c = 0; c < TV4; ++c) {
+          const int t = lane * 4 + 64 * c;
+          e[4 * c + 0] = v[jj][c].x;
+          e[4 * c + 1] = (t + 1 < Tv) ? v[jj][c].y : -INFINITY;
+          e[4 * c + 2] = (t + 2 < Tv) ? v[jj][c].z : -INFINITY;
+          e[4 * c + 3] = (t + 3 < Tv) ? v[jj][c].w : -INFINITY;
+        }
+        // One exponential per logit: with gm the row's text max,
+        //   mass = sum_content e^(x-gm) / (sum_valid e^(x-gm) + e^(lse_img-gm)),
+        // which equals sum_content exp(x - LSE) for LSE = log(exp(lse_img) + sum_valid exp(x)).
+        float m = -INFINITY;
+#pragma unroll
+        for (int q = 0; q < TV4 * 4; ++q) m = fmaxf(m, e[q]);
+        const float gm = group16_max(m);
+        float sum = 0.f, cs = 0.f;
+        if (gm != -INFINITY) {
+          const float gml = gm * kLog2e;
+#pragma unroll
+          for (int c = 0; c < TV4; ++c)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int t = lane * 4 + 64 * c + q;
+              const float ev = __builtin_amdgcn_exp2f(fmaf(e[4 * c + q], kLog2e, -gml));
+              sum += ev;
+              cs += (t >= c0 && t < c1) ? ev : 0.f;
+            }
+        }
+        sum = group16_sum(sum);
+        cs = group16_sum(cs);
+        float den = sum;
+        if (lse_img != nullptr) {
+          const float li = lse_img[static_cast<size_t>(h) * N + i];
+          den += (gm == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f((li - gm) * kLog2e);
+        }
+        contrib = den > 0.f ? cs / den : 0.f;
+      }
+      if (lane == 0) part[r * H + h] = contrib;
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < kPcspRows) {
+    const int i = i0 + threadIdx.x;
+    if (i < N) {
+      float acc = 0.f;
+      for (int h = 0; h < H; ++h) acc += part[threadIdx.x * H + h];
+      scores[i] = accumulate ? scores[i] + acc : acc;
+    }
+  }
+}
+
 hipError_t launch_pcsp_accumulate(const float* x, const float* lse_img, int H, int N, int T, int Tv, int c0, int c1,
                                   float* scores, int accumulate, hipStream_t s) {
   const int blocks = (N + kPcspRows - 1) / kPcspRows;
   const size_t lds = sizeof(float) * kPcspRows * H;
   const bool vec = (T % 4 == 0) && (reinterpret_cast<uintptr_t>(x) % 16 == 0);
-  if (vec)
+  if (vec && Tv <= 256) {
+    const int tv4 = Tv <= 64 ? 1 : Tv <= 128 ? 2 : Tv <= 192 ? 3 : 4;
+    switch (tv4) {
+      case 1: k_pcsp_accumulate_b<1><<<blocks, kPcspThreads, lds, s>>>(x, lse_img, H, N, T, Tv, c0, c1, scores, accumulate); break;
+      case 2: k_pcsp_accumulate_b<2><<<blocks, kPcspThreads, lds, s>>>(x, lse_img, H, N, T, Tv, c0, c1, scores, accumulate); break;
+      case 3: k_pcsp_accumulate_b<3><<<blocks, kPcspThreads, lds, s>>>(x, lse_img, H, N, T, Tv, c0, c1, scores, accumulate); break;
+      default: k_pcsp_accumulate_b<4><<<blocks, kPcspThreads, lds, s>>>(x, lse_img, H, N, T, Tv, c0, c1, scores, accumulate); break;
+    }
+  } else if (vec)
     k_pcsp_accumulate<true><<<blocks, kPcspThreads, lds, s>>>(x, lse_img, H, N, T, Tv, c0, c1, scores, accumulate, H);
   else
     k_pcsp_accumulate<false><<<blocks, kPcspThreads, lds, s>>>(x, lse_img, H, N, T, Tv, c0, c1, scores, accumulate, H);
@@ -106,10 +202,11 @@ hipError_t launch_pcsp_accumulate(const float* x, const float* lse_img, int H, i
 
 // ---------------------------------------------------------------------------------------------
 // Partition: one workgroup of 1024 threads.  Scores map to order-preserving uint32 keys (NaN -> 0,
-// below every number; -0 -> +0).  An MSB-first 8-bit radix select finds the k-th largest key K*;
-// S = {key > K*} plus the lowest-index (k - #greater) entries equal to K*.  Thread t owns the
-// contiguous index chunk [t*E, (t+1)*E), so two block-wide exclusive scans give each index its
-// rank among the equal keys and its slot in S (or C) in ascending index order.
+// below every number; -0 -> +0).  An MSB-first 8-bit radix select finds the k-th largest key K*
+// (coalesced strided passes, LDS histogram, the digit found by one wave with a prefix scan over the
+// 256 bins); S = {key > K*} plus the lowest-index (k - #greater) entries equal to K*.  The output is
+// then written in rounds of 1024 consecutive indices: ballot/popcount block scans give each index its
+// rank among the equal keys and its slot in S (or C), in ascending index order.
 constexpr int kPartThreads = 1024;
 constexpr int kPartWaves = kPartThreads / 64;
 
@@ -120,132 +217,117 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-// Block-wide exclusive scan of one uint32 per thread; also returns the total.
-__device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* wave_tot, uint32_t* total) {
+// Exclusive block prefix count of a per-thread flag and the block total.  wcnt: [kPartWaves] LDS slots
+// used by this call only (alternate two sets between consecutive calls so one barrier suffices).
+__device__ __forceinline__ uint32_t block_flag_scan(bool flag, uint32_t* wcnt, uint32_t* total) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  uint32_t inc = v;
+  const unsigned long long b = __ballot(flag ? 1 : 0);
+  const uint32_t wexcl = static_cast<uint32_t>(__popcll(b & ((1ull << lane) - 1ull)));
+  if (lane == 0) wcnt[w] = static_cast<uint32_t>(__popcll(b));
+  __syncthreads();
+  uint32_t before = 0, tot = 0;
 #pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = __shfl_up(inc, o, 64);
-    if (lane >= o) inc += y;
+  for (int j = 0; j < kPartWaves; ++j) {
+    const uint32_t c = wcnt[j];
+    before += (j < w) ? c : 0u;
+    tot += c;
   }
-  if (lane == 63) wave_tot[w] = inc;
-  __syncthreads();
-  if (w == 0) {
-    uint32_t t = lane < kPartWaves ? wave_tot[lane] : 0u;
-    uint32_t ti = t;
-#pragma unroll
-    for (int o = 1; o < kPartWaves; o <<= 1) {
-      const uint32_t y = __shfl_up(ti, o, 64);
-      if (lane >= o) ti += y;
-    }
-    if (lane < kPartWaves) wave_tot[kPartWaves + lane] = ti - t;  // exclusive wave offsets
-    if (lane == kPartWaves - 1) wave_tot[2 * kPartWaves] = ti;
-  }
-  __syncthreads();
-  const uint32_t r = wave_tot[kPartWaves + w] + inc - v;
-  *total = wave_tot[2 * kPartWaves];
-  __syncthreads();
-  return r;
+  *total = tot;
+  return before + wexcl;
 }
 
 __global__ __launch_bounds__(kPartThreads) void k_partition(const float* __restrict__ scores, int N, int k,
                                                             int32_t* __restrict__ S, int32_t* __restrict__ C,
                                                             uint8_t* __restrict__ is_sens, float* __restrict__ s01) {
   __shared__ uint32_t hist[256];
-  __shared__ uint32_t wave_tot[2 * kPartWaves + 1];
+  __shared__ uint32_t wcnt[4][kPartWaves];
   __shared__ uint32_t sel_digit, sel_above;
   __shared__ float red_lo[kPartWaves], red_hi[kPartWaves];
-  const int tid = threadIdx.x;
-  const int E = (N + kPartThreads - 1) / kPartThreads;
-  const int beg = min(N, tid * E), end = min(N, beg + E);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+
+  // ---- min / max over non-NaN scores for s01
+  float lo = INFINITY, hi = -INFINITY;
+  if (s01 != nullptr) {
+    for (int i = tid; i < N; i += kPartThreads) { const float a = scores[i]; lo = fminf(lo, a); hi = fmaxf(hi, a); }
+    for (int o = 32; o >= 1; o >>= 1) { lo = fminf(lo, __shfl_xor(lo, o, 64)); hi = fmaxf(hi, __shfl_xor(hi, o, 64)); }
+    if (lane == 0) { red_lo[w] = lo; red_hi[w] = hi; }
+    __syncthreads();
+    lo = red_lo[0]; hi = red_hi[0];
+    for (int j = 1; j < kPartWaves; ++j) { lo = fminf(lo, red_lo[j]); hi = fmaxf(hi, red_hi[j]); }
+  }
+  const bool all_nan = !(lo <= hi);
 
   // ---- radix select of the k-th largest key (skipped when k == 0)
   uint32_t prefix = 0, pmask = 0, remaining = static_cast<uint32_t>(k);
   if (k > 0) {
     for (int shift = 24; shift >= 0; shift -= 8) {
-      for (int j = tid; j < 256; j += kPartThreads) hist[j] = 0;
+      if (tid < 256) hist[tid] = 0;
       __syncthreads();
-      for (int i = beg; i < end; ++i) {
+      for (int i = tid; i < N; i += kPartThreads) {
         const uint32_t key = order_key(scores[i]);
         if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
       }
       __syncthreads();
-      if (tid == 0) {
-        uint32_t above = 0;
-        int dsel = 0;
-        for (int dgt = 255; dgt >= 0; --dgt) {
-          if (above + hist[dgt] >= remaining) { dsel = dgt; break; }
-          above += hist[dgt];
+      if (w == 0) {
+        // lane l owns bins 255-4l .. 252-4l (descending); find where the running count from the top
+        // first reaches `remaining`
+        uint32_t c[4], loc = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) { c[j] = hist[255 - 4 * lane - j]; loc += c[j]; }
+        uint32_t inc = loc;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const uint32_t y = __shfl_up(inc, o, 64);
+          if (lane >= o) inc += y;
         }
-        sel_digit = static_cast<uint32_t>(dsel);
-        sel_above = above;
+        const uint32_t exc = inc - loc;
+        if (exc < remaining && remaining <= inc) {
+          uint32_t acc = exc;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            if (acc + c[j] >= remaining) { sel_digit = 255u - 4u * lane - j; sel_above = acc; break; }
+            acc += c[j];
+          }
+        }
       }
       __syncthreads();
       remaining -= sel_above;
       prefix |= sel_digit << shift;
       pmask |= 255u << shift;
-      __syncthreads();
     }
   }
   const uint32_t kstar = prefix;
   const uint32_t need = (k > 0) ? remaining : 0u;  // how many keys equal to K* are taken
 
-  // ---- rank among equal keys, in index order
-  uint32_t neq = 0;
-  if (k > 0)
-    for (int i = beg; i < end; ++i) neq += (order_key(scores[i]) == kstar) ? 1u : 0u;
-  uint32_t tot;
-  const uint32_t eq_base = block_exclusive_scan(neq, wave_tot, &tot);
-
-  // ---- selection flags and their count per chunk
-  uint32_t nsel = 0;
-  {
-    uint32_t er = eq_base;
-    for (int i = beg; i < end; ++i) {
-      const uint32_t key = order_key(scores[i]);
-      bool sel = false;
-      if (k > 0) {
-        if (key > kstar) sel = true;
-        else if (key == kstar) { sel = er < need; ++er; }
-      }
-      nsel += sel ? 1u : 0u;
-    }
-  }
-  const uint32_t s_base = block_exclusive_scan(nsel, wave_tot, &tot);
-
-  // ---- min / max over non-NaN scores for s01
-  float lo = INFINITY, hi = -INFINITY;
-  if (s01 != nullptr) {
-    for (int i = beg; i < end; ++i) { const float a = scores[i]; lo = fminf(lo, a); hi = fmaxf(hi, a); }
-    for (int o = 32; o >= 1; o >>= 1) { lo = fminf(lo, __shfl_xor(lo, o, 64)); hi = fmaxf(hi, __shfl_xor(hi, o, 64)); }
-    if ((tid & 63) == 0) { red_lo[tid >> 6] = lo; red_hi[tid >> 6] = hi; }
-    __syncthreads();
-    lo = red_lo[0]; hi = red_hi[0];
-    for (int w = 1; w < kPartWaves; ++w) { lo = fminf(lo, red_lo[w]); hi = fmaxf(hi, red_hi[w]); }
-  }
-  const bool all_nan = !(lo <= hi);
-
-  // ---- write S, C, is_sens, s01
-  uint32_t er = eq_base, sp = s_base;
-  for (int i = beg; i < end; ++i) {
-    const float a = scores[i];
+  // ---- output in rounds of 1024 consecutive indices
+  uint32_t run_eq = 0, run_s = 0;
+  int set = 0;
+  for (int base = 0; base < N; base += kPartThreads) {
+    const int i = base + tid;
+    const bool valid = i < N;
+    const float a = valid ? scores[i] : 0.f;
     const uint32_t key = order_key(a);
-    bool sel = false;
-    if (k > 0) {
-      if (key > kstar) sel = true;
-      else if (key == kstar) { sel = er < need; ++er; }
+    const bool eq = valid && k > 0 && key == kstar;
+    const bool gt = valid && k > 0 && key > kstar;
+    uint32_t eq_tot, s_tot;
+    const uint32_t eq_rank = run_eq + block_flag_scan(eq, wcnt[set], &eq_tot);
+    const bool sel = gt || (eq && eq_rank < need);
+    const uint32_t s_pos = run_s + block_flag_scan(sel, wcnt[set + 1], &s_tot);
+    set ^= 2;
+    if (valid) {
+      if (sel) S[s_pos] = i;
+      else C[static_cast<uint32_t>(i) - s_pos] = i;
+      is_sens[i] = sel ? 1 : 0;
+      if (s01 != nullptr) {
+        float v;
+        if (a != a || all_nan) v = NAN;
+        else if (hi > lo) v = (a - lo) / (hi - lo);
+        else v = 0.f;
+        s01[i] = v;
+      }
     }
-    if (sel) S[sp++] = i;
-    else C[static_cast<uint32_t>(i) - sp] = i;
-    is_sens[i] = sel ? 1 : 0;
-    if (s01 != nullptr) {
-      float v;
-      if (a != a || all_nan) v = NAN;
-      else if (hi > lo) v = (a - lo) / (hi - lo);
-      else v = 0.f;
-      s01[i] = v;
-    }
+    run_eq += eq_tot;
+    run_s += s_tot;
   }
 }
 
