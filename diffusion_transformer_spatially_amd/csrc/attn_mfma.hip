@@ -34,6 +34,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
@@ -117,12 +118,153 @@ struct WaveState {
   float l[QB];       // running row sum of exp2((s - m) * c2), lane-half partial
 };
 
+// Fast path (no lse, no emission): Q was pre-multiplied by scale * log2(e) and rounded to bf16 once, so
+// the logits come out of the MFMA in log2 units, and each tile's logit accumulators start at -m (two
+// 64-bit moves per four registers), so the MFMA output is already s - m and each probability costs a
+// single exp2 instead of an fma and an exp2.  Rounding the scaled Q to bf16 perturbs a logit by about
+// 2^-9 of the root-sum-square of its products, below the bf16 rounding of the probabilities
+// themselves.  The lazy running max and its exact path are as in the general step below (m is kept in
+// log2 units here).
+template <int QB, bool MASKED>
+__device__ __forceinline__ void tile_step_fast(WaveState<QB>& st, const uint16_t* kl, const uint16_t* vl, int kperm,
+                                               int g, int li, int dc0, int nvalid) {
+  f32x16 s[QB][2];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const double nm2 = __builtin_bit_cast(double, (f32x2){-st.m[qb], -st.m[qb]});
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      double d[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) d[i] = nm2;
+      s[qb][kb] = __builtin_bit_cast(f32x16, d);
+    }
+  }
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    const int key = kb * 32 + kperm;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kl + lds_off(key, 2 * ks + g));
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+        s[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, st.q[qb][ks], s[qb][kb], 0, 0, 0);
+    }
+  }
+  if (MASKED) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[qb][kb][i] = (kb * 32 + 16 * g + i) < nvalid ? s[qb][kb][i] : -INFINITY;
+  }
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  bf16x8 p[QB][2][2];
+  float tl[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    float tsum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int mm = 0; mm < 2; ++mm) {
+        uint32_t pk[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          pk[e] = pack_bf16x2(__builtin_amdgcn_exp2f(s[qb][kb][8 * mm + 2 * e]),
+                              __builtin_amdgcn_exp2f(s[qb][kb][8 * mm + 2 * e + 1]));
+          tsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[e]), ones, tsum, false);
+        }
+        p[qb][kb][mm] = __builtin_bit_cast(bf16x8, (uint4){pk[0], pk[1], pk[2], pk[3]});
+      }
+    tl[qb] = tsum;
+  }
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    if (__any(!(tl[qb] <= 65536.f))) {
+      f32x16 sx[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int key = kb * 32 + kperm;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kl + lds_off(key, 2 * ks + g));
+          sx[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, st.q[qb][ks], ks == 0 ? (f32x16){} : sx[kb], 0, 0, 0);
+        }
+      }
+      if (MASKED) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) sx[kb][i] = (kb * 32 + 16 * g + i) < nvalid ? sx[kb][i] : -INFINITY;
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sx[kb][i]);
+      mx = fmaxf(mx, swap_halves(mx));
+      const float mnew = fmaxf(st.m[qb], mx);
+      if (mnew > st.m[qb]) {
+        const float alpha = __builtin_amdgcn_exp2f(st.m[qb] - mnew);
+        st.l[qb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) st.o[qb][db][i] *= alpha;
+        st.m[qb] = mnew;
+      }
+      const float m = st.m[qb];
+      float tsum = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int mm = 0; mm < 2; ++mm) {
+          uint32_t pk[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            pk[e] = pack_bf16x2(__builtin_amdgcn_exp2f(sx[kb][8 * mm + 2 * e] - m),
+                                __builtin_amdgcn_exp2f(sx[kb][8 * mm + 2 * e + 1] - m));
+            tsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[e]), ones, tsum, false);
+          }
+          p[qb][kb][mm] = __builtin_bit_cast(bf16x8, (uint4){pk[0], pk[1], pk[2], pk[3]});
+        }
+      tl[qb] = tsum;
+    }
+    st.l[qb] += tl[qb];
+  }
+  lds_u16* vl3 = (lds_u16*)(vl);
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+    for (int mm = 0; mm < 2; ++mm) {
+      const int key = kb * 32 + 16 * g + 8 * mm + (li >> 2);
+#pragma unroll
+      for (int db = 0; db < 2; ++db) {
+        const int col = db * 32 + dc0 + 4 * (li & 3);
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vl3 + lds_off(key, col >> 3) + (col & 4)));
+        const s16x4 hi =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vl3 + lds_off(key + 4, col >> 3) + (col & 4)));
+        const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+          st.o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, p[qb][kb][mm], st.o[qb][db], 0, 0, 0);
+      }
+    }
+  }
+}
+
 // One 64-key tile: logits, online softmax, P V.  MASKED handles partial tiles (keys >= nvalid are
 // -inf) and the optional store of the tile's logits (text tiles of the warmup emission).
 template <int QB, bool MASKED, bool EXACT_SUM>
 __device__ __forceinline__ void tile_step(WaveState<QB>& st, const uint16_t* kl, const uint16_t* vl, int kperm,
                                           int g, int li, int dc0, float c2, int nvalid, float* const (&xo)[QB],
                                           float scale) {
+  if constexpr (!EXACT_SUM) {
+    tile_step_fast<QB, MASKED>(st, kl, vl, kperm, g, li, dc0, nvalid);
+    return;
+  }
   // ---- S^T = K Q^T
   f32x16 s[QB][2];
 #pragma unroll
@@ -345,6 +487,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const int ntiles = n_img + n_txt;
   const bool emit = b == 0 && (a.xattn_out != nullptr || a.lse_img_out != nullptr);
   const float c2 = a.scale * kLog2e;
+  if constexpr (!EXACT_SUM) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const f32x8 qf = __builtin_convertvector(st.q[qb][ks], f32x8) * c2;
+        st.q[qb][ks] = __builtin_convertvector(qf, bf16x8);
+      }
+    }
+  }
   // K rows fed to the MFMA: A-row R reads key kb*32 + 16*((R>>2)&1) + 4*(R>>3) + (R&3), which makes
   // output register r of lane half g hold key 16*g + r.
   const int kperm = 16 * ((qi >> 2) & 1) + 4 * (qi >> 3) + (qi & 3);
@@ -431,7 +583,7 @@ static void launch_sum(const AttnArgs& a, hipStream_t s) {
   // The row sum accumulates the bf16-rounded probabilities (v_dot2, exactly the values the P V
   // product uses) unless a log-sum-exp output is requested; then it sums the fp32 probabilities so
   // that lse / lse_img keep fp32 accuracy (they feed the sensitivity scores).
-  const bool exact = a.lse != nullptr || a.lse_img_out != nullptr;
+  const bool exact = a.lse != nullptr || a.lse_img_out != nullptr || a.xattn_out != nullptr;
   if (exact) launch<GATHER, QB, true>(a, s);
   else launch<GATHER, QB, false>(a, s);
 }

@@ -1,0 +1,68 @@
+"""The attention step's main-stream work (PCSP aggregation, partition, dense and sensitive-row attention,
+gather, scatter, guidance combine) captured once in a HIP graph and replayed: every replay must equal
+the eager run bit for bit.  Replays are interleaved with eager work and synchronisations, and every
+output is poisoned before each replay, so a replay that skipped or reordered a node would show."""
+import numpy as np
+import pytest
+
+import synthetic as syn
+from tests.gpu_util import torch
+
+pytestmark = pytest.mark.gpu
+
+
+def test_step_graph_replays_match_eager(lib):
+    t = torch()
+    w = syn.WORKLOADS["srsu_1024"]
+    N, k, Tv = w.N, w.k, w.tv[0]
+    inp = syn.attention_inputs(w)
+    bf = lambda n: t.from_numpy(inp[n + "_bits"].view(np.int16)).view(t.bfloat16).cuda()
+    q, ki, vi, kt, vt = (bf(n) for n in ("q", "k_img", "v_img", "k_txt", "v_txt"))
+    x = syn.pcsp_logits(w)
+    xd, lid = t.from_numpy(x["x"]).cuda(), t.from_numpy(x["lse_img"]).cuda()
+    eps = t.from_numpy(syn.latent_eps(w)).cuda()
+    state = t.empty_like(q)
+    scores = t.empty(N, dtype=t.float32, device="cuda")
+    S = t.empty(k, dtype=t.int32, device="cuda")
+    C = t.empty(N - k, dtype=t.int32, device="cuda")
+    isn = t.empty(N, dtype=t.uint8, device="cuda")
+    s01 = t.empty(N, dtype=t.float32, device="cuda")
+    packed = t.empty((w.B, w.H, k, w.d), dtype=t.bfloat16, device="cuda")
+    cfg = t.empty(eps.shape[1:], dtype=t.float32, device="cuda")
+    outs = (scores, S, C, isn, s01, state, packed, cfg)
+
+    def poison():
+        for o in outs:
+            o.fill_(3 if o.dtype in (t.int32, t.uint8) else -1.5)
+
+    def work():
+        lib.safe_pcsp_accumulate(xd, lid, Tv, 0, Tv, scores, False)
+        lib.safe_pcsp_partition(scores, k, S, C, isn, s01)
+        lib.safe_attn_dense(q, ki, vi, kt, vt, w.tv, state)
+        lib.safe_attn_rows(q, ki, vi, kt, vt, w.tv, S, state)
+        lib.safe_gather_rows(state, S, packed)
+        lib.safe_scatter_rows(packed, S, state)
+        lib.safe_swcfg_combine(eps, s01, w.side, w.g_ctx, w.g_sens, cfg)
+
+    poison()
+    work()
+    t.cuda.synchronize()
+    ref = [o.clone() for o in outs]
+
+    g = t.cuda.CUDAGraph()
+    poison()
+    t.cuda.synchronize()
+    with t.cuda.graph(g):
+        work()
+    t.cuda.synchronize()
+    for rep in range(4):
+        poison()
+        t.cuda.synchronize()
+        g.replay()
+        t.cuda.synchronize()
+        for i, (o, r) in enumerate(zip(outs, ref)):
+            assert t.equal(o, r), (rep, i)
+        poison()
+        work()  # eager work between replays
+        t.cuda.synchronize()
+        assert t.equal(state, ref[5])

@@ -116,9 +116,11 @@ def test_mask_check_dense_1024_all_valid(lib):
     f[0, 0, 17, 3] = -0.0
     ok, c = _check(lib, f, w.N, w.T, w.tv)
     assert ok and np.all(c == 0)
+    assert _check(lib, f, w.N, w.T, w.tv, want_c=False)[0]
     f[0, 0, 17, 3] = 1e-30
     ok, c = _check(lib, f, w.N, w.T, w.tv)
     assert not ok and np.isnan(c[17]) and np.sum(np.isnan(c)) == 1
+    assert not _check(lib, f, w.N, w.T, w.tv, want_c=False)[0]
 
 
 def test_mask_check_srsu_2560_all_valid(lib):
@@ -135,10 +137,13 @@ def test_mask_check_unaligned_row_lengths(lib):
         m = np.zeros((1, 2, N, cols), dtype=np.float32)
         ok, c = _check(lib, m, N, T, (3,))
         assert ok
+        assert _check(lib, m, N, T, (3,), want_c=False)[0]
         m[0, 1, 28, cols - 1] = 2.0
         ok, c = _check(lib, m, N, T, (3,))
         assert not ok and np.isnan(c[N + 28])
+        assert not _check(lib, m, N, T, (3,), want_c=False)[0]
         mb = np.ones((1, 1, N, cols), dtype=np.bool_)
         mb[0, 0, 3, cols - 1] = False
-        assert not _check(lib, mb, N, T, (3,))[0]
-        assert _check(lib, mb, N, T, (0,))[0] == (cols == N + T)
+        for want_c in (True, False):
+            assert not _check(lib, mb, N, T, (3,), want_c=want_c)[0]
+            assert _check(lib, mb, N, T, (0,), want_c=want_c)[0] == (cols == N + T)
