@@ -130,6 +130,9 @@ def main():
             else:
                 fn()
         elided = []
+        if record:
+            # no overlap in the timed eager pass: each kernel's events see it alone on the GPU
+            torch.cuda.current_stream().synchronize()
         mark("mask_check", lambda: elided.append(check()), on=side)
         work(None if elided[0] else mask, mark)
 
@@ -144,7 +147,8 @@ def main():
     ms_per_step = 1e3 * elapsed / args.steps
 
     # Per-kernel durations: HIP events around each launch on its stream, in an eager pass of the same
-    # steps (events cannot sit inside the graph).
+    # steps (events cannot sit inside the graph), with each step's check started only once the previous
+    # step's kernels have finished, so that no kernel shares the GPU with another.
     for _ in range(args.warmup):
         eager_step(False)
     torch.cuda.synchronize()
@@ -189,7 +193,8 @@ def main():
         "ms_per_step": ms_per_step,
         "ms_per_step_eager": ms_per_step_eager,
         "timing": "wall clock of K whole steps (check + graph replay of the main-stream kernels); kernel "
-                  "durations and the roofline from HIP events in an eager pass of the same steps",
+                  "durations and the roofline from HIP events in an eager pass of the same steps, run "
+                  "without overlap between steps",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

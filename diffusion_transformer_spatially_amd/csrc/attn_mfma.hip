@@ -88,11 +88,19 @@ __device__ __forceinline__ TileSrc tile_src(const AttnArgs& a, size_t bh, int t,
 // the global address of each lane is chosen to land its chunk in that slot.  Rows past nvalid are
 // clamped to the last valid row (never read out of bounds, never read padded text); the softmax
 // masks those keys to -inf and their probabilities are exactly 0.
+//
+// OPAQUE (used with two query blocks per wave, where registers are scarce): the wave's first slot goes
+// through an empty asm, so the compiler cannot treat the LDS destinations derived from it as loop
+// invariants; it recomputes them per tile (two scalar adds) instead of hoisting all of them out of the
+// tile loop, where they were spilled and each reload waited for the tile copies already in flight.
+template <bool OPAQUE>
 __device__ __forceinline__ void stage_issue(const TileSrc& s, uint16_t* kl, uint16_t* vl) {
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int lane = threadIdx.x & 63;
+  int wslot = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6)) * 64;
+  if (OPAQUE) asm volatile("" : "+s"(wslot));
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
-    const int base = (u * kWaves + w) * 64;  // first slot of this wave instruction
+    const int base = u * kWaves * 64 + wslot;  // first slot of this wave instruction
     const int p = base + lane;
     const int row = p >> 3;
     const int c = (p & 7) ^ swz(row);
@@ -501,7 +509,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   // output register r of lane half g hold key 16*g + r.
   const int kperm = 16 * ((qi >> 2) & 1) + 4 * (qi >> 3) + (qi & 3);
 
-  stage_issue(tile_src(a, bh, 0, n_img, tv), k_a, v_a);
+  stage_issue<(QB > 1)>(tile_src(a, bh, 0, n_img, tv), k_a, v_a);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
@@ -509,14 +517,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   // One tile: prefetch tile t+1 into the other buffer, compute on this one, then wait for the
   // prefetch and synchronise.
   auto full_tile = [&](int t, const uint16_t* ck, const uint16_t* cv, uint16_t* nk, uint16_t* nv) {
-    if (t + 1 < ntiles) stage_issue(tile_src(a, bh, t + 1, n_img, tv), nk, nv);
+    if (t + 1 < ntiles) stage_issue<(QB > 1)>(tile_src(a, bh, t + 1, n_img, tv), nk, nv);
     tile_step<QB, false, EXACT_SUM>(st, ck, cv, kperm, g, li, dc0, c2, kBN, no_store, a.scale);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
   auto masked_tile = [&](int t, const uint16_t* ck, const uint16_t* cv, uint16_t* nk, uint16_t* nv) {
     if (emit && t == n_img && a.lse_img_out != nullptr) store_lse_img(a, st, h, row, valid, g);
-    if (t + 1 < ntiles) stage_issue(tile_src(a, bh, t + 1, n_img, tv), nk, nv);
+    if (t + 1 < ntiles) stage_issue<(QB > 1)>(tile_src(a, bh, t + 1, n_img, tv), nk, nv);
     const bool txt = t >= n_img;
     const int nvalid = txt ? min(kBN, tv - (t - n_img) * kBN) : min(kBN, a.N - t * kBN);
     float* xo[QB];

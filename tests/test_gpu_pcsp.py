@@ -33,11 +33,24 @@ def _check_exact(lib, a32: np.ndarray, k: int):
     assert np.max(np.abs(s01[fin] - rs[fin]), initial=0.0) <= 2e-7
 
 
-@pytest.mark.parametrize("N,k", [(1, 0), (1, 1), (7, 3), (1000, 1), (1000, 999), (4096, 1229), (25600, 5120),
-                                 (36864, 7373), (70000, 12345)])
+@pytest.mark.parametrize("N,k", [(1, 0), (1, 1), (7, 3), (1000, 1), (1000, 999), (4096, 1229), (16384, 8000),
+                                 (16385, 16385), (25600, 5120), (36864, 7373), (70000, 12345)])
 def test_partition_exact_random(lib, N, k):
     a = np.random.default_rng(N + k).random(N).astype(np.float32)
     _check_exact(lib, a, k)
+
+
+@pytest.mark.parametrize("N", [3000, 20000])
+def test_partition_exact_mixed_signs_and_all_nan(lib, N):
+    r = np.random.default_rng(N)
+    a = (r.standard_normal(N) * 3).astype(np.float32)
+    a[r.integers(0, N, N // 50)] = np.nan
+    for k in (1, N // 3, N - 1):
+        _check_exact(lib, a, k)
+    allnan = np.full(N, np.nan, dtype=np.float32)
+    S, C, isn, s = _partition(lib, allnan, 10)
+    rS, rC, _, _ = OP.partition(allnan.astype(np.float64), 10)
+    assert np.array_equal(S, rS) and np.array_equal(C, rC) and np.all(np.isnan(s))
 
 
 @pytest.mark.parametrize("levels", [1, 2, 5, 300])
