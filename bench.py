@@ -157,7 +157,7 @@ def main():
         eager_step(True)
     torch.cuda.synchronize()
     ms_per_step_eager = 1e3 * (time.perf_counter() - t0) / args.steps
-    avg_ms = {s: float(np.mean([a.elapsed_time(b) for a, b in ev[s]])) for s in stages}
+    avg_ms = {s: float(np.median([a.elapsed_time(b) for a, b in ev[s]])) for s in stages}  # median per launch
 
     attn_flops = w.flops_dense + w.flops_rows
     value = attn_flops / (ms_per_step * 1e-3) / 1e12
@@ -171,16 +171,18 @@ def main():
     gs_bytes = 2 * 2.0 * B * H * k * d
     mask_bytes = 1.0 * N * N
     gbs = lambda b, ms: b / (ms * 1e-3) / 1e9
+    hbm = lambda b, ms: {"ms": ms, "gbs": gbs(b, ms), "frac_hbm": gbs(b, ms) / HBM_PEAK_GBS, "bytes": b}
     breakdown = {
         "attn_dense": {"ms": avg_ms["attn_dense"], "tflops": dense_tf, "frac_mfma": dense_tf / MFMA_BF16_PEAK_TFLOPS},
         "attn_rows": {"ms": avg_ms["attn_rows"], "tflops": rows_tf, "frac_mfma": rows_tf / MFMA_BF16_PEAK_TFLOPS},
-        "pcsp_accumulate": {"ms": avg_ms["pcsp_accumulate"], "gbs": gbs(pcsp_bytes, avg_ms["pcsp_accumulate"])},
-        "pcsp_partition": {"ms": avg_ms["pcsp_partition"]},
-        "swcfg_combine": {"ms": avg_ms["swcfg_combine"], "gbs": gbs(cfg_bytes, avg_ms["swcfg_combine"])},
-        "gather_rows": {"ms": avg_ms["gather_rows"], "gbs": gbs(gs_bytes, avg_ms["gather_rows"])},
-        "scatter_rows": {"ms": avg_ms["scatter_rows"], "gbs": gbs(gs_bytes, avg_ms["scatter_rows"])},
-        "mask_check": {"ms": avg_ms["mask_check"], "gbs": gbs(mask_bytes, avg_ms["mask_check"]),
-                       "note": "synchronous (host verdict), includes the device-to-host copy"},
+        "pcsp_accumulate": hbm(pcsp_bytes, avg_ms["pcsp_accumulate"]),
+        "pcsp_partition": {"ms": avg_ms["pcsp_partition"], "note": "one workgroup: latency-bound, no roofline"},
+        "swcfg_combine": hbm(cfg_bytes, avg_ms["swcfg_combine"]),
+        "gather_rows": hbm(gs_bytes, avg_ms["gather_rows"]),
+        "scatter_rows": hbm(gs_bytes, avg_ms["scatter_rows"]),
+        "mask_check": dict(hbm(mask_bytes, avg_ms["mask_check"]),
+                           note="synchronous (host verdict), includes the device-to-host copy"),
+        "stat": "median over the timed launches",
     }
 
     result = {
@@ -239,6 +241,7 @@ def main():
                                     "dense_frac_mfma": tfd / MFMA_BF16_PEAK_TFLOPS,
                                     "rows_ms": timing["rows"], "rows_tflops": tfr,
                                     "rows_frac_mfma": tfr / MFMA_BF16_PEAK_TFLOPS}
+        result["hbm_large"] = hbm_large(dts, torch, np, syn, dev, lout, lrows, hbm)
         del lq, lki, lvi, lkt, lvt, lout
 
     if args.copy_calibration:
@@ -252,7 +255,82 @@ def main():
     # ---------------------------------------------------------------- oracle on the host cores
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
+        result["cpu_oracle_other_stages"] = cpu_other_stages(w, x, syn)
     print(json.dumps(result), flush=True)
+
+
+def time_launches(torch, fn, reps=20):
+    """Median duration (ms) of `reps` launches, each bracketed by its own HIP events."""
+    import numpy as np
+    fn()
+    torch.cuda.synchronize()
+    pairs = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        pairs.append((e0, e1))
+    torch.cuda.synchronize()
+    return float(np.median([a.elapsed_time(b) for a, b in pairs]))
+
+
+def hbm_large(dts, torch, np, syn, dev, state, rows, hbm):
+    """The HBM-bound stages on the 2560^2 / 3072^2 shapes (working sets of tens to hundreds of MB, far
+    beyond the launch-overhead regime of the 1024^2 step), and a plain device copy as the measured
+    HBM ceiling."""
+    wl, w5 = syn.WORKLOADS["srsu_2560"], syn.WORKLOADS["traj_3072"]
+    g = torch.Generator(device=dev)
+    g.manual_seed(wl.seed + 100)
+    out = {}
+    H, N, T, Tv = wl.H, wl.N, wl.T, wl.tv[0]
+    x = torch.randn((H, N, T), generator=g, device=dev)
+    li = torch.randn((H, N), generator=g, device=dev) + float(np.log(N))
+    sc = torch.empty(N, dtype=torch.float32, device=dev)
+    out["pcsp_accumulate_2560"] = hbm(4.0 * H * N * Tv + 4.0 * H * N + 4.0 * N,
+                                      time_launches(torch, lambda: dts.safe_pcsp_accumulate(x, li, Tv, 0, Tv, sc, False)))
+    del x, li
+    S = torch.empty(wl.k, dtype=torch.int32, device=dev)
+    C = torch.empty(N - wl.k, dtype=torch.int32, device=dev)
+    isn = torch.empty(N, dtype=torch.uint8, device=dev)
+    s01 = torch.empty(N, dtype=torch.float32, device=dev)
+    out["pcsp_partition_2560"] = {"ms": time_launches(torch, lambda: dts.safe_pcsp_partition(sc, wl.k, S, C, isn, s01)),
+                                  "note": "one workgroup over N=25600: latency-bound, no roofline"}
+    packed = torch.empty((wl.B, wl.H, wl.k, wl.d), dtype=torch.bfloat16, device=dev)
+    gs = 2 * 2.0 * wl.B * wl.H * wl.k * wl.d
+    out["gather_rows_2560"] = hbm(gs, time_launches(torch, lambda: dts.safe_gather_rows(state, rows, packed)))
+    out["scatter_rows_2560"] = hbm(gs, time_launches(torch, lambda: dts.safe_scatter_rows(packed, rows, state)))
+    C5, Hl, Wl = w5.latent
+    eps = torch.randn((2, C5, Hl, Wl), generator=g, device=dev)
+    s5 = torch.rand(w5.N, generator=g, device=dev)
+    cout = torch.empty((C5, Hl, Wl), dtype=torch.float32, device=dev)
+    out["swcfg_combine_3072"] = hbm(3 * 4.0 * C5 * Hl * Wl + 4.0 * w5.N,
+                                    time_launches(torch, lambda: dts.safe_swcfg_combine(eps, s5, w5.side, w5.g_ctx,
+                                                                                         w5.g_sens, cout)))
+    src = torch.empty(256 << 20, dtype=torch.float32, device=dev).fill_(1.0)  # 1 GiB
+    dst = torch.empty_like(src)
+    out["device_copy_1GiB"] = hbm(2.0 * src.numel() * 4, time_launches(torch, lambda: dst.copy_(src), reps=10))
+    out["note"] = ("shapes: PCSP x [24,25600,256] fp32 (Tv=120 valid), partition N=25600 k=5120, gather/scatter "
+                   "[2,24,25600,64] bf16 k=5120, SW-CFG [2,16,384,384] fp32; device_copy_1GiB is the measured ceiling")
+    return out
+
+
+def cpu_other_stages(w, x, syn):
+    """The fp64 oracle of the non-attention stages of the step, in full, on the step's own inputs."""
+    import numpy as np
+    from oracle import pcsp as OP, swcfg as OS
+    t0 = time.perf_counter()
+    a = OP.scores(x["x"].astype(np.float64), x["lse_img"].astype(np.float64), w.tv[0], 0, w.tv[0])
+    t1 = time.perf_counter()
+    OP.partition(a, w.k)
+    t2 = time.perf_counter()
+    s = OP.normalise(a)
+    eps = syn.latent_eps(w).astype(np.float64)
+    t3 = time.perf_counter()
+    OS.combine(eps, s, w.side, w.g_ctx, w.g_sens)
+    t4 = time.perf_counter()
+    return {"pcsp_accumulate_ms": 1e3 * (t1 - t0), "pcsp_partition_ms": 1e3 * (t2 - t1),
+            "swcfg_combine_ms": 1e3 * (t4 - t3), "kind": "oracle", "sample": "srsu_1024 stages in full"}
 
 
 def profiled_traffic():

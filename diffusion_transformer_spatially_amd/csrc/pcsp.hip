@@ -100,7 +100,7 @@ __global__ __launch_bounds__(kPcspThreads) void k_pcsp_accumulate_b(const float*
                                                                    const float* __restrict__ lse_img, int H, int N,
                                                                    int T, int Tv, int c0, int c1,
                                                                    float* __restrict__ scores, int accumulate) {
-  constexpr int JB = 4;
+  constexpr int JB = 6;  // 16 groups x 6 = 96 (row, head) pairs: one pass of loads covers 4 rows x 24 heads
   extern __shared__ float part[];  // [kPcspRows][H]
   const int g = threadIdx.x >> 4;
   const int lane = threadIdx.x & 15;

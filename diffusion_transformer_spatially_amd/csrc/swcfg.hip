@@ -1,30 +1,45 @@
 // SW-CFG combine (SAFE-DiT technical summary, Methodology 4; AccelAes summary B.2, spatial CFG):
 // gamma_i = g_ctx + (g_sens - g_ctx) s_i per token, out = eps_u + gamma (eps_c - eps_u) per latent
 // pixel.  Elementwise and HBM-bound: 8 bytes read and 4 written per pixel, float4 vectors along x.
+// The pixel -> token index arithmetic must stay cheaper than the memory traffic, so the vector path
+// divides through float reciprocals (exactly, see fdiv) instead of 32-bit integer divisions.
 #include "common.hpp"
 
 namespace safe {
 
 __device__ __forceinline__ float guided(float ec, float eu, float g) { return fmaf(g, ec - eu, eu); }
 
+// floor(a / b) for a < 2^24 without an integer divide: the float quotient is off by at most one, and
+// one exact integer comparison each way fixes it.
+struct FastDiv {
+  uint32_t b;
+  float inv;
+};
+__device__ __forceinline__ uint32_t fdiv(uint32_t a, FastDiv d) {
+  uint32_t q = static_cast<uint32_t>(static_cast<float>(a) * d.inv);
+  q -= (q * d.b > a) ? 1u : 0u;
+  q += ((q + 1u) * d.b <= a) ? 1u : 0u;
+  return q;
+}
+
 __global__ __launch_bounds__(256) void k_swcfg_vec(const float4* __restrict__ ec4, const float4* __restrict__ eu4,
-                                                   const float* __restrict__ sv, uint32_t Wl4, uint32_t Hl,
-                                                   uint32_t side, uint32_t ph, uint32_t pw, float g_ctx, float g_d,
+                                                   const float* __restrict__ sv, FastDiv wl4, FastDiv hl,
+                                                   uint32_t side, FastDiv ph, FastDiv pw, float g_ctx, float g_d,
                                                    float4* __restrict__ out4, uint32_t total4) {
-  const uint32_t stride = gridDim.x * blockDim.x;
-  for (uint32_t e = blockIdx.x * blockDim.x + threadIdx.x; e < total4; e += stride) {
-    const uint32_t x0 = (e % Wl4) * 4;
-    const uint32_t y = (e / Wl4) % Hl;
-    const uint32_t trow = (y / ph) * side;
-    const float4 c = ec4[e];
-    const float4 u = eu4[e];
-    float4 o;
-    o.x = guided(c.x, u.x, fmaf(g_d, sv[trow + (x0 + 0) / pw], g_ctx));
-    o.y = guided(c.y, u.y, fmaf(g_d, sv[trow + (x0 + 1) / pw], g_ctx));
-    o.z = guided(c.z, u.z, fmaf(g_d, sv[trow + (x0 + 2) / pw], g_ctx));
-    o.w = guided(c.w, u.w, fmaf(g_d, sv[trow + (x0 + 3) / pw], g_ctx));
-    out4[e] = o;
-  }
+  const uint32_t e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= total4) return;
+  const float4 c = ec4[e];
+  const float4 u = eu4[e];
+  const uint32_t row = fdiv(e, wl4);           // c * Hl + y
+  const uint32_t x0 = (e - row * wl4.b) * 4;
+  const uint32_t y = row - fdiv(row, hl) * hl.b;
+  const uint32_t trow = fdiv(y, ph) * side;
+  float4 o;
+  o.x = guided(c.x, u.x, fmaf(g_d, sv[trow + fdiv(x0 + 0, pw)], g_ctx));
+  o.y = guided(c.y, u.y, fmaf(g_d, sv[trow + fdiv(x0 + 1, pw)], g_ctx));
+  o.z = guided(c.z, u.z, fmaf(g_d, sv[trow + fdiv(x0 + 2, pw)], g_ctx));
+  o.w = guided(c.w, u.w, fmaf(g_d, sv[trow + fdiv(x0 + 3, pw)], g_ctx));
+  out4[e] = o;
 }
 
 __global__ __launch_bounds__(256) void k_swcfg_scalar(const float* __restrict__ ec, const float* __restrict__ eu,
@@ -45,12 +60,13 @@ hipError_t launch_swcfg(const float* eps, const float* sv, int C, int Hl, int Wl
   const uint32_t ph = Hl / side, pw = Wl / side;
   const float g_d = g_sens - g_ctx;
   const bool vec = (Wl % 4 == 0) && ((reinterpret_cast<uintptr_t>(eps) | reinterpret_cast<uintptr_t>(out)) % 16 == 0);
-  if (vec) {
+  if (vec && total / 4 < (1u << 24)) {
+    // one float4 per thread; the index arithmetic uses the float-reciprocal division (exact below 2^24)
     const uint32_t total4 = total / 4;
-    uint32_t blocks = (total4 + 255) / 256;
-    if (blocks > 256 * 32) blocks = 256 * 32;
-    k_swcfg_vec<<<blocks, 256, 0, s>>>(reinterpret_cast<const float4*>(eps), reinterpret_cast<const float4*>(eps + total),
-                                        sv, Wl / 4, Hl, side, ph, pw, g_ctx, g_d, reinterpret_cast<float4*>(out), total4);
+    auto fd = [](uint32_t b) { return FastDiv{b, 1.0f / static_cast<float>(b)}; };
+    k_swcfg_vec<<<(total4 + 255) / 256, 256, 0, s>>>(
+        reinterpret_cast<const float4*>(eps), reinterpret_cast<const float4*>(eps + total), sv, fd(Wl / 4), fd(Hl),
+        side, fd(ph), fd(pw), g_ctx, g_d, reinterpret_cast<float4*>(out), total4);
   } else {
     uint32_t blocks = (total + 255) / 256;
     if (blocks > 256 * 32) blocks = 256 * 32;
