@@ -147,3 +147,22 @@ def test_mask_check_unaligned_row_lengths(lib):
         for want_c in (True, False):
             assert not _check(lib, mb, N, T, (3,), want_c=want_c)[0]
             assert _check(lib, mb, N, T, (0,), want_c=want_c)[0] == (cols == N + T)
+
+
+def test_mask_policy_checks_once_per_tensor_version(lib):
+    """The host side of "check once, then elide or keep": a redundant mask is dropped, a semantic one is
+    kept, the verdict is cached per tensor version, and an in-place edit of the mask is re-checked."""
+    t = torch()
+    N, T = 96, 16
+    pol = lib.MaskPolicy()
+    m = t.ones((1, 1, N, N), dtype=t.bool, device="cuda")
+    assert pol.elide(m, N, T, (5, 9)) is None
+    assert pol.elide(m, N, T, (5, 9)) is None and len(pol._cache) == 1
+    m[0, 0, 3, 7] = False  # bumps the tensor version
+    assert pol.elide(m, N, T, (5, 9)) is m and len(pol._cache) == 2
+    f = t.zeros((1, 1, N, N + T), dtype=t.float32, device="cuda")
+    assert pol.elide(f, N, T, (T, T)) is None
+    f[0, 0, 1, N + T - 1] = -1.0  # a valid text column of row 1 differs
+    assert pol.elide(f, N, T, (T, T)) is f
+    assert pol.elide(f, N, T, (T - 1, T - 1)) is None  # that column is padding for these lengths
+    assert pol.elide(None, N, T, (T, T)) is None
