@@ -212,6 +212,20 @@ def main():
         "breakdown": breakdown,
     }
 
+    # ---------------------------------------------------------------- the mask tax on this stack
+    # The redundant all-valid mask passed through (kept) instead of elided: the dense anchor launch with
+    # the mask streamed from HBM into the same MFMA kernel, bool and fp32.
+    fmask = torch.zeros((1, 1, N, N), dtype=torch.float32, device=dev)
+    tax = {"dense_elided_ms": time_launches(torch, lambda: dts.safe_attn_dense(q, ki, vi, kt, vt, w.tv, state)),
+           "dense_kept_bool_ms": time_launches(torch, lambda: dts.safe_attn_dense(q, ki, vi, kt, vt, w.tv, state,
+                                                                                  mask=mask)),
+           "dense_kept_f32_ms": time_launches(torch, lambda: dts.safe_attn_dense(q, ki, vi, kt, vt, w.tv, state,
+                                                                                 mask=fmask))}
+    tax["tax_bool"] = tax["dense_kept_bool_ms"] / tax["dense_elided_ms"]
+    tax["tax_f32"] = tax["dense_kept_f32_ms"] / tax["dense_elided_ms"]
+    tax["workload"] = "srsu_1024 dense anchor; mask [1,1,4096,4096] all valid (16.8 MB bool / 67.1 MB fp32)"
+    del fmask
+
     # ---------------------------------------------------------------- 2560^2 attention (same kernels)
     if not args.no_large:
         wl = syn.WORKLOADS["srsu_2560"]
@@ -242,7 +256,15 @@ def main():
                                     "rows_ms": timing["rows"], "rows_tflops": tfr,
                                     "rows_frac_mfma": tfr / MFMA_BF16_PEAK_TFLOPS}
         result["hbm_large"] = hbm_large(dts, torch, np, syn, dev, lout, lrows, hbm)
+        lmask = torch.ones((1, 1, wl.N, wl.N), dtype=torch.bool, device=dev)  # 655 MB
+        kept = time_launches(torch, lambda: dts.safe_attn_dense(lq, lki, lvi, lkt, lvt, wl.tv, lout, mask=lmask), reps=3)
+        tax["dense_2560_elided_ms"] = timing["dense"]
+        tax["dense_2560_kept_bool_ms"] = kept
+        tax["tax_2560_bool"] = kept / timing["dense"]
+        del lmask
         del lq, lki, lvi, lkt, lvt, lout
+
+    result["mask_tax"] = tax
 
     if args.copy_calibration:
         src = torch.empty(64 << 20, dtype=torch.float32, device=dev).fill_(1.0)

@@ -72,10 +72,19 @@ AttnArgs make_args(const safe_attn_desc* d, const int32_t* rows, int R) {
   return a;
 }
 
+// A kept mask runs on the MFMA kernel when each lane's 16-entry mask chunks are aligned and never cross a
+// mask row (N and the row length multiples of 16, 16-byte aligned base) and no emission is asked (the
+// emission of masked logits stays on the generic kernel); otherwise on the generic kernel.
+bool mfma_takes_mask(const safe_attn_desc* d) {
+  return d->xattn_out == nullptr && d->lse_img_out == nullptr && d->N % 16 == 0 && d->mask_cols % 16 == 0 &&
+         (reinterpret_cast<uintptr_t>(d->mask) & 15u) == 0;
+}
+
 safe_status run_attn(const safe_attn_desc* d, const int32_t* rows, int R, hipStream_t s) {
   const AttnArgs a = make_args(d, rows, R);
   if (R == 0) return SAFE_OK;
-  if (d->dtype == SAFE_DTYPE_BF16 && d->mask == nullptr) return from_hip(launch_attn_mfma_bf16(a, s));
+  if (d->dtype == SAFE_DTYPE_BF16 && (d->mask == nullptr || mfma_takes_mask(d)))
+    return from_hip(launch_attn_mfma_bf16(a, s));
   return from_hip(launch_attn_generic(a, d->dtype, s));
 }
 

@@ -126,6 +126,55 @@ struct WaveState {
   float l[QB];       // running row sum of exp2((s - m) * c2), lane-half partial
 };
 
+// Kept general mask on the MFMA path (KM = 1: bool, a false entry makes the logit -inf; KM = 2: fp32,
+// added to the scaled logit), one query block per wave.  A lane needs its own query row's entries for
+// keys 16g .. 16g+15 of both 32-key halves of a tile: two 16-byte chunks (bool) or two 64-byte chunks
+// (fp32), loaded into registers one tile ahead.  Chunks wholly past the tile's valid keys are not
+// loaded (those keys are -inf anyway); a chunk never crosses the end of a mask row because the host
+// only takes this path when N and the row length are multiples of 16.
+template <int KM>
+struct MaskTile {
+  uint4 w[2][KM == 2 ? 4 : 1];
+};
+
+template <int KM>
+__device__ __forceinline__ void mask_load(MaskTile<KM>& mt, const uint8_t* mrow, int col0, int nvalid, int g,
+                                          bool zero) {
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    const int off = kb * 32 + 16 * g;
+    const bool ld = !zero && off < nvalid;
+    if (KM == 1) {
+      mt.w[kb][0] = ld ? *reinterpret_cast<const uint4*>(mrow + col0 + off) : make_uint4(~0u, ~0u, ~0u, ~0u);
+    } else {
+#pragma unroll
+      for (int j = 0; j < (KM == 2 ? 4 : 1); ++j)
+        mt.w[kb][j] = ld ? *reinterpret_cast<const uint4*>(mrow + 4 * static_cast<size_t>(col0 + off) + 16 * j)
+                         : make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+}
+
+// Applies the mask to the 16 logits of half kb; factor turns a natural-log mask value into the units of
+// the logits (1/scale for raw dot products, log2 e for pre-scaled log2 logits).
+template <int KM>
+__device__ __forceinline__ void mask_apply(f32x16& s, const MaskTile<KM>& mt, int kb, float factor) {
+  if (KM == 1) {
+    const uint32_t w[4] = {mt.w[kb][0].x, mt.w[kb][0].y, mt.w[kb][0].z, mt.w[kb][0].w};
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s[i] = ((w[i >> 2] >> (8 * (i & 3))) & 0xffu) ? s[i] : -INFINITY;
+  } else if (KM == 2) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint4 v = mt.w[kb][j];
+      s[4 * j + 0] = fmaf(__uint_as_float(v.x), factor, s[4 * j + 0]);
+      s[4 * j + 1] = fmaf(__uint_as_float(v.y), factor, s[4 * j + 1]);
+      s[4 * j + 2] = fmaf(__uint_as_float(v.z), factor, s[4 * j + 2]);
+      s[4 * j + 3] = fmaf(__uint_as_float(v.w), factor, s[4 * j + 3]);
+    }
+  }
+}
+
 // Fast path (no lse, no emission): Q was pre-multiplied by scale * log2(e) and rounded to bf16 once, so
 // the logits come out of the MFMA in log2 units, and each tile's logit accumulators start at -m (two
 // 64-bit moves per four registers), so the MFMA output is already s - m and each probability costs a
@@ -133,9 +182,10 @@ struct WaveState {
 // 2^-9 of the root-sum-square of its products, below the bf16 rounding of the probabilities
 // themselves.  The lazy running max and its exact path are as in the general step below (m is kept in
 // log2 units here).
-template <int QB, bool MASKED>
+template <int QB, bool MASKED, int KM>
 __device__ __forceinline__ void tile_step_fast(WaveState<QB>& st, const uint16_t* kl, const uint16_t* vl, int kperm,
-                                               int g, int li, int dc0, int nvalid) {
+                                               int g, int li, int dc0, int nvalid, const MaskTile<KM>& mt) {
+  static_assert(KM == 0 || QB == 1, "a kept mask runs with one query block per wave");
   f32x16 s[QB][2];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
@@ -166,6 +216,10 @@ __device__ __forceinline__ void tile_step_fast(WaveState<QB>& st, const uint16_t
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) s[qb][kb][i] = (kb * 32 + 16 * g + i) < nvalid ? s[qb][kb][i] : -INFINITY;
+  }
+  if constexpr (KM != 0) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) mask_apply<KM>(s[0][kb], mt, kb, kLog2e);
   }
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
   bf16x8 p[QB][2][2];
@@ -207,6 +261,10 @@ __device__ __forceinline__ void tile_step_fast(WaveState<QB>& st, const uint16_t
 #pragma unroll
           for (int i = 0; i < 16; ++i) sx[kb][i] = (kb * 32 + 16 * g + i) < nvalid ? sx[kb][i] : -INFINITY;
       }
+      if constexpr (KM != 0) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) mask_apply<KM>(sx[kb], mt, kb, kLog2e);
+      }
       float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -225,6 +283,14 @@ __device__ __forceinline__ void tile_step_fast(WaveState<QB>& st, const uint16_t
       }
       const float m = st.m[qb];
       float tsum = 0.f;
+      if (KM != 0 && m == -INFINITY) {  // every key so far masked: nothing to add yet
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int mm = 0; mm < 2; ++mm) p[qb][kb][mm] = (bf16x8){};
+        tl[qb] = 0.f;
+        continue;
+      }
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -265,14 +331,16 @@ __device__ __forceinline__ void tile_step_fast(WaveState<QB>& st, const uint16_t
 
 // One 64-key tile: logits, online softmax, P V.  MASKED handles partial tiles (keys >= nvalid are
 // -inf) and the optional store of the tile's logits (text tiles of the warmup emission).
-template <int QB, bool MASKED, bool EXACT_SUM>
+template <int QB, bool MASKED, bool EXACT_SUM, int KM>
 __device__ __forceinline__ void tile_step(WaveState<QB>& st, const uint16_t* kl, const uint16_t* vl, int kperm,
                                           int g, int li, int dc0, float c2, int nvalid, float* const (&xo)[QB],
-                                          float scale) {
+                                          float scale, const MaskTile<KM>& mt) {
   if constexpr (!EXACT_SUM) {
-    tile_step_fast<QB, MASKED>(st, kl, vl, kperm, g, li, dc0, nvalid);
+    tile_step_fast<QB, MASKED, KM>(st, kl, vl, kperm, g, li, dc0, nvalid, mt);
     return;
   }
+  static_assert(KM == 0 || QB == 1, "a kept mask runs with one query block per wave");
+  const float inv_scale = 1.f / scale;
   // ---- S^T = K Q^T
   f32x16 s[QB][2];
 #pragma unroll
@@ -311,6 +379,10 @@ __device__ __forceinline__ void tile_step(WaveState<QB>& st, const uint16_t* kl,
             if (key < nvalid) xo[qb][key] = s[qb][kb][i] * scale;
           }
       }
+  }
+  if constexpr (KM != 0) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) mask_apply<KM>(s[0][kb], mt, kb, inv_scale);
   }
 
   // ---- online softmax in log2 units against the running max m.  The tile's probabilities are made
@@ -365,6 +437,10 @@ __device__ __forceinline__ void tile_step(WaveState<QB>& st, const uint16_t* kl,
 #pragma unroll
           for (int i = 0; i < 16; ++i) sx[kb][i] = (kb * 32 + 16 * g + i) < nvalid ? sx[kb][i] : -INFINITY;
       }
+      if constexpr (KM != 0) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) mask_apply<KM>(sx[kb], mt, kb, inv_scale);
+      }
       float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -383,6 +459,14 @@ __device__ __forceinline__ void tile_step(WaveState<QB>& st, const uint16_t* kl,
       }
       const float mc = st.m[qb] * c2;
       float tsum = 0.f;
+      if (KM != 0 && st.m[qb] == -INFINITY) {  // every key so far masked: nothing to add yet
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int mm = 0; mm < 2; ++mm) p[qb][kb][mm] = (bf16x8){};
+        tl[qb] = 0.f;
+        continue;
+      }
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -439,7 +523,7 @@ __device__ __forceinline__ void store_lse_img(const AttnArgs& a, const WaveState
   }
 }
 
-template <bool GATHER, int QB, bool EXACT_SUM>
+template <bool GATHER, int QB, bool EXACT_SUM, int KM>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void k_attn_mfma(AttnArgs a) {
   constexpr int kRowsW = 32 * QB;
   constexpr int kBM = kWaves * kRowsW;
@@ -509,6 +593,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   // output register r of lane half g hold key 16*g + r.
   const int kperm = 16 * ((qi >> 2) & 1) + 4 * (qi >> 3) + (qi & 3);
 
+  // kept mask: this lane's query row of the (b, h) mask slice, tile t's first column and valid keys
+  const uint8_t* mrow = nullptr;
+  if constexpr (KM != 0) {
+    const int mb = a.mask_B == 1 ? 0 : b, mh = a.mask_H == 1 ? 0 : h;
+    mrow = static_cast<const uint8_t*>(a.mask) +
+           ((static_cast<size_t>(mb) * a.mask_H + mh) * a.N + row[0]) * static_cast<size_t>(a.mask_cols) * (KM == 1 ? 1 : 4);
+  }
+  auto mask_fetch = [&](MaskTile<KM>& mt, int t) {
+    if constexpr (KM != 0) {
+      const bool txt = t >= n_img;
+      const int col0 = txt ? a.N + (t - n_img) * kBN : t * kBN;
+      const int nvalid = txt ? min(kBN, tv - (t - n_img) * kBN) : min(kBN, a.N - t * kBN);
+      mask_load<KM>(mt, mrow, col0, nvalid, g, txt && a.mask_cols == a.N);  // image-only mask: 0 on text
+    }
+  };
+  MaskTile<KM> mcur, mnext;
+  mask_fetch(mcur, 0);
+
   stage_issue<(QB > 1)>(tile_src(a, bh, 0, n_img, tv), k_a, v_a);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -517,14 +619,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   // One tile: prefetch tile t+1 into the other buffer, compute on this one, then wait for the
   // prefetch and synchronise.
   auto full_tile = [&](int t, const uint16_t* ck, const uint16_t* cv, uint16_t* nk, uint16_t* nv) {
-    if (t + 1 < ntiles) stage_issue<(QB > 1)>(tile_src(a, bh, t + 1, n_img, tv), nk, nv);
-    tile_step<QB, false, EXACT_SUM>(st, ck, cv, kperm, g, li, dc0, c2, kBN, no_store, a.scale);
+    if (t + 1 < ntiles) {
+      stage_issue<(QB > 1)>(tile_src(a, bh, t + 1, n_img, tv), nk, nv);
+      mask_fetch(mnext, t + 1);
+    }
+    tile_step<QB, false, EXACT_SUM, KM>(st, ck, cv, kperm, g, li, dc0, c2, kBN, no_store, a.scale, mcur);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    if constexpr (KM != 0) mcur = mnext;
   };
   auto masked_tile = [&](int t, const uint16_t* ck, const uint16_t* cv, uint16_t* nk, uint16_t* nv) {
     if (emit && t == n_img && a.lse_img_out != nullptr) store_lse_img(a, st, h, row, valid, g);
-    if (t + 1 < ntiles) stage_issue<(QB > 1)>(tile_src(a, bh, t + 1, n_img, tv), nk, nv);
+    if (t + 1 < ntiles) {
+      stage_issue<(QB > 1)>(tile_src(a, bh, t + 1, n_img, tv), nk, nv);
+      mask_fetch(mnext, t + 1);
+    }
     const bool txt = t >= n_img;
     const int nvalid = txt ? min(kBN, tv - (t - n_img) * kBN) : min(kBN, a.N - t * kBN);
     float* xo[QB];
@@ -533,9 +642,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       xo[qb] = (emit && txt && a.xattn_out != nullptr && valid[qb])
                    ? a.xattn_out + (static_cast<size_t>(h) * a.N + row[qb]) * a.T + (t - n_img) * kBN
                    : nullptr;
-    tile_step<QB, true, EXACT_SUM>(st, ck, cv, kperm, g, li, dc0, c2, nvalid, xo, a.scale);
+    tile_step<QB, true, EXACT_SUM, KM>(st, ck, cv, kperm, g, li, dc0, c2, nvalid, xo, a.scale, mcur);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    if constexpr (KM != 0) mcur = mnext;
   };
 
   int t = 0;
@@ -578,37 +688,39 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   }
 }
 
-template <bool GATHER, int QB, bool EXACT_SUM>
+template <bool GATHER, int QB, bool EXACT_SUM, int KM>
 static void launch(const AttnArgs& a, hipStream_t s) {
   constexpr int kBM = kWaves * 32 * QB;
   const int nqt = (a.R + kBM - 1) / kBM;
   const uint32_t grid = static_cast<uint32_t>(a.B) * a.H * nqt;
-  k_attn_mfma<GATHER, QB, EXACT_SUM><<<grid, kThreads, 0, s>>>(a);
+  k_attn_mfma<GATHER, QB, EXACT_SUM, KM><<<grid, kThreads, 0, s>>>(a);
 }
 
-template <bool GATHER, int QB>
+template <bool GATHER, int QB, int KM>
 static void launch_sum(const AttnArgs& a, hipStream_t s) {
-  // The row sum accumulates the bf16-rounded probabilities (v_dot2, exactly the values the P V
-  // product uses) unless a log-sum-exp output is requested; then it sums the fp32 probabilities so
-  // that lse / lse_img keep fp32 accuracy (they feed the sensitivity scores).
   const bool exact = a.lse != nullptr || a.lse_img_out != nullptr || a.xattn_out != nullptr;
-  if (exact) launch<GATHER, QB, true>(a, s);
-  else launch<GATHER, QB, false>(a, s);
+  if (exact) launch<GATHER, QB, true, KM>(a, s);
+  else launch<GATHER, QB, false, KM>(a, s);
+}
+
+template <bool GATHER>
+static void launch_rows(const AttnArgs& a, hipStream_t s) {
+  if (a.mask != nullptr) {
+    // kept mask: one query block per wave (the per-lane mask chunks need the registers of the second)
+    if (a.mask_dtype == SAFE_DTYPE_BOOL) launch_sum<GATHER, 1, 1>(a, s);
+    else launch_sum<GATHER, 1, 2>(a, s);
+    return;
+  }
+  // Two query blocks per wave when that still fills the GPU's wave slots at least once over.
+  const double waves_qb2 = static_cast<double>(a.B) * a.H * ((a.R + 63) / 64);
+  if (waves_qb2 >= 2048.0) launch_sum<GATHER, 2, 0>(a, s);
+  else launch_sum<GATHER, 1, 0>(a, s);
 }
 
 hipError_t launch_attn_mfma_bf16(const AttnArgs& a, hipStream_t s) {
   if (a.R == 0) return hipSuccess;
-  // Two query blocks per wave halve the LDS traffic per flop; one block per wave doubles the number
-  // of waves, which wins when the row count alone cannot fill the 1024 SIMDs about twice over.
-  const double waves_qb2 = static_cast<double>(a.B) * a.H * ((a.R + 63) / 64);
-  const bool qb2 = waves_qb2 >= 2048.0;
-  if (a.rows != nullptr) {
-    if (qb2) launch_sum<true, 2>(a, s);
-    else launch_sum<true, 1>(a, s);
-  } else {
-    if (qb2) launch_sum<false, 2>(a, s);
-    else launch_sum<false, 1>(a, s);
-  }
+  if (a.rows != nullptr) launch_rows<true>(a, s);
+  else launch_rows<false>(a, s);
   return hipGetLastError();
 }
 

@@ -257,3 +257,91 @@ def test_full_size_sampled(lib, name):
     got = host(out[:, :, t.as_tensor(rows_checked, device="cuda")])
     ro, _ = OA.attention(inp["q"], inp["k_img"], inp["v_img"], inp["k_txt"], inp["v_txt"], w.tv, rows=rows_checked)
     assert_close(got, ro, "bf16", name)
+
+
+# ---------------------------------------------------------------- kept masks on the MFMA kernel
+def _kept_mask(r, kind, shape, n_img, tv_max, full_rows=()):
+    """A non-removable mask: bool with ~40% False, or fp32 N(0, 2) with ~10% -inf; the listed rows are
+    fully masked over every column (image and text)."""
+    if kind == "bool":
+        m = r.random(shape) < 0.6
+        m[..., 0] = True
+        for i in full_rows:
+            m[..., i, :] = False
+    else:
+        m = (r.standard_normal(shape) * 2).astype(np.float32)
+        m[r.random(shape) < 0.1] = -np.inf
+        m[..., 0] = 0.0
+        for i in full_rows:
+            m[..., i, :] = -np.inf
+    return m
+
+
+@pytest.mark.parametrize("N,T,tv,kind,text_cols,mB,mH,want_lse", [
+    (256, 64, (30, 64), "bool", True, 1, 1, False),
+    (256, 64, (30, 64), "bool", False, 2, 3, True),
+    (448, 256, (77, 20), "f32", True, 2, 1, False),
+    (448, 256, (77, 20), "f32", False, 1, 3, True),
+    (320, 32, (0, 32), "bool", True, 2, 3, True),
+])
+def test_bf16_kept_mask_on_mfma_kernel(lib, N, T, tv, kind, text_cols, mB, mH, want_lse):
+    """Masks with N and the row length multiples of 16 run on the MFMA kernel: dense and gathered rows
+    match the oracle, fully masked rows give 0 and lse = -inf, an image-only mask leaves text unmasked."""
+    w = syn.scaled(syn.WORKLOADS["dense_1024"], B=2, H=3, N=N, T=T, tv=tv, side=1)
+    inp = syn.attention_inputs(w)
+    r = np.random.default_rng(N + T + mB + mH)
+    cols = N + T if text_cols else N
+    full = (5, N - 1) if text_cols else ()
+    m = _kept_mask(r, kind, (mB, mH, N, cols), N, max(tv), full_rows=full)
+    o, lse, _, _ = _run(lib, w, inp, mask=dev(m), want_lse=want_lse)
+    ro, rlse = _oracle(w, inp, mask=m)
+    assert_close(o, ro, "bf16", "dense kept mask")
+    if want_lse:
+        fin = np.isfinite(rlse)
+        assert np.array_equal(fin, np.isfinite(lse))
+        assert np.max(np.abs(lse[fin] - rlse[fin])) < 1e-4
+    for i in full:
+        assert np.all(o[:, :, i] == 0)
+    rows = np.array(sorted({0, 1, 5, 17, N // 2, N - 1}), dtype=np.int32)
+    state = np.full((w.B, w.H, N, 64), 0.25, np.float32)
+    o, _, _, _ = _run(lib, w, inp, mask=dev(m), rows=rows, state=state, want_lse=False)
+    ro, _ = _oracle(w, inp, mask=m, rows=rows)
+    assert_close(o[:, :, rows], ro, "bf16", "rows kept mask")
+    untouched = np.setdiff1d(np.arange(N), rows)
+    assert np.all(o[:, :, untouched] == 0.25)
+
+
+def test_bf16_kept_mask_late_first_valid_key(lib):
+    """Rows whose first unmasked key comes after several fully masked tiles (the running max stays -inf
+    over those tiles) and rows that are masked except for one text key."""
+    w = syn.scaled(syn.WORKLOADS["dense_1024"], B=2, H=2, N=512, T=64, tv=(64, 10), side=1)
+    inp = syn.attention_inputs(w)
+    m = np.zeros((1, 1, w.N, w.N + w.T), dtype=bool)
+    m[0, 0, :, 300:] = True          # first 4 image tiles masked for every row, rest attends
+    m[0, 0, 7, :] = False
+    m[0, 0, 7, w.N + 3] = True       # row 7: only text key 3
+    for want_lse in (False, True):
+        o, lse, _, _ = _run(lib, w, inp, mask=dev(m), want_lse=want_lse)
+        ro, rlse = _oracle(w, inp, mask=m)
+        assert_close(o, ro, "bf16", "late first key")
+        if want_lse:
+            assert np.max(np.abs(lse - rlse)) < 1e-4
+
+
+def test_bf16_kept_mask_full_size_sampled(lib):
+    """The 1024^2 shape with a random bool image mask: sampled rows against the oracle."""
+    w = syn.WORKLOADS["dense_1024"]
+    t = torch()
+    inp = syn.attention_inputs(w)
+    q, ki, vi, kt, vt = attn_tensors(inp, w.dtype)
+    r = np.random.default_rng(7)
+    m = r.random((1, 1, w.N, w.N)) < 0.8
+    out = t.zeros_like(q)
+    lib.safe_attn_dense(q, ki, vi, kt, vt, w.tv, out, mask=dev(m))
+    t.cuda.synchronize()
+    sample = syn.sample_rows(w.N, 16, seed=3)
+    sl = lambda a: a[:, :2]
+    ro, _ = OA.attention(sl(inp["q"]), sl(inp["k_img"]), sl(inp["v_img"]), sl(inp["k_txt"]), sl(inp["v_txt"]), w.tv,
+                         rows=sample, mask=m)
+    got = host(out)[:, :2][:, :, sample]
+    assert_close(got, ro, "bf16", "1024^2 kept bool mask")
