@@ -1,6 +1,7 @@
 // General attention kernel on the vector ALUs: fp32 or bf16 storage, dense or sensitive rows,
 // optional kept additive mask (fp32 or bool), optional warmup emission.  It serves the fp32 path and
-// every kept-mask call; the mask-free bf16 hot path runs on the MFMA kernel instead.
+// the bf16 kept-mask calls the MFMA kernel does not take (an emission request, or N or the mask row
+// length not a multiple of 16, or an unaligned mask); all other bf16 calls run on the MFMA kernel.
 //
 // Semantics (SAFE-DiT technical summary, Methodology 1 and 3): one joint softmax per image query row
 // over the image keys then the valid text keys (padded text slots never enter), logits scaled by

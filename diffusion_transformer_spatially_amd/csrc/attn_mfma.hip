@@ -1,4 +1,5 @@
-// Mask-free bf16 attention for gfx950 (dense anchor rows or gathered sensitive rows).
+// bf16 attention for gfx950 (dense anchor rows or gathered sensitive rows), mask-free or with a kept
+// general mask.
 //
 // Computes, for image query rows of (b,h) -- all N rows (anchor refresh, SAFE-DiT technical summary
 // Methodology 3 "CAR") or the rows of S (Methodology 3 "SRSU"; AccelAes summary B.2 SkipSparse) --
@@ -13,11 +14,13 @@
 //    dimension), so every lane holds the 32 logits of one query row per block: lane L owns query
 //    L%32 and keys 16*(L/32) + r (r = 0..15) of each 32-key block, thanks to a fixed permutation of
 //    the K rows fed to the instruction;
-//  * fp32 online softmax in log2 units (scale*log2(e) folded into one FMA per logit, v_exp_f32); the
-//    row max is combined across the two lane halves with v_permlane32_swap; the output is rescaled
-//    only when some row's max grew; the row sum accumulates the bf16-rounded probabilities with
-//    v_dot2_f32_bf16, i.e. exactly the values the P V product uses (the fp32 probabilities when a
-//    log-sum-exp output is requested);
+//  * fp32 online softmax in log2 units (scale*log2(e) folded into one FMA per logit, or into Q once
+//    when no log-sum-exp is returned, v_exp_f32); the row max is combined across the two lane halves
+//    with v_permlane32_swap; the output is rescaled only when some row's max grew; the row sum
+//    accumulates the bf16-rounded probabilities with v_dot2_f32_bf16, i.e. exactly the values the P V
+//    product uses (the fp32 probabilities when a log-sum-exp output is requested);
+//  * a kept mask (bool or fp32, one query block per wave) is read straight from global memory one tile
+//    ahead, each lane loading its own row's 16-key chunks, and applied to the logits after S^T;
 //  * O^T += V^T P^T on the same instruction: the P^T operand is the lane's own probabilities (no data
 //    movement), the V^T operand is read from row-major LDS with ds_read_b64_tr_b16;
 //  * full image tiles run a loop without any masking; the ragged image tail and the text tiles run a
