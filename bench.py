@@ -185,6 +185,8 @@ def main():
         "stat": "median over the timed launches",
     }
 
+    sclk = profiled_traffic("sclk_mhz")
+    peak_sclk = 256 * 4 * 1024 * sclk / 1e6 if sclk else None  # TFLOP/s
     result = {
         "metric": "attention TFLOP/s + % bf16 MFMA peak (dense & |S|-row) at N=4096/25600",
         "value": value,
@@ -207,8 +209,12 @@ def main():
         "roofline": {"bound": "mfma", "achieved": dense_tf, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": dense_tf / MFMA_BF16_PEAK_TFLOPS, "traffic": profiled_traffic(),
                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE/WRITE_SIZE, copy-calibrated)",
-                     "kernel": "k_attn_mfma<false, 2, false> (dense anchor attention)",
-                     "flops_per_launch": w.flops_dense, "avg_launch_ms": avg_ms["attn_dense"]},
+                     "kernel": "k_attn_mfma<false, 2, false, 0> (dense anchor attention)",
+                     "flops_per_launch": w.flops_dense, "avg_launch_ms": avg_ms["attn_dense"],
+                     "sclk_mhz": sclk, "peak_at_sclk": peak_sclk,
+                     "frac_at_sclk": (dense_tf / peak_sclk) if peak_sclk else None,
+                     "sclk_note": "shader clock during this kernel from the profile's GRBM_COUNT pass; "
+                                  "peak_at_sclk = 256 CU x 4 SIMD x 1024 flop/clk x sclk"},
         "breakdown": breakdown,
     }
 
@@ -355,25 +361,26 @@ def cpu_other_stages(w, x, syn):
             "swcfg_combine_ms": 1e3 * (t4 - t3), "kind": "oracle", "sample": "srsu_1024 stages in full"}
 
 
-def profiled_traffic():
-    """HBM bytes per launch of the dense attention kernel from the committed counter summary, or None
-    when the kernel source has changed since those counters were taken."""
+def profiled_traffic(field: str = "traffic_bytes_per_launch"):
+    """A counter-derived figure of the dense attention kernel from the committed profile summary (HBM
+    bytes per launch, or the shader clock in MHz), or None when the kernel source has changed since
+    those counters were taken."""
     import hashlib
     prof = os.path.join(ROOT, "profiles", "attn_dense_1024.md")
     if not os.path.exists(prof):
         return None
     fields = {}
     for line in open(prof):
-        if ":" in line and line.strip().split(":")[0] in ("traffic_bytes_per_launch", "kernel_source_sha256"):
+        if ":" in line and line.strip().split(":")[0] in ("traffic_bytes_per_launch", "sclk_mhz", "kernel_source_sha256"):
             k, v = line.strip().split(":", 1)
             fields[k] = v.strip()
     h = hashlib.sha256()
     for f in ("attn_mfma.hip", "common.hpp"):
         with open(os.path.join(ROOT, "diffusion_transformer_spatially_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
-    if fields.get("kernel_source_sha256") != h.hexdigest() or "traffic_bytes_per_launch" not in fields:
+    if fields.get("kernel_source_sha256") != h.hexdigest() or field not in fields:
         return None
-    return float(fields["traffic_bytes_per_launch"])
+    return float(fields[field])
 
 
 def cpu_baseline(w, inp, budget_s: float):
