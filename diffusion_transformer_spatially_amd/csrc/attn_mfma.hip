@@ -23,6 +23,9 @@
 //    ahead, each lane loading its own row's 16-key chunks, and applied to the logits after S^T;
 //  * O^T += V^T P^T on the same instruction: the P^T operand is the lane's own probabilities (no data
 //    movement), the V^T operand is read from row-major LDS with ds_read_b64_tr_b16;
+//  * with two query blocks per wave the tile is staggered: the logits of block 1 and the output update
+//    of block 0 are issued alongside the softmax of the other block, so one wave keeps its matrix and
+//    vector work overlapped (sched_group_barrier sets the interleave);
 //  * full image tiles run a loop without any masking; the ragged image tail and the text tiles run a
 //    separate path that masks keys past the valid count and, for the warmup emission, stores the
 //    text-block logits and the image-block log-sum-exp;
@@ -185,10 +188,175 @@ __device__ __forceinline__ void mask_apply(f32x16& s, const MaskTile<KM>& mt, in
 // 2^-9 of the root-sum-square of its products, below the bf16 rounding of the probabilities
 // themselves.  The lazy running max and its exact path are as in the general step below (m is kept in
 // log2 units here).
+
+// One query block's softmax of a tile on the fast path (logits s are log2 units minus m): probabilities
+// p and their bf16 row-sum contribution, with the lazy-max exact path.  Split out so that the two query
+// blocks of a wave can be staggered against each other's matrix work.
+template <bool MASKED>
+__device__ __forceinline__ float fast_probs(bf16x8 (&p)[2][2], f32x16 (&s)[2], int g, int nvalid) {
+  if (MASKED) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[kb][i] = (kb * 32 + 16 * g + i) < nvalid ? s[kb][i] : -INFINITY;
+  }
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  float tsum = 0.f;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int mm = 0; mm < 2; ++mm) {
+      uint32_t pk[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        pk[e] = pack_bf16x2(__builtin_amdgcn_exp2f(s[kb][8 * mm + 2 * e]), __builtin_amdgcn_exp2f(s[kb][8 * mm + 2 * e + 1]));
+        tsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[e]), ones, tsum, false);
+      }
+      p[kb][mm] = __builtin_bit_cast(bf16x8, (uint4){pk[0], pk[1], pk[2], pk[3]});
+    }
+  return tsum;
+}
+
+// Exact path of one query block (rare): logits again from K in LDS, tile max, rescale, probabilities again.
+template <bool MASKED>
+__device__ __forceinline__ float fast_exact(bf16x8 (&p)[2][2], const bf16x8 (&q)[4], float& m, float& l, f32x16 (&o)[2],
+                                            const uint16_t* kl, int kperm, int g, int nvalid) {
+  f32x16 sx[2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kl + lds_off(kb * 32 + kperm, 2 * ks + g));
+      sx[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, q[ks], ks == 0 ? (f32x16){} : sx[kb], 0, 0, 0);
+    }
+  if (MASKED) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sx[kb][i] = (kb * 32 + 16 * g + i) < nvalid ? sx[kb][i] : -INFINITY;
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sx[kb][i]);
+  mx = fmaxf(mx, swap_halves(mx));
+  const float mnew = fmaxf(m, mx);
+  if (mnew > m) {
+    const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+    l *= alpha;
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+    m = mnew;
+  }
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sx[kb][i] -= m;
+  return fast_probs<false>(p, sx, g, kBN);
+}
+
+// Two query blocks, staggered: logits of block 0; logits of block 1 alongside the softmax of block 0;
+// output update of block 0 alongside the softmax of block 1; output update of block 1.  The vector
+// work of one block runs while the matrix cores work for the other (sched_group_barrier interleaves the
+// two streams inside the wave).
+template <bool MASKED>
+__device__ __forceinline__ void tile_step_fast2(WaveState<2>& st, const uint16_t* kl, const uint16_t* vl, int kperm,
+                                                int g, int li, int dc0, int nvalid) {
+  bf16x8 ka[2][4];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) ka[kb][ks] = *reinterpret_cast<const bf16x8*>(kl + lds_off(kb * 32 + kperm, 2 * ks + g));
+  f32x16 s0[2], s1[2];
+  {
+    const double n0 = __builtin_bit_cast(double, (f32x2){-st.m[0], -st.m[0]});
+    const double n1 = __builtin_bit_cast(double, (f32x2){-st.m[1], -st.m[1]});
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      double d0[8], d1[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) { d0[i] = n0; d1[i] = n1; }
+      s0[kb] = __builtin_bit_cast(f32x16, d0);
+      s1[kb] = __builtin_bit_cast(f32x16, d1);
+    }
+  }
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) s0[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kb][ks], st.q[0][ks], s0[kb], 0, 0, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  // logits of block 1 | softmax of block 0
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) s1[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kb][ks], st.q[1][ks], s1[kb], 0, 0, 0);
+  bf16x8 p0[2][2];
+  float t0 = fast_probs<MASKED>(p0, s0, g, nvalid);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  if (__any(!(t0 <= 65536.f))) t0 = fast_exact<MASKED>(p0, st.q[0], st.m[0], st.l[0], st.o[0], kl, kperm, g, nvalid);
+  st.l[0] += t0;
+  // V^T operands (shared by both blocks)
+  lds_u16* vl3 = (lds_u16*)(vl);
+  bf16x8 va[2][2][2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int mm = 0; mm < 2; ++mm) {
+      const int key = kb * 32 + 16 * g + 8 * mm + (li >> 2);
+#pragma unroll
+      for (int db = 0; db < 2; ++db) {
+        const int col = db * 32 + dc0 + 4 * (li & 3);
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vl3 + lds_off(key, col >> 3) + (col & 4)));
+        const s16x4 hi =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vl3 + lds_off(key + 4, col >> 3) + (col & 4)));
+        va[kb][mm][db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+    }
+  // output update of block 0 | softmax of block 1
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int mm = 0; mm < 2; ++mm)
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+        st.o[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[kb][mm][db], p0[kb][mm], st.o[0][db], 0, 0, 0);
+  bf16x8 p1[2][2];
+  float t1 = fast_probs<MASKED>(p1, s1, g, nvalid);
+  __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);  // the V reads first
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  if (__any(!(t1 <= 65536.f))) t1 = fast_exact<MASKED>(p1, st.q[1], st.m[1], st.l[1], st.o[1], kl, kperm, g, nvalid);
+  st.l[1] += t1;
+  // output update of block 1
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int mm = 0; mm < 2; ++mm)
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+        st.o[1][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[kb][mm][db], p1[kb][mm], st.o[1][db], 0, 0, 0);
+}
+
 template <int QB, bool MASKED, int KM>
 __device__ __forceinline__ void tile_step_fast(WaveState<QB>& st, const uint16_t* kl, const uint16_t* vl, int kperm,
                                                int g, int li, int dc0, int nvalid, const MaskTile<KM>& mt) {
   static_assert(KM == 0 || QB == 1, "a kept mask runs with one query block per wave");
+  if constexpr (QB == 2) {
+    tile_step_fast2<MASKED>(st, kl, vl, kperm, g, li, dc0, nvalid);
+    return;
+  }
   f32x16 s[QB][2];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
