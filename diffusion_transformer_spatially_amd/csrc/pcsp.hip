@@ -14,15 +14,28 @@ constexpr int kPcspThreads = 256;
 constexpr int kPcspGroups = kPcspThreads / 16;
 constexpr int kPcspRows = 4;
 
+// All-reduce inside each 16-lane row of the wave through DPP lane permutations (no LDS round trip):
+// swap neighbours, swap pairs, mirror within each half-row of 8, mirror the row.  Every lane ends with
+// the same value (each step combines two equal-shaped partial results, and + and max commute).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
 __device__ __forceinline__ float group16_max(float v) {
-#pragma unroll
-  for (int m = 8; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 16));
-  return v;
+  v = fmaxf(v, dpp_mov<kDppXor1>(v));
+  v = fmaxf(v, dpp_mov<kDppXor2>(v));
+  v = fmaxf(v, dpp_mov<kDppHalfMirror>(v));
+  return fmaxf(v, dpp_mov<kDppMirror>(v));
 }
 __device__ __forceinline__ float group16_sum(float v) {
-#pragma unroll
-  for (int m = 8; m >= 1; m >>= 1) v += __shfl_xor(v, m, 16);
-  return v;
+  v += dpp_mov<kDppXor1>(v);
+  v += dpp_mov<kDppXor2>(v);
+  v += dpp_mov<kDppHalfMirror>(v);
+  return v + dpp_mov<kDppMirror>(v);
 }
 
 template <bool VEC>
@@ -92,15 +105,17 @@ __global__ __launch_bounds__(kPcspThreads) void k_pcsp_accumulate(const float* _
   }
 }
 
-// Batched form for Tv <= 64*TV4 with float4 rows: each 16-lane group issues the loads of up to JB
-// (head, token) rows at once (JB*TV4 float4 per lane in flight) and then reduces them from registers,
-// so HBM latency is paid once per batch instead of once per row.
+// Batched form for Tv <= 64*TV4 with float4 rows: each 16-lane group issues the loads of JB (head,
+// token) rows at once, with their image log-sum-exp values, and then reduces them from registers, so
+// HBM latency is paid once per batch instead of once per row.  The loads are unconditional (addresses
+// of padded slots and of pairs past the end are clamped to valid memory and their values discarded
+// afterwards), so no load sits under divergent control flow and the waits stay exact.
 template <int TV4>
 __global__ __launch_bounds__(kPcspThreads) void k_pcsp_accumulate_b(const float* __restrict__ x,
                                                                    const float* __restrict__ lse_img, int H, int N,
                                                                    int T, int Tv, int c0, int c1,
                                                                    float* __restrict__ scores, int accumulate) {
-  constexpr int JB = 6;  // 16 groups x 6 = 96 (row, head) pairs: one pass of loads covers 4 rows x 24 heads
+  constexpr int JB = 3;
   extern __shared__ float part[];  // [kPcspRows][H]
   const int g = threadIdx.x >> 4;
   const int lane = threadIdx.x & 15;
@@ -108,65 +123,60 @@ __global__ __launch_bounds__(kPcspThreads) void k_pcsp_accumulate_b(const float*
   const int pairs = kPcspRows * H;
   for (int pb = g; pb < pairs; pb += kPcspGroups * JB) {
     float4 v[JB][TV4];
+    float li[JB];
 #pragma unroll
     for (int jj = 0; jj < JB; ++jj) {
       const int p = pb + kPcspGroups * jj;
       const int r = p / H, h = p - r * H, i = i0 + r;
       const bool ok = p < pairs && i < N;
-      const float* row = x + (static_cast<size_t>(ok ? h : 0) * N + (ok ? i : 0)) * T;
+      const size_t ri = ok ? static_cast<size_t>(h) * N + i : 0;
+      const float* row = x + ri * T;
 #pragma unroll
       for (int c = 0; c < TV4; ++c) {
         const int t = lane * 4 + 64 * c;
-        v[jj][c] = (ok && t < Tv) ? *reinterpret_cast<const float4*>(row + t)
-                                  : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+        v[jj][c] = *reinterpret_cast<const float4*>(row + (t < Tv ? t : 0));
       }
+      li[jj] = lse_img != nullptr ? lse_img[ri] : 0.f;
     }
 #pragma unroll
     for (int jj = 0; jj < JB; ++jj) {
       const int p = pb + kPcspGroups * jj;
-      if (p >= pairs) break;
       const int r = p / H, h = p - r * H, i = i0 + r;
-      float contrib = 0.f;
-      if (i < N) {
-        float e[TV4 * 4];
+      const bool ok = p < pairs && i < N;
+      float e[TV4 * 4];
 #pragma unroll
-        for (int c = 0; c < TV4; ++c) {
-          const int t = lane * 4 + 64 * c;
-          e[4 * c + 0] = v[jj][c].x;
-          e[4 * c + 1] = (t + 1 < Tv) ? v[jj][c].y : -INFINITY;
-          e[4 * c + 2] = (t + 2 < Tv) ? v[jj][c].z : -INFINITY;
-          e[4 * c + 3] = (t + 3 < Tv) ? v[jj][c].w : -INFINITY;
-        }
-        // One exponential per logit: with gm the row's text max,
-        //   mass = sum_content e^(x-gm) / (sum_valid e^(x-gm) + e^(lse_img-gm)),
-        // which equals sum_content exp(x - LSE) for LSE = log(exp(lse_img) + sum_valid exp(x)).
-        float m = -INFINITY;
-#pragma unroll
-        for (int q = 0; q < TV4 * 4; ++q) m = fmaxf(m, e[q]);
-        const float gm = group16_max(m);
-        float sum = 0.f, cs = 0.f;
-        if (gm != -INFINITY) {
-          const float gml = gm * kLog2e;
-#pragma unroll
-          for (int c = 0; c < TV4; ++c)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const int t = lane * 4 + 64 * c + q;
-              const float ev = __builtin_amdgcn_exp2f(fmaf(e[4 * c + q], kLog2e, -gml));
-              sum += ev;
-              cs += (t >= c0 && t < c1) ? ev : 0.f;
-            }
-        }
-        sum = group16_sum(sum);
-        cs = group16_sum(cs);
-        float den = sum;
-        if (lse_img != nullptr) {
-          const float li = lse_img[static_cast<size_t>(h) * N + i];
-          den += (gm == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f((li - gm) * kLog2e);
-        }
-        contrib = den > 0.f ? cs / den : 0.f;
+      for (int c = 0; c < TV4; ++c) {
+        const int t = lane * 4 + 64 * c;
+        e[4 * c + 0] = (t + 0 < Tv) ? v[jj][c].x : -INFINITY;
+        e[4 * c + 1] = (t + 1 < Tv) ? v[jj][c].y : -INFINITY;
+        e[4 * c + 2] = (t + 2 < Tv) ? v[jj][c].z : -INFINITY;
+        e[4 * c + 3] = (t + 3 < Tv) ? v[jj][c].w : -INFINITY;
       }
-      if (lane == 0) part[r * H + h] = contrib;
+      // One exponential per logit: with gm the row's text max (0 when there is no valid text slot),
+      //   mass = sum_content e^(x-gm) / (sum_valid e^(x-gm) + e^(lse_img-gm)),
+      // which equals sum_content exp(x - LSE) for LSE = log(exp(lse_img) + sum_valid exp(x)).
+      float m = -INFINITY;
+#pragma unroll
+      for (int q = 0; q < TV4 * 4; ++q) m = fmaxf(m, e[q]);
+      const float gm = group16_max(m);
+      const float gmu = gm == -INFINITY ? 0.f : gm;
+      const float gml = gmu * kLog2e;
+      float sum = 0.f, cs = 0.f;
+#pragma unroll
+      for (int c = 0; c < TV4; ++c)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int t = lane * 4 + 64 * c + q;
+          const float ev = __builtin_amdgcn_exp2f(fmaf(e[4 * c + q], kLog2e, -gml));
+          sum += ev;
+          cs += (t >= c0 && t < c1) ? ev : 0.f;
+        }
+      sum = group16_sum(sum);
+      cs = group16_sum(cs);
+      float den = sum;
+      if (lse_img != nullptr) den += __builtin_amdgcn_exp2f((li[jj] - gmu) * kLog2e);
+      const float contrib = den > 0.f ? cs / den : 0.f;
+      if (ok && lane == 0) part[r * H + h] = contrib;
     }
   }
   __syncthreads();

@@ -35,10 +35,21 @@ __global__ __launch_bounds__(256) void k_swcfg_vec(const float4* __restrict__ ec
   const uint32_t y = row - fdiv(row, hl) * hl.b;
   const uint32_t trow = fdiv(y, ph) * side;
   float4 o;
-  o.x = guided(c.x, u.x, fmaf(g_d, sv[trow + fdiv(x0 + 0, pw)], g_ctx));
-  o.y = guided(c.y, u.y, fmaf(g_d, sv[trow + fdiv(x0 + 1, pw)], g_ctx));
-  o.z = guided(c.z, u.z, fmaf(g_d, sv[trow + fdiv(x0 + 2, pw)], g_ctx));
-  o.w = guided(c.w, u.w, fmaf(g_d, sv[trow + fdiv(x0 + 3, pw)], g_ctx));
+  if (pw.b >= 2) {
+    // four consecutive pixels span at most two tokens: load the first and the last one's score
+    const uint32_t tf = fdiv(x0, pw), tl = fdiv(x0 + 3, pw);
+    const uint32_t split = (tf + 1) * pw.b;  // first pixel of the next token
+    const float ga = fmaf(g_d, sv[trow + tf], g_ctx), gb = fmaf(g_d, sv[trow + tl], g_ctx);
+    o.x = guided(c.x, u.x, ga);
+    o.y = guided(c.y, u.y, x0 + 1 >= split ? gb : ga);
+    o.z = guided(c.z, u.z, x0 + 2 >= split ? gb : ga);
+    o.w = guided(c.w, u.w, gb);
+  } else {
+    o.x = guided(c.x, u.x, fmaf(g_d, sv[trow + x0 + 0], g_ctx));
+    o.y = guided(c.y, u.y, fmaf(g_d, sv[trow + x0 + 1], g_ctx));
+    o.z = guided(c.z, u.z, fmaf(g_d, sv[trow + x0 + 2], g_ctx));
+    o.w = guided(c.w, u.w, fmaf(g_d, sv[trow + x0 + 3], g_ctx));
+  }
   out4[e] = o;
 }
 
