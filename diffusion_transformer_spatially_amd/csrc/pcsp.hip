@@ -341,9 +341,189 @@ __global__ __launch_bounds__(kPartThreads) void k_partition(const float* __restr
   }
 }
 
+// Register-resident form for N <= 1024 * IPT.  Wave w owns the CH = 64 * IPT consecutive indices
+// [w * CH, (w + 1) * CH); lane l holds item j at index w * CH + 64 j + l, so every load is coalesced
+// and, for each j, the wave's 64 lanes cover 64 consecutive indices.  The keys are loaded once and stay
+// in registers for every pass.  The radix select starts at the highest bit in which the keys differ
+// (block AND / OR of the keys), so the leading bits that all keys share -- sign and exponent for scores
+// of one magnitude -- cost no pass, and no pass piles every key onto one histogram bin.  The output
+// walks each wave's items in index order with ballots (rank among the wave's earlier lanes by mbcnt,
+// running totals in scalars); one block scan of the per-wave totals gives each wave its base.  Slots
+// past N hold key 0 (the NaN key) and take part in the counts: they are the lowest keys and, among
+// equal keys, the highest indices, so they never reach S (k <= N) and never move the k-th largest key;
+// only the AND / OR and the stores skip them.
+__device__ __forceinline__ float key_value(uint32_t key) {
+  if (key == 0u) return NAN;
+  return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
+}
+
+// Number of set bits of a wave ballot in the lanes below this one.
+__device__ __forceinline__ uint32_t lanes_below(unsigned long long b) {
+  return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(b >> 32),
+                                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(b), 0u));
+}
+
+template <int IPT>
+__global__ __launch_bounds__(kPartThreads) void k_partition_reg(const float* __restrict__ scores, int N, int k,
+                                                                int32_t* __restrict__ S, int32_t* __restrict__ C,
+                                                                uint8_t* __restrict__ is_sens,
+                                                                float* __restrict__ s01) {
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t wred[4][kPartWaves];
+  __shared__ uint32_t sel_digit, sel_above;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int base = w * 64 * IPT + lane;  // index of item j: base + 64 j
+
+  uint32_t key[IPT];
+  uint32_t kand = 0xffffffffu, kor = 0u;
+  float lo = INFINITY, hi = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < IPT; ++j) {
+    const int i = base + 64 * j;
+    const float a = i < N ? scores[i] : NAN;
+    key[j] = order_key(a);
+    kand &= i < N ? key[j] : 0xffffffffu;
+    kor |= i < N ? key[j] : 0u;
+    lo = fminf(lo, a);
+    hi = fmaxf(hi, a);
+  }
+  for (int o = 32; o >= 1; o >>= 1) {
+    kand &= __shfl_xor(kand, o, 64);
+    kor |= __shfl_xor(kor, o, 64);
+    lo = fminf(lo, __shfl_xor(lo, o, 64));
+    hi = fmaxf(hi, __shfl_xor(hi, o, 64));
+  }
+  if (lane == 0) {
+    wred[0][w] = kand;
+    wred[1][w] = kor;
+    wred[2][w] = __float_as_uint(lo);
+    wred[3][w] = __float_as_uint(hi);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kPartWaves; ++j) {
+    kand &= wred[0][j];
+    kor |= wred[1][j];
+    lo = fminf(lo, __uint_as_float(wred[2][j]));
+    hi = fmaxf(hi, __uint_as_float(wred[3][j]));
+  }
+  __syncthreads();
+  const bool all_nan = !(lo <= hi);
+
+  // ---- radix select of the k-th largest key over the bits in which the keys differ
+  uint32_t prefix = 0, pmask = 0, remaining = static_cast<uint32_t>(k);
+  if (k > 0) {
+    const uint32_t diff = kand ^ kor;
+    int hb = diff != 0u ? 31 - __clz(diff) : -1;  // highest differing bit; -1: all keys equal
+    pmask = hb < 0 ? 0xffffffffu : hb == 31 ? 0u : ~((2u << hb) - 1u);
+    prefix = kand & pmask;
+    while (hb >= 0) {
+      const int lob = hb >= 7 ? hb - 7 : 0;
+      const uint32_t dmask = (2u << (hb - lob)) - 1u;
+      if (tid < 256) hist[tid] = 0;
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < IPT; ++j)
+        if ((key[j] & pmask) == prefix) atomicAdd(&hist[(key[j] >> lob) & dmask], 1u);
+      __syncthreads();
+      if (w == 0) {
+        // lane l owns bins 255-4l .. 252-4l (descending); find where the running count from the top
+        // first reaches `remaining`
+        uint32_t c[4], loc = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) { c[j] = hist[255 - 4 * lane - j]; loc += c[j]; }
+        uint32_t inc = loc;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const uint32_t y = __shfl_up(inc, o, 64);
+          if (lane >= o) inc += y;
+        }
+        const uint32_t exc = inc - loc;
+        if (exc < remaining && remaining <= inc) {
+          uint32_t acc = exc;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            if (acc + c[j] >= remaining) { sel_digit = 255u - 4u * lane - j; sel_above = acc; break; }
+            acc += c[j];
+          }
+        }
+      }
+      __syncthreads();
+      remaining -= sel_above;
+      prefix |= sel_digit << lob;
+      pmask |= dmask << lob;
+      hb = lob - 1;
+    }
+  }
+  const uint32_t kstar = prefix;
+  const uint32_t need = (k > 0) ? remaining : 0u;  // how many keys equal to K* are taken
+
+  // ---- output.  Pass 1: each wave's count of keys equal to K*; block scan -> the wave's base rank.
+  uint32_t w_eq = 0;
+#pragma unroll
+  for (int j = 0; j < IPT; ++j) w_eq += static_cast<uint32_t>(__popcll(__ballot(k > 0 && key[j] == kstar)));
+  if (lane == 0) wred[0][w] = w_eq;
+  __syncthreads();
+  uint32_t eq_run = 0;
+  for (int j = 0; j < w; ++j) eq_run += wred[0][j];
+  // Pass 2: each wave's count of selected keys (equal keys in index order against `need`).
+  uint32_t w_sel = 0;
+  {
+    uint32_t run = eq_run;
+#pragma unroll
+    for (int j = 0; j < IPT; ++j) {
+      const unsigned long long be = __ballot(k > 0 && key[j] == kstar);
+      const bool eq = (be >> lane) & 1ull;
+      const bool sel = k > 0 && (key[j] > kstar || (eq && run + lanes_below(be) < need));
+      w_sel += static_cast<uint32_t>(__popcll(__ballot(sel)));
+      run += static_cast<uint32_t>(__popcll(be));
+    }
+  }
+  if (lane == 0) wred[1][w] = w_sel;
+  __syncthreads();
+  uint32_t s_run = 0;
+  for (int j = 0; j < w; ++j) s_run += wred[1][j];
+  // Pass 3: write S, C, is_sens and s01 in index order.  The bound goes through an empty asm so that
+  // the compiler does not keep the IPT lane masks of the load loop alive until here (they spill).
+  int n_end = N;
+  asm volatile("" : "+s"(n_end));
+#pragma unroll
+  for (int j = 0; j < IPT; ++j) {
+    const int i = base + 64 * j;
+    const unsigned long long be = __ballot(k > 0 && key[j] == kstar);
+    const bool eq = (be >> lane) & 1ull;
+    const bool sel = k > 0 && (key[j] > kstar || (eq && eq_run + lanes_below(be) < need));
+    const unsigned long long bs = __ballot(sel);
+    const uint32_t s_pos = s_run + lanes_below(bs);
+    if (i < n_end) {
+      if (sel) S[s_pos] = i;
+      else C[static_cast<uint32_t>(i) - s_pos] = i;
+      is_sens[i] = sel ? 1 : 0;
+      if (s01 != nullptr) {
+        const float a = key_value(key[j]);
+        float v;
+        if (a != a || all_nan) v = NAN;
+        else if (hi > lo) v = (a - lo) / (hi - lo);
+        else v = 0.f;
+        s01[i] = v;
+      }
+    }
+    eq_run += static_cast<uint32_t>(__popcll(be));
+    s_run += static_cast<uint32_t>(__popcll(bs));
+  }
+}
+
 hipError_t launch_pcsp_partition(const float* scores, int N, int k, int32_t* S, int32_t* C, uint8_t* is_sens,
                                  float* s01, hipStream_t s) {
-  k_partition<<<1, kPartThreads, 0, s>>>(scores, N, k, S, C, is_sens, s01);
+  const int ipt = (N + kPartThreads - 1) / kPartThreads;
+  if (ipt <= 1) k_partition_reg<1><<<1, kPartThreads, 0, s>>>(scores, N, k, S, C, is_sens, s01);
+  else if (ipt <= 2) k_partition_reg<2><<<1, kPartThreads, 0, s>>>(scores, N, k, S, C, is_sens, s01);
+  else if (ipt <= 4) k_partition_reg<4><<<1, kPartThreads, 0, s>>>(scores, N, k, S, C, is_sens, s01);
+  else if (ipt <= 8) k_partition_reg<8><<<1, kPartThreads, 0, s>>>(scores, N, k, S, C, is_sens, s01);
+  else if (ipt <= 16) k_partition_reg<16><<<1, kPartThreads, 0, s>>>(scores, N, k, S, C, is_sens, s01);
+  else if (ipt <= 32) k_partition_reg<32><<<1, kPartThreads, 0, s>>>(scores, N, k, S, C, is_sens, s01);
+  else if (ipt <= 40) k_partition_reg<40><<<1, kPartThreads, 0, s>>>(scores, N, k, S, C, is_sens, s01);
+  else k_partition<<<1, kPartThreads, 0, s>>>(scores, N, k, S, C, is_sens, s01);
   return hipGetLastError();
 }
 
