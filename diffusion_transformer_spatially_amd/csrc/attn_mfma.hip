@@ -25,7 +25,8 @@
 //    movement), the V^T operand is read from row-major LDS with ds_read_b64_tr_b16;
 //  * with two query blocks per wave the tile is staggered: the logits of block 1 and the output update
 //    of block 0 are issued alongside the softmax of the other block, so one wave keeps its matrix and
-//    vector work overlapped (sched_group_barrier sets the interleave);
+//    vector work overlapped: each matrix instruction of one block is followed by the exp2 / pack /
+//    row-sum work of 4 logits of the other, in a fixed order (sched_barrier between the groups);
 //  * full image tiles run a loop without any masking; the ragged image tail and the text tiles run a
 //    separate path that masks keys past the valid count and, for the warmup emission, stores the
 //    text-block logits and the image-block log-sum-exp;
@@ -258,10 +259,26 @@ __device__ __forceinline__ float fast_exact(bf16x8 (&p)[2][2], const bf16x8 (&q)
   return fast_probs<false>(p, sx, g, kBN);
 }
 
-// Two query blocks, staggered: logits of block 0; logits of block 1 alongside the softmax of block 0;
-// output update of block 0 alongside the softmax of block 1; output update of block 1.  The vector
-// work of one block runs while the matrix cores work for the other (sched_group_barrier interleaves the
-// two streams inside the wave).
+// 4 logits of one block (chunk c of 8: half kb = c>>2, word group mm = (c>>1)&1, quarter h = c&1):
+// exp2, pack to bf16 pairs, add to the row sum.
+__device__ __forceinline__ void soft_chunk(uint32_t (&pk)[2][2][4], const f32x16 (&s)[2], float& tsum, int c) {
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  const int kb = c >> 2, mm = (c >> 1) & 1, h = c & 1;
+  const int i0 = 8 * mm + 4 * h;
+  const uint32_t w0 = pack_bf16x2(__builtin_amdgcn_exp2f(s[kb][i0 + 0]), __builtin_amdgcn_exp2f(s[kb][i0 + 1]));
+  const uint32_t w1 = pack_bf16x2(__builtin_amdgcn_exp2f(s[kb][i0 + 2]), __builtin_amdgcn_exp2f(s[kb][i0 + 3]));
+  pk[kb][mm][2 * h] = w0;
+  pk[kb][mm][2 * h + 1] = w1;
+  tsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w0), ones, tsum, false);
+  tsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w1), ones, tsum, false);
+}
+
+// Two query blocks, staggered: logits of block 0; logits of block 1 interleaved with the softmax of
+// block 0; the V operands; output update of block 0 interleaved with the softmax of block 1; output
+// update of block 1.  Each interleaved group is one MFMA (32 cycles) and the vector work of 4 logits
+// (4 exp2, 2 packs, 2 dot products, about as long); sched_barrier pins the groups in this order, which
+// the scheduler otherwise bunches into long vector runs with the matrix core idle.  The lazy-max exact
+// path of a block runs between its softmax and its output update.
 template <bool MASKED>
 __device__ __forceinline__ void tile_step_fast2(WaveState<2>& st, const uint16_t* kl, const uint16_t* vl, int kperm,
                                                 int g, int li, int dc0, int nvalid) {
@@ -287,20 +304,35 @@ __device__ __forceinline__ void tile_step_fast2(WaveState<2>& st, const uint16_t
   for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) s0[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kb][ks], st.q[0][ks], s0[kb], 0, 0, 0);
-  __builtin_amdgcn_sched_barrier(0);
-  // logits of block 1 | softmax of block 0
+  if (MASKED) {
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) s1[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kb][ks], st.q[1][ks], s1[kb], 0, 0, 0);
-  bf16x8 p0[2][2];
-  float t0 = fast_probs<MASKED>(p0, s0, g, nvalid);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+      for (int i = 0; i < 16; ++i) s0[kb][i] = (kb * 32 + 16 * g + i) < nvalid ? s0[kb][i] : -INFINITY;
   }
   __builtin_amdgcn_sched_barrier(0);
+  // logits of block 1 | softmax of block 0, one MFMA per 4 logits
+  uint32_t pk0[2][2][4];
+  float t0 = 0.f;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const int ks = c >> 1, kb = c & 1;
+    s1[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kb][ks], st.q[1][ks], s1[kb], 0, 0, 0);
+    soft_chunk(pk0, s0, t0, c);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (MASKED) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s1[kb][i] = (kb * 32 + 16 * g + i) < nvalid ? s1[kb][i] : -INFINITY;
+  }
+  bf16x8 p0[2][2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int mm = 0; mm < 2; ++mm)
+      p0[kb][mm] = __builtin_bit_cast(bf16x8, (uint4){pk0[kb][mm][0], pk0[kb][mm][1], pk0[kb][mm][2], pk0[kb][mm][3]});
   if (__any(!(t0 <= 65536.f))) t0 = fast_exact<MASKED>(p0, st.q[0], st.m[0], st.l[0], st.o[0], kl, kperm, g, nvalid);
   st.l[0] += t0;
   // V^T operands (shared by both blocks)
@@ -320,23 +352,26 @@ __device__ __forceinline__ void tile_step_fast2(WaveState<2>& st, const uint16_t
         va[kb][mm][db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       }
     }
-  // output update of block 0 | softmax of block 1
+  __builtin_amdgcn_sched_barrier(0);
+  // output update of block 0 | softmax of block 1: two chunks first (covering the V reads' latency)
+  uint32_t pk1[2][2][4];
+  float t1 = 0.f;
+  soft_chunk(pk1, s1, t1, 0);
+  soft_chunk(pk1, s1, t1, 1);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int kb = i >> 2, mm = (i >> 1) & 1, db = i & 1;
+    st.o[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[kb][mm][db], p0[kb][mm], st.o[0][db], 0, 0, 0);
+    if (i + 2 < 8) soft_chunk(pk1, s1, t1, i + 2);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  bf16x8 p1[2][2];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int mm = 0; mm < 2; ++mm)
-#pragma unroll
-      for (int db = 0; db < 2; ++db)
-        st.o[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[kb][mm][db], p0[kb][mm], st.o[0][db], 0, 0, 0);
-  bf16x8 p1[2][2];
-  float t1 = fast_probs<MASKED>(p1, s1, g, nvalid);
-  __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);  // the V reads first
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-  }
-  __builtin_amdgcn_sched_barrier(0);
+      p1[kb][mm] = __builtin_bit_cast(bf16x8, (uint4){pk1[kb][mm][0], pk1[kb][mm][1], pk1[kb][mm][2], pk1[kb][mm][3]});
   if (__any(!(t1 <= 65536.f))) t1 = fast_exact<MASKED>(p1, st.q[1], st.m[1], st.l[1], st.o[1], kl, kperm, g, nvalid);
   st.l[1] += t1;
   // output update of block 1
@@ -748,7 +783,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const int n_full = a.N / kBN;  // image tiles with all 64 keys valid
   const int n_txt = (tv + kBN - 1) / kBN;
   const int ntiles = n_img + n_txt;
-  const bool emit = b == 0 && (a.xattn_out != nullptr || a.lse_img_out != nullptr);
+  // the warmup emission only runs on the exact-sum path (the host picks it whenever an output asks for it)
+  const bool emit = EXACT_SUM && b == 0 && (a.xattn_out != nullptr || a.lse_img_out != nullptr);
   const float c2 = a.scale * kLog2e;
   if constexpr (!EXACT_SUM) {
 #pragma unroll
@@ -831,10 +867,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   }
   // ---- ragged image tail and text tiles (tile t sits in buffer a when t is even)
   for (; t < ntiles; ++t) {
-    if ((t & 1) == 0)
-      masked_tile(t, k_a, v_a, k_b, v_b);
-    else
-      masked_tile(t, k_b, v_b, k_a, v_a);
+    const bool odd = (t & 1) != 0;
+    masked_tile(t, odd ? k_b : k_a, odd ? v_b : v_a, odd ? k_a : k_b, odd ? v_a : v_b);
   }
   if (emit && n_txt == 0 && a.lse_img_out != nullptr) store_lse_img(a, st, h, row, valid, g);
 
