@@ -211,7 +211,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": dense_tf, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": dense_tf / MFMA_BF16_PEAK_TFLOPS, "traffic": profiled_traffic(),
                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE/WRITE_SIZE, copy-calibrated)",
-                     "kernel": "k_attn_mfma<false, 2, false, 0> (dense anchor attention)",
+                     "kernel": "k_attn_mfma<false, 2, false, 0, 1> (dense anchor attention)",
                      "flops_per_launch": w.flops_dense, "avg_launch_ms": avg_ms["attn_dense"],
                      "sclk_mhz": sclk, "peak_at_sclk": peak_sclk,
                      "frac_at_sclk": (dense_tf / peak_sclk) if peak_sclk else None,

@@ -30,7 +30,11 @@
 //  * full image tiles run a loop without any masking; the ragged image tail and the text tiles run a
 //    separate path that masks keys past the valid count and, for the warmup emission, stores the
 //    text-block logits and the image-block log-sum-exp;
-//  * gathered rows: Q rows are loaded from rows[r] and outputs scattered to rows[r] in the epilogue.
+//  * gathered rows: Q rows are loaded from rows[r] and outputs scattered to rows[r] in the epilogue;
+//  * few query rows (too few waves to fill the GPU): 8-wave workgroups, waves 0-3 take the first half
+//    of the key tiles and waves 4-7 the rest, each half with its own LDS buffers; at the end the
+//    second half's running max, row sum and output accumulators go through LDS to the first half,
+//    which merges them (the usual rescale by exp2 of the max differences) and writes the output.
 // The workgroup id is remapped so that the Q tiles of one (b,h) run on the same XCD and share K/V
 // in that XCD's L2.
 #include "common.hpp"
@@ -103,7 +107,7 @@ __device__ __forceinline__ TileSrc tile_src(const AttnArgs& a, size_t bh, int t,
 template <bool OPAQUE>
 __device__ __forceinline__ void stage_issue(const TileSrc& s, uint16_t* kl, uint16_t* vl) {
   const int lane = threadIdx.x & 63;
-  int wslot = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6)) * 64;
+  int wslot = __builtin_amdgcn_readfirstlane(static_cast<int>((threadIdx.x >> 6) & 3)) * 64;
   if (OPAQUE) asm volatile("" : "+s"(wslot));
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
@@ -729,17 +733,25 @@ __device__ __forceinline__ void store_lse_img(const AttnArgs& a, const WaveState
   }
 }
 
-template <bool GATHER, int QB, bool EXACT_SUM, int KM>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void k_attn_mfma(AttnArgs a) {
+template <bool GATHER, int QB, bool EXACT_SUM, int KM, int KS>
+__global__ __launch_bounds__(kThreads * KS) __attribute__((amdgpu_waves_per_eu(2))) void k_attn_mfma(AttnArgs a) {
+  static_assert(KS == 1 || (KS == 2 && !EXACT_SUM && KM == 0), "key halves only on the mask-free fast path");
   constexpr int kRowsW = 32 * QB;
   constexpr int kBM = kWaves * kRowsW;
   // Two LDS buffers as distinct objects: every read and every DMA target below names one of them
   // statically, so the compiler can see that the prefetch into one never aliases reads of the other
-  // and does not wait for the prefetch before computing.
-  __shared__ __attribute__((aligned(16))) uint16_t k_a[kTileElems];
-  __shared__ __attribute__((aligned(16))) uint16_t v_a[kTileElems];
-  __shared__ __attribute__((aligned(16))) uint16_t k_b[kTileElems];
-  __shared__ __attribute__((aligned(16))) uint16_t v_b[kTileElems];
+  // and does not wait for the prefetch before computing.  With KS = 2 each key half of the workgroup
+  // has its own pair.
+  __shared__ __attribute__((aligned(16))) uint16_t k_as[KS][kTileElems];
+  __shared__ __attribute__((aligned(16))) uint16_t v_as[KS][kTileElems];
+  __shared__ __attribute__((aligned(16))) uint16_t k_bs[KS][kTileElems];
+  __shared__ __attribute__((aligned(16))) uint16_t v_bs[KS][kTileElems];
+  // key half of this wave (KS = 2: waves 0-3 take the first half of the key tiles, waves 4-7 the rest)
+  const int half = KS == 1 ? 0 : __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 8));
+  uint16_t* const k_a = k_as[half];
+  uint16_t* const v_a = v_as[half];
+  uint16_t* const k_b = k_bs[half];
+  uint16_t* const v_b = v_bs[half];
 
   const int nqt = (a.R + kBM - 1) / kBM;
   const uint32_t G = static_cast<uint32_t>(a.B) * a.H * nqt;
@@ -750,7 +762,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const int b = bhi / a.H, h = bhi - b * a.H;
   const int tv = a.tv[b];
 
-  const int w = threadIdx.x >> 6;
+  const int w = (threadIdx.x >> 6) & 3;
   const int L = threadIdx.x & 63;
   const int qi = L & 31;  // query column of the MFMA tiles owned by this lane
   const int g = L >> 5;   // lane half
@@ -783,6 +795,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const int n_full = a.N / kBN;  // image tiles with all 64 keys valid
   const int n_txt = (tv + kBN - 1) / kBN;
   const int ntiles = n_img + n_txt;
+  // this wave's key tiles [t_begin, t_end); with two key halves the shorter half passes `pad` extra
+  // barriers so that both halves pass the same number
+  int t_begin = 0, t_end = ntiles, pad = 0;
+  if constexpr (KS == 2) {
+    const int n0 = (ntiles + 1) >> 1;
+    t_begin = half ? n0 : 0;
+    t_end = half ? ntiles : n0;
+    pad = half ? 2 * n0 - ntiles : 0;
+  }
   // the warmup emission only runs on the exact-sum path (the host picks it whenever an output asks for it)
   const bool emit = EXACT_SUM && b == 0 && (a.xattn_out != nullptr || a.lse_img_out != nullptr);
   const float c2 = a.scale * kLog2e;
@@ -818,7 +839,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   MaskTile<KM> mcur, mnext;
   mask_fetch(mcur, 0);
 
-  stage_issue<(QB > 1)>(tile_src(a, bh, 0, n_img, tv), k_a, v_a);
+  if (t_begin < t_end) stage_issue<(QB > 1)>(tile_src(a, bh, t_begin, n_img, tv), k_a, v_a);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
@@ -826,7 +847,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   // One tile: prefetch tile t+1 into the other buffer, compute on this one, then wait for the
   // prefetch and synchronise.
   auto full_tile = [&](int t, const uint16_t* ck, const uint16_t* cv, uint16_t* nk, uint16_t* nv) {
-    if (t + 1 < ntiles) {
+    if (t + 1 < t_end) {
       stage_issue<(QB > 1)>(tile_src(a, bh, t + 1, n_img, tv), nk, nv);
       mask_fetch(mnext, t + 1);
     }
@@ -837,7 +858,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   };
   auto masked_tile = [&](int t, const uint16_t* ck, const uint16_t* cv, uint16_t* nk, uint16_t* nv) {
     if (emit && t == n_img && a.lse_img_out != nullptr) store_lse_img(a, st, h, row, valid, g);
-    if (t + 1 < ntiles) {
+    if (t + 1 < t_end) {
       stage_issue<(QB > 1)>(tile_src(a, bh, t + 1, n_img, tv), nk, nv);
       mask_fetch(mnext, t + 1);
     }
@@ -855,22 +876,62 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     if constexpr (KM != 0) mcur = mnext;
   };
 
-  int t = 0;
+  int t = t_begin;
+  const int f_end = min(t_end, n_full);
   // ---- full image tiles, two per iteration (buffer a, then buffer b)
-  for (; t + 1 < n_full; t += 2) {
+  for (; t + 1 < f_end; t += 2) {
     full_tile(t, k_a, v_a, k_b, v_b);
     full_tile(t + 1, k_b, v_b, k_a, v_a);
   }
-  if (t < n_full) {
+  if (t < f_end) {
     full_tile(t, k_a, v_a, k_b, v_b);
     ++t;
   }
-  // ---- ragged image tail and text tiles (tile t sits in buffer a when t is even)
-  for (; t < ntiles; ++t) {
-    const bool odd = (t & 1) != 0;
+  // ---- ragged image tail and text tiles (tile t sits in buffer a when t - t_begin is even)
+  for (; t < t_end; ++t) {
+    const bool odd = ((t - t_begin) & 1) != 0;
     masked_tile(t, odd ? k_b : k_a, odd ? v_b : v_a, odd ? k_a : k_b, odd ? v_a : v_b);
   }
   if (emit && n_txt == 0 && a.lse_img_out != nullptr) store_lse_img(a, st, h, row, valid, g);
+
+  if constexpr (KS == 2) {
+    for (int i = 0; i < pad; ++i) __syncthreads();
+    // merge the second key half into the first through LDS (the tile buffers are idle now): per query
+    // block, the partner wave's running max, row sum and output accumulators, each lane with the
+    // lane of the same index (same rows, same register layout)
+    float* const xo0 = reinterpret_cast<float*>(&k_as[0][0]);  // [4 waves][16][64]
+    float* const xo1 = reinterpret_cast<float*>(&v_as[0][0]);
+    float* const xml = reinterpret_cast<float*>(&k_bs[0][0]);  // [4 waves][2][64]
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      if (half == 1) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          xo0[(w * 16 + i) * 64 + L] = st.o[qb][0][i];
+          xo1[(w * 16 + i) * 64 + L] = st.o[qb][1][i];
+        }
+        xml[(w * 2 + 0) * 64 + L] = st.m[qb];
+        xml[(w * 2 + 1) * 64 + L] = st.l[qb];
+      }
+      __syncthreads();
+      if (half == 0) {
+        const float m1 = xml[(w * 2 + 0) * 64 + L], l1 = xml[(w * 2 + 1) * 64 + L];
+        const float m0 = st.m[qb];
+        const float mm = fmaxf(m0, m1);
+        const float a0 = mm == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m0 - mm);
+        const float a1 = mm == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - mm);
+        st.m[qb] = mm;
+        st.l[qb] = a0 * st.l[qb] + a1 * l1;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          st.o[qb][0][i] = a0 * st.o[qb][0][i] + a1 * xo0[(w * 16 + i) * 64 + L];
+          st.o[qb][1][i] = a0 * st.o[qb][1][i] + a1 * xo1[(w * 16 + i) * 64 + L];
+        }
+      }
+      __syncthreads();
+    }
+    if (half == 1) return;
+  }
 
   // ---- epilogue: normalise, write the output rows (scatter for gathered rows) and their lse
 #pragma unroll
@@ -893,12 +954,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   }
 }
 
-template <bool GATHER, int QB, bool EXACT_SUM, int KM>
+template <bool GATHER, int QB, bool EXACT_SUM, int KM, int KS = 1>
 static void launch(const AttnArgs& a, hipStream_t s) {
   constexpr int kBM = kWaves * 32 * QB;
   const int nqt = (a.R + kBM - 1) / kBM;
   const uint32_t grid = static_cast<uint32_t>(a.B) * a.H * nqt;
-  k_attn_mfma<GATHER, QB, EXACT_SUM, KM><<<grid, kThreads, 0, s>>>(a);
+  k_attn_mfma<GATHER, QB, EXACT_SUM, KM, KS><<<grid, kThreads * KS, 0, s>>>(a);
 }
 
 template <bool GATHER, int QB, int KM>
@@ -916,10 +977,21 @@ static void launch_rows(const AttnArgs& a, hipStream_t s) {
     else launch_sum<GATHER, 1, 2>(a, s);
     return;
   }
-  // Two query blocks per wave when that still fills the GPU's wave slots at least once over.
+  // Work shape by the number of two-block waves w2 against the GPU's 2048 wave slots (thresholds from
+  // measurements of the 1024^2 rows launch at |S| = 128 ... 2048):
+  //   w2 >= 2048: two query blocks per wave;
+  //   the exact-sum path, or 1024 < w2 < 2048: one query block per wave (twice the waves);
+  //   512 <= w2 <= 1024 (mask-free fast path): two query blocks per wave and the key range of each
+  //   workgroup split into two halves run by 8 waves, merged at the end;
+  //   w2 < 512: one query block per wave with the key range split in two.
+  // (An 8-wave workgroup holds a whole CU, so the split only pays while its workgroups fit in about
+  // one round over the 256 CUs.)
   const double waves_qb2 = static_cast<double>(a.B) * a.H * ((a.R + 63) / 64);
+  const bool exact = a.lse != nullptr || a.lse_img_out != nullptr || a.xattn_out != nullptr;
   if (waves_qb2 >= 2048.0) launch_sum<GATHER, 2, 0>(a, s);
-  else launch_sum<GATHER, 1, 0>(a, s);
+  else if (exact || waves_qb2 > 1024.0) launch_sum<GATHER, 1, 0>(a, s);
+  else if (waves_qb2 >= 512.0) launch<GATHER, 2, false, 0, 2>(a, s);
+  else launch<GATHER, 1, false, 0, 2>(a, s);
 }
 
 hipError_t launch_attn_mfma_bf16(const AttnArgs& a, hipStream_t s) {

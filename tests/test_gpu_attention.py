@@ -132,6 +132,34 @@ def test_bf16_rows_parity_and_untouched_context(lib, k):
         assert np.array_equal(o, od)
 
 
+@pytest.mark.parametrize("B,H,N,T,tv,k", [
+    (1, 8, 2000, 256, (77,), None),         # few two-block waves: one block per wave, key range in two halves
+    (2, 8, 2304, 256, (120, 3), None),      # 576 two-block waves: two blocks per wave, key halves
+    (2, 8, 4096, 64, (64, 64), None),       # 1024 two-block waves: the largest split case
+    (2, 8, 4160, 256, (77, 0), None),       # 1040: one block per wave, no split
+    (2, 24, 4096, 256, (77, 77), 1229),     # the 1024^2 rows launch: two blocks per wave, key halves, gathered
+    (1, 3, 193, 0, (0,), None),             # 4 key tiles: halves of 2 and 2 (ragged tail in the second)
+    (1, 3, 130, 0, (0,), None),             # 3 key tiles: the second half passes one extra barrier
+])
+def test_bf16_key_split_dispatch_parity(lib, B, H, N, T, tv, k):
+    """Every work shape of the mask-free fast path (one or two query blocks per wave, with or without the
+    key range split across two halves of a workgroup) against the oracle, element by element."""
+    w = syn.scaled(syn.WORKLOADS["srsu_1024"], B=B, H=H, N=N, T=T, tv=tv, side=1)
+    inp = syn.attention_inputs(w)
+    if k is None:
+        o, _, _, _ = _run(lib, w, inp, want_lse=False)
+        ro, _ = _oracle(w, inp)
+        assert_close(o, ro, "bf16", f"dense B{B}H{H}N{N}")
+    else:
+        rows = syn.random_rows(w, k=k)
+        state = syn.initial_state(w)
+        o, _, _, _ = _run(lib, w, inp, rows=rows, state=state, want_lse=False)
+        ro, _ = _oracle(w, inp, rows=rows)
+        assert_close(o[:, :, rows], ro, "bf16", f"rows B{B}H{H}N{N}k{k}")
+        C = np.setdiff1d(np.arange(w.N), rows)
+        assert np.array_equal(o[:, :, C], state[:, :, C].astype(np.float64))
+
+
 def test_bf16_padding_contents_never_leak(lib):
     w = syn.scaled(syn.WORKLOADS["dense_1024"], B=2, H=2, N=200, T=256, tv=(77, 3), side=1)
     inp = syn.attention_inputs(w)
