@@ -308,21 +308,19 @@ def gpu_busy(torch, ms=1.0):
 
 
 def time_launches(torch, fn, reps=20):
-    """Median duration (ms) of `reps` launches, each bracketed by its own HIP events and queued behind
-    a spin so that they run back to back."""
-    import numpy as np
+    """Average duration (ms) of `reps` back-to-back launches between one pair of HIP events, queued
+    behind a spin so that they run back to back (one event pair per launch would add the dispatch of
+    each event packet to every kernel, about 2 us, which is a third of a 6 us kernel)."""
     fn()
     torch.cuda.synchronize()
     gpu_busy(torch, 0.05 * reps + 0.5)
-    pairs = []
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
     for _ in range(reps):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
         fn()
-        e1.record()
-        pairs.append((e0, e1))
+    e1.record()
     torch.cuda.synchronize()
-    return float(np.median([a.elapsed_time(b) for a, b in pairs]))
+    return e0.elapsed_time(e1) / reps
 
 
 def hbm_large(dts, torch, np, syn, dev, state, rows, hbm):
