@@ -16,7 +16,8 @@ LIB_PATH = os.path.join(_HERE, "libsafe_attn.so")
 
 SAFE_DTYPE_BF16, SAFE_DTYPE_F32, SAFE_DTYPE_BOOL = 0, 1, 2
 SAFE_MAX_BATCH = 64
-EXPORTS = ("safe_attn_dense", "safe_attn_rows", "safe_mask_is_row_constant", "safe_pcsp_accumulate",
+EXPORTS = ("safe_attn_dense", "safe_attn_rows", "safe_mask_is_row_constant", "safe_mask_check_launch",
+           "safe_pcsp_accumulate",
            "safe_pcsp_partition", "safe_swcfg_combine", "safe_gather_rows", "safe_scatter_rows",
            "safe_status_string", "safe_version")
 
@@ -61,6 +62,7 @@ def load(path: Optional[str] = None):
     lib.safe_attn_dense.argtypes = [P(safe_attn_desc), vp]
     lib.safe_attn_rows.argtypes = [P(safe_attn_desc), vp, i32, vp]
     lib.safe_mask_is_row_constant.argtypes = [vp, i32, i32, i32, i32, i32, i32, P(i32), i32, vp, P(i32), vp, vp]
+    lib.safe_mask_check_launch.argtypes = [vp, i32, i32, i32, i32, i32, i32, P(i32), i32, vp, vp, vp]
     lib.safe_pcsp_accumulate.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, vp, i32, vp]
     lib.safe_pcsp_partition.argtypes = [vp, i32, i32, vp, vp, vp, vp, vp]
     lib.safe_swcfg_combine.argtypes = [vp, vp, i32, i32, i32, i32, f32, f32, vp, vp]
@@ -181,6 +183,20 @@ def safe_mask_is_row_constant(mask, N: int, T: int, text_valid_len, flag_ws, c_o
         ctypes.cast(tv, ctypes.POINTER(ctypes.c_int32)), B, _ptr(flag_ws), ctypes.byref(res), _ptr(c_out),
         _stream(stream)), "safe_mask_is_row_constant")
     return bool(res.value)
+
+
+def safe_mask_check_launch(mask, N: int, T: int, text_valid_len, flag_ws, c_out=None, stream=None):
+    """Exact elision check, launched only: flag_ws (device int32[1]) holds the verdict once the stream
+    reaches this point (safe_mask_check_launch)."""
+    if mask.dim() != 4:
+        raise ValueError("mask must be [mask_B, mask_H, N, mask_cols]")
+    B = len(text_valid_len)
+    tv = (ctypes.c_int32 * B)(*[int(x) for x in text_valid_len])
+    _check(load().safe_mask_check_launch(
+        _ptr(mask), _dtype_code(mask), mask.shape[0], mask.shape[1], N, mask.shape[3], T,
+        ctypes.cast(tv, ctypes.POINTER(ctypes.c_int32)), B, _ptr(flag_ws), _ptr(c_out), _stream(stream)),
+        "safe_mask_check_launch")
+    return flag_ws
 
 
 def safe_pcsp_accumulate(x, lse_img, Tv: int, c0: int, c1: int, scores, accumulate: bool, stream=None):

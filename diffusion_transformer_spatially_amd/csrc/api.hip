@@ -107,10 +107,10 @@ safe_status safe_attn_rows(const safe_attn_desc* desc, const int32_t* rows, int3
   return run_attn(desc, rows, k, stream);
 }
 
-safe_status safe_mask_is_row_constant(const void* mask, int32_t mask_dtype, int32_t mask_B, int32_t mask_H, int32_t N,
-                                      int32_t mask_cols, int32_t T, const int32_t* text_valid_len, int32_t B,
-                                      int32_t* flag_ws, int32_t* is_const, float* c_out, hipStream_t stream) {
-  if (mask == nullptr || text_valid_len == nullptr || flag_ws == nullptr || is_const == nullptr) return SAFE_ERR_NULL;
+static safe_status mask_check_validate(const void* mask, int32_t mask_dtype, int32_t mask_B, int32_t mask_H, int32_t N,
+                                       int32_t mask_cols, int32_t T, const int32_t* text_valid_len, int32_t B,
+                                       const int32_t* flag_ws) {
+  if (mask == nullptr || text_valid_len == nullptr || flag_ws == nullptr) return SAFE_ERR_NULL;
   if (mask_dtype != SAFE_DTYPE_F32 && mask_dtype != SAFE_DTYPE_BOOL) return SAFE_ERR_DTYPE;
   if (B < 1 || B > SAFE_MAX_BATCH || N < 1 || T < 0 || mask_H < 1) return SAFE_ERR_SHAPE;
   if (!(mask_B == 1 || mask_B == B)) return SAFE_ERR_SHAPE;
@@ -120,6 +120,15 @@ safe_status safe_mask_is_row_constant(const void* mask, int32_t mask_dtype, int3
   if (static_cast<double>(mask_H) * N > 2.0e9) return SAFE_ERR_SHAPE;
   if (mask_dtype == SAFE_DTYPE_F32 && (reinterpret_cast<uintptr_t>(mask) & 3u) != 0) return SAFE_ERR_ALIGN;
   if ((reinterpret_cast<uintptr_t>(flag_ws) & 3u) != 0) return SAFE_ERR_ALIGN;
+  return SAFE_OK;
+}
+
+safe_status safe_mask_is_row_constant(const void* mask, int32_t mask_dtype, int32_t mask_B, int32_t mask_H, int32_t N,
+                                      int32_t mask_cols, int32_t T, const int32_t* text_valid_len, int32_t B,
+                                      int32_t* flag_ws, int32_t* is_const, float* c_out, hipStream_t stream) {
+  if (is_const == nullptr) return SAFE_ERR_NULL;
+  const safe_status v = mask_check_validate(mask, mask_dtype, mask_B, mask_H, N, mask_cols, T, text_valid_len, B, flag_ws);
+  if (v != SAFE_OK) return v;
   hipError_t e = launch_mask_check(mask, mask_dtype, mask_B, mask_H, N, mask_cols, T, text_valid_len, B, flag_ws,
                                    c_out, stream);
   if (e != hipSuccess) return SAFE_ERR_HIP;
@@ -130,6 +139,15 @@ safe_status safe_mask_is_row_constant(const void* mask, int32_t mask_dtype, int3
   if (e != hipSuccess) return SAFE_ERR_HIP;
   *is_const = h ? 1 : 0;
   return SAFE_OK;
+}
+
+safe_status safe_mask_check_launch(const void* mask, int32_t mask_dtype, int32_t mask_B, int32_t mask_H, int32_t N,
+                                   int32_t mask_cols, int32_t T, const int32_t* text_valid_len, int32_t B,
+                                   int32_t* flag_ws, float* c_out, hipStream_t stream) {
+  const safe_status v = mask_check_validate(mask, mask_dtype, mask_B, mask_H, N, mask_cols, T, text_valid_len, B, flag_ws);
+  if (v != SAFE_OK) return v;
+  return from_hip(launch_mask_check(mask, mask_dtype, mask_B, mask_H, N, mask_cols, T, text_valid_len, B, flag_ws,
+                                    c_out, stream));
 }
 
 safe_status safe_pcsp_accumulate(const float* x, const float* lse_img, int32_t H, int32_t N, int32_t T, int32_t Tv,

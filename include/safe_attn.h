@@ -133,6 +133,18 @@ safe_status safe_mask_is_row_constant(const void* mask, int32_t mask_dtype, int3
                                       hipStream_t stream);
 
 /*
+ * The same exact elision check without the host round trip: launches the scan on `stream` and returns;
+ * when the stream reaches that point, flag_ws holds the verdict (1: the mask is removable, 0: it is not)
+ * and c_out (if not NULL) the per-row constants.  For callers that know the mask before they need the
+ * decision (a fixed mask across the steps of a trajectory): they read flag_ws later, e.g. with an
+ * asynchronous copy and an event, and the check's kernels run beside other work meanwhile.  Arguments
+ * and validation as safe_mask_is_row_constant, without is_const.
+ */
+safe_status safe_mask_check_launch(const void* mask, int32_t mask_dtype, int32_t mask_B, int32_t mask_H, int32_t N,
+                                   int32_t mask_cols, int32_t T, const int32_t* text_valid_len, int32_t B,
+                                   int32_t* flag_ws, float* c_out, hipStream_t stream);
+
+/*
  * PCSP aggregation (SAFE-DiT summary Methodology 2): attention mass from image tokens to the text
  * content slots [c0, c1), summed over heads.  For each head h and image token i,
  *   LSE = log( exp(lse_img[h,i]) + sum_{t<Tv} exp(x[h,i,t]) )      (lse_img == NULL: text only)

@@ -99,6 +99,13 @@ def test_other_entry_validation():
     assert chk(f, 1, 1, 1, 8, 8, 3, tvp, 2, f, ctypes.byref(res), None, None) == RANGE
     assert chk(f + 1, 1, 1, 1, 8, 8, 4, tvp, 2, f, ctypes.byref(res), None, None) == ALIGN
     assert res.value == -1
+    launch = lambda *a: lib.safe_mask_check_launch(*a)
+    assert launch(None, 1, 1, 1, 8, 8, 4, tvp, 2, f, None, None) == NULL
+    assert launch(f, 1, 1, 1, 8, 8, 4, tvp, 2, None, None, None) == NULL
+    assert launch(f, 7, 1, 1, 8, 8, 4, tvp, 2, f, None, None) == DTYPE
+    assert launch(f, 1, 1, 1, 8, 9, 4, tvp, 2, f, None, None) == SHAPE
+    assert launch(f, 1, 1, 1, 8, 8, 3, tvp, 2, f, None, None) == RANGE
+    assert launch(f + 1, 1, 1, 1, 8, 8, 4, tvp, 2, f, None, None) == ALIGN
     acc = lib.safe_pcsp_accumulate
     assert acc(None, None, 2, 8, 16, 4, 0, 4, f, 0, None) == NULL
     assert acc(f, None, 2, 8, 16, 17, 0, 4, f, 0, None) == RANGE

@@ -1,7 +1,10 @@
-"""The attention step's main-stream work (PCSP aggregation, partition, dense and sensitive-row attention,
-gather, scatter, guidance combine) captured once in a HIP graph and replayed: every replay must equal
-the eager run bit for bit.  Replays are interleaved with eager work and synchronisations, and every
-output is poisoned before each replay, so a replay that skipped or reordered a node would show."""
+"""The attention step's work after the elision verdict (PCSP aggregation, partition, dense and
+sensitive-row attention, gather, scatter, guidance combine) captured once in a HIP graph and replayed:
+every replay must equal the eager run bit for bit, both for the sequential capture and for the
+two-branch capture the benchmark replays (aggregation, partition and guidance on a second stream beside
+the dense attention, joined before the sensitive rows).  Replays are interleaved with eager work and
+synchronisations, and every output is poisoned before each replay, so a replay that skipped or reordered a
+node would show."""
 import numpy as np
 import pytest
 
@@ -11,7 +14,8 @@ from tests.gpu_util import torch
 pytestmark = pytest.mark.gpu
 
 
-def test_step_graph_replays_match_eager(lib):
+@pytest.mark.parametrize("branched", [False, True], ids=["sequential", "two-branch"])
+def test_step_graph_replays_match_eager(lib, branched):
     t = torch()
     w = syn.WORKLOADS["srsu_1024"]
     N, k, Tv = w.N, w.k, w.tv[0]
@@ -44,6 +48,25 @@ def test_step_graph_replays_match_eager(lib):
         lib.safe_scatter_rows(packed, S, state)
         lib.safe_swcfg_combine(eps, s01, w.side, w.g_ctx, w.g_sens, cfg)
 
+    branch = t.cuda.Stream()
+
+    def work_branched():
+        main = t.cuda.current_stream()
+        fork = t.cuda.Event()
+        fork.record(main)
+        lib.safe_attn_dense(q, ki, vi, kt, vt, w.tv, state)
+        branch.wait_event(fork)
+        with t.cuda.stream(branch):
+            lib.safe_pcsp_accumulate(xd, lid, Tv, 0, Tv, scores, False)
+            lib.safe_pcsp_partition(scores, k, S, C, isn, s01)
+            lib.safe_swcfg_combine(eps, s01, w.side, w.g_ctx, w.g_sens, cfg)
+            join = t.cuda.Event()
+            join.record(branch)
+        main.wait_event(join)
+        lib.safe_attn_rows(q, ki, vi, kt, vt, w.tv, S, state)
+        lib.safe_gather_rows(state, S, packed)
+        lib.safe_scatter_rows(packed, S, state)
+
     poison()
     work()
     t.cuda.synchronize()
@@ -53,7 +76,7 @@ def test_step_graph_replays_match_eager(lib):
     poison()
     t.cuda.synchronize()
     with t.cuda.graph(g):
-        work()
+        (work_branched if branched else work)()
     t.cuda.synchronize()
     for rep in range(4):
         poison()

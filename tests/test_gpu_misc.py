@@ -106,6 +106,40 @@ def test_mask_check_random_small(lib):
         assert ok2 == rok
 
 
+def test_mask_check_launch_matches_the_synchronous_verdict(lib):
+    """The launch-only form leaves in its device flag exactly the verdict (and per-row constants) the
+    synchronous form returns, also with other work queued on the stream behind it."""
+    t = torch()
+    r = np.random.default_rng(5)
+    N, T = 37, 9
+    for trial in range(24):
+        tv = tuple(int(x) for x in r.integers(0, T + 1, size=2))
+        cols = N if trial % 2 else N + T
+        if trial % 3 == 0:
+            m = r.random((1, 2, N, cols)) < 0.99
+        else:
+            m = np.broadcast_to(r.integers(-2, 3, size=(2, 1, N, 1)).astype(np.float32), (2, 1, N, cols)).copy()
+            if trial % 3 == 1:
+                m[tuple(int(r.integers(0, s)) for s in m.shape)] = 0.25
+        ok, c = _check(lib, m, N, T, tv)
+        flag = t.full((1,), 7, dtype=t.int32, device="cuda")
+        c2 = t.full((m.shape[0] * m.shape[1] * N,), 123.0, dtype=t.float32, device="cuda")
+        lib.safe_mask_check_launch(dev(m), N, T, tv, flag, c_out=c2)
+        t.cuda.synchronize()
+        assert int(host(flag)[0]) == (1 if ok else 0), trial
+        assert _same(host(c2).astype(np.float64), c), trial
+        flag.fill_(7)
+        lib.safe_mask_check_launch(dev(m), N, T, tv, flag)
+        t.cuda.synchronize()
+        assert int(host(flag)[0]) == (1 if ok else 0), trial
+    w = syn.WORKLOADS["dense_1024"]
+    big = dev(syn.mask_all_valid_bool(w.N, w.N))
+    flag = t.zeros(1, dtype=t.int32, device="cuda")
+    lib.safe_mask_check_launch(big, w.N, w.T, w.tv, flag)
+    t.cuda.synchronize()
+    assert int(host(flag)[0]) == 1
+
+
 def test_mask_check_dense_1024_all_valid(lib):
     w = syn.WORKLOADS["dense_1024"]
     m = syn.mask_all_valid_bool(w.N, w.N)
