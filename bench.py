@@ -10,9 +10,9 @@ H = 24, d = 64, N = 4096 image tokens, T = 256 text slots with 77 valid, |S| = 1
 Inputs are seeded synthetic tensors already resident in HBM.  The reported value is attention
 TFLOP/s over the whole step (dense + sensitive-row algorithmic flops, 4*rows*(N+Tv)*d per head,
 divided by the wall time of the whole step).  Each step's elision check runs on a side stream, launched
-two steps ahead (the mask is a step input; the host reads the verdict when it launches the step), and the rest of the step is replayed from a HIP graph in which PCSP aggregation, the partition
-and SW-CFG run on a branch beside the dense anchor attention (it does not depend on them); per-kernel
-durations come from HIP events in an eager pass of the same steps.
+two steps ahead (the mask is a step input; the host reads the verdict when it launches the step), and the
+rest of the step is replayed from a HIP graph of the stages in order; per-kernel durations come from HIP
+events in an eager pass of the same steps.
 
 Prints ONE JSON line.  --gpus above 1 exits with a message: this path runs on one GPU.
 """
@@ -108,12 +108,10 @@ def main():
         mark("swcfg_combine", lambda: dts.safe_swcfg_combine(eps, s01, w.side, w.g_ctx, w.g_sens, cfg_out))
 
     # Headline: the work of a step after the verdict is one HIP graph (captured once per verdict, outside
-    # the timed region) replayed after each step's check, which removes the per-kernel launch gaps. The
-    # graph has two branches: the dense anchor attention does not depend on the partition, so PCSP
-    # aggregation, the partition and SW-CFG (latency-bound kernels of a few workgroups' worth of work) run
-    # on a second stream beside it, in the CUs its last, half-full round of workgroups leaves free; the
-    # sensitive rows, gather and scatter wait for both branches (they read S and overwrite the rows of the
-    # state the anchor wrote).
+    # the timed region) replayed after each step's check, which removes the per-kernel launch gaps; its
+    # kernels run in stage order on one stream.  A second graph puts PCSP aggregation, the partition and
+    # SW-CFG on a branch beside the dense anchor attention (none of them reads the anchor's output; the
+    # sensitive rows, gather and scatter wait for both branches); it is timed as a side line.
     graphs = {}
     branch = torch.cuda.Stream(device=dev)
 
@@ -151,17 +149,21 @@ def main():
             verdicts[slot].copy_(flags[slot], non_blocking=True)
             checked[slot].record(side)
 
-    def graph_step():
+    def graph_step(overlapped=False):
         slot = step_no[0] % ring
         step_no[0] += 1
         checked[slot].synchronize()
         elided = bool(int(verdicts[slot][0]))
-        if elided not in graphs:
+        key = (elided, overlapped)
+        if key not in graphs:
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                work_overlapped(None if elided else mask)
-            graphs[elided] = g
-        graphs[elided].replay()
+                if overlapped:
+                    work_overlapped(None if elided else mask)
+                else:
+                    work(None if elided else mask, lambda name, fn: fn())
+            graphs[key] = g
+        graphs[key].replay()
         launch_check(slot)  # the check of the step `ring` steps ahead
 
     def eager_step(record: bool):
@@ -211,6 +213,16 @@ def main():
     elapsed = time.perf_counter() - t0
     ms_per_step = 1e3 * elapsed / args.steps
 
+    # The same steps from the two-branch graph.
+    for _ in range(min(args.warmup, 50)):
+        graph_step(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        graph_step(True)
+    torch.cuda.synchronize()
+    ms_per_step_branched = 1e3 * (time.perf_counter() - t0) / args.steps
+
     attn_flops = w.flops_dense + w.flops_rows
     value = attn_flops / (ms_per_step * 1e-3) / 1e12
 
@@ -237,6 +249,25 @@ def main():
         "stat": "median over the timed launches",
     }
 
+    # Cold mode: each HBM-bound stage of the step with L2 and MALL swept by a 1 GiB write before the launch
+    # (the step's own working set, tens of MB, otherwise stays in the 256 MB MALL from step to step).
+    flush = torch.empty(256 << 20, dtype=torch.float32, device=dev)
+    cold = {
+        "pcsp_accumulate": cold_line(hbm, pcsp_bytes, cold_launch_ms(
+            torch, lambda: dts.safe_pcsp_accumulate(xd, lid, Tv, 0, Tv, scores, False), flush)),
+        "gather_rows": cold_line(hbm, gs_bytes, cold_launch_ms(
+            torch, lambda: dts.safe_gather_rows(state, S, packed), flush)),
+        "scatter_rows": cold_line(hbm, gs_bytes, cold_launch_ms(
+            torch, lambda: dts.safe_scatter_rows(packed, S, state), flush)),
+        "swcfg_combine": cold_line(hbm, cfg_bytes, cold_launch_ms(
+            torch, lambda: dts.safe_swcfg_combine(eps, s01, w.side, w.g_ctx, w.g_sens, cfg_out), flush)),
+        "mask_scan": cold_line(hbm, mask_bytes, cold_launch_ms(
+            torch, lambda: dts.safe_mask_check_launch(mask, N, T, w.tv, flags[0]), flush)),
+        "note": "1024^2 step shapes; a 1 GiB write and a 1 GiB read sweep L2 and MALL before each launch; one event "
+                "pair per launch, the median of an empty pair after the same sweep subtracted (ms_raw, event_pair_ms)",
+    }
+    del flush
+
     sclk = profiled_traffic("sclk_mhz")
     peak_sclk = 256 * 4 * 1024 * sclk / 1e6 if sclk else None  # TFLOP/s
     result = {
@@ -249,8 +280,7 @@ def main():
         "ms_per_step": ms_per_step,
         "kernel_ms_sum": kernel_ms_sum,
         "timing": "wall clock of K whole steps (each step: its elision check, launched two steps ahead on a "
-                  "side stream, and a graph replay of the rest, PCSP, partition and SW-CFG on a branch beside the "
-                  "dense anchor attention); kernel "
+                  "side stream, and a graph replay of the rest, every stage in order on one stream); kernel "
                   "durations and the roofline from HIP events in an eager pass of the same steps, run "
                   "without overlap between steps, each step's launches queued behind a spin so that the "
                   "events time the kernels; kernel_ms_sum adds the main-stream kernels' medians",
@@ -271,6 +301,11 @@ def main():
                      "sclk_note": "shader clock during this kernel from the profile's GRBM_COUNT pass; "
                                   "peak_at_sclk = 256 CU x 4 SIMD x 1024 flop/clk x sclk"},
         "breakdown": breakdown,
+        "hbm_cold": cold,
+        "step_branched": {"ms_per_step": ms_per_step_branched,
+                          "value": attn_flops / (ms_per_step_branched * 1e-3) / 1e12,
+                          "note": "the same steps from a graph that runs PCSP, partition and SW-CFG on a branch beside "
+                                  "the dense anchor attention (the headline graph runs every stage in order)"},
     }
 
     # ---------------------------------------------------------------- the mask tax on this stack
@@ -290,40 +325,18 @@ def main():
     # ---------------------------------------------------------------- 2560^2 attention (same kernels)
     if not args.no_large:
         wl = syn.WORKLOADS["srsu_2560"]
-        g = torch.Generator(device=dev)
-        g.manual_seed(wl.seed)
-        mk = lambda n: (torch.randn((wl.B, wl.H, n, wl.d), generator=g, device=dev) * wl.std).to(torch.bfloat16)
-        lq, lki, lvi, lkt, lvt = mk(wl.N), mk(wl.N), mk(wl.N), mk(wl.T), mk(wl.T)
-        lrows = torch.from_numpy(syn.random_rows(wl)).to(dev)
-        lout = torch.zeros_like(lq)
-        timing = {}
-        for name, fn in (("dense", lambda: dts.safe_attn_dense(lq, lki, lvi, lkt, lvt, wl.tv, lout)),
-                         ("rows", lambda: dts.safe_attn_rows(lq, lki, lvi, lkt, lvt, wl.tv, lrows, lout))):
-            fn()
-            torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            reps = 5
-            e0.record(stream)
-            for _ in range(reps):
-                fn()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            timing[name] = e0.elapsed_time(e1) / reps
-        tfd = wl.flops_dense / (timing["dense"] * 1e-3) / 1e12
-        tfr = wl.flops_rows / (timing["rows"] * 1e-3) / 1e12
-        result["attention_2560"] = {"workload": "srsu_2560: B=2, H=24, d=64, N=25600, Tv=120, |S|=5120",
-                                    "dense_ms": timing["dense"], "dense_tflops": tfd,
-                                    "dense_frac_mfma": tfd / MFMA_BF16_PEAK_TFLOPS,
-                                    "rows_ms": timing["rows"], "rows_tflops": tfr,
-                                    "rows_frac_mfma": tfr / MFMA_BF16_PEAK_TFLOPS}
+        lq, lki, lvi, lkt, lvt, lrows, lout, line = attention_large(dts, torch, syn, dev, wl, stream)
+        result["attention_2560"] = line
         result["hbm_large"] = hbm_large(dts, torch, np, syn, dev, lout, lrows, hbm)
         lmask = torch.ones((1, 1, wl.N, wl.N), dtype=torch.bool, device=dev)  # 655 MB
         kept = time_launches(torch, lambda: dts.safe_attn_dense(lq, lki, lvi, lkt, lvt, wl.tv, lout, mask=lmask), reps=3)
-        tax["dense_2560_elided_ms"] = timing["dense"]
+        tax["dense_2560_elided_ms"] = line["dense_ms"]
         tax["dense_2560_kept_bool_ms"] = kept
-        tax["tax_2560_bool"] = kept / timing["dense"]
+        tax["tax_2560_bool"] = kept / line["dense_ms"]
         del lmask
-        del lq, lki, lvi, lkt, lvt, lout
+        del lq, lki, lvi, lkt, lvt, lout, lrows
+        result["attention_3072"] = attention_large(dts, torch, syn, dev, syn.WORKLOADS["traj_3072"], stream,
+                                                   reps=3)[-1]
 
     result["mask_tax"] = tax
 
@@ -360,6 +373,67 @@ def gpu_busy(torch, ms=1.0):
     torch.cuda._sleep(int(ms * _SLEEP_CYCLES_PER_MS[0]))
 
 
+def cold_launch_ms(torch, fn, flush, reps=10):
+    """Duration (ms) of one launch that finds none of its data in L2 or the 256 MB MALL: before each launch
+    a 1 GiB write and then a 1 GiB read sweep both caches (the read leaves them holding clean lines, so the
+    timed launch does not pay for writing back the sweep's dirty ones); a HIP event pair brackets the
+    launch alone.  The median of an event pair bracketing nothing after the same sweep (the event packets'
+    own cost, about 2-4 us) is subtracted.  Returns (corrected, raw, empty-pair) medians."""
+    import statistics
+    fn()
+    torch.cuda.synchronize()
+    raw, empty = [], []
+    for r in range(2 * reps):
+        flush.fill_(float(r))
+        flush.sum()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        if r % 2 == 0:
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        (raw if r % 2 == 0 else empty).append(e0.elapsed_time(e1))
+    raw_ms, empty_ms = statistics.median(raw), statistics.median(empty)
+    return max(raw_ms - empty_ms, 1e-6), raw_ms, empty_ms
+
+
+def cold_line(hbm, bytes_, timed):
+    ms, raw, empty = timed
+    line = hbm(bytes_, ms)
+    line.update({"ms_raw": raw, "event_pair_ms": empty})
+    return line
+
+
+def attention_large(dts, torch, syn, dev, wl, stream, reps=5):
+    """Dense and sensitive-row attention on a large workload (same kernels as the step): seeded
+    N(0,1)*std bf16 tensors drawn on the device, `reps` back-to-back launches between one event pair."""
+    g = torch.Generator(device=dev)
+    g.manual_seed(wl.seed)
+    mk = lambda n: (torch.randn((wl.B, wl.H, n, wl.d), generator=g, device=dev) * wl.std).to(torch.bfloat16)
+    q, ki, vi, kt, vt = mk(wl.N), mk(wl.N), mk(wl.N), mk(wl.T), mk(wl.T)
+    rows = torch.from_numpy(syn.random_rows(wl)).to(dev)
+    out = torch.zeros_like(q)
+    timing = {}
+    for name, fn in (("dense", lambda: dts.safe_attn_dense(q, ki, vi, kt, vt, wl.tv, out)),
+                     ("rows", lambda: dts.safe_attn_rows(q, ki, vi, kt, vt, wl.tv, rows, out))):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        timing[name] = e0.elapsed_time(e1) / reps
+    tfd = wl.flops_dense / (timing["dense"] * 1e-3) / 1e12
+    tfr = wl.flops_rows / (timing["rows"] * 1e-3) / 1e12
+    line = {"workload": f"{wl.name}: B={wl.B}, H={wl.H}, d={wl.d}, N={wl.N}, Tv={wl.tv[0]}, |S|={wl.k}",
+            "dense_ms": timing["dense"], "dense_tflops": tfd, "dense_frac_mfma": tfd / MFMA_BF16_PEAK_TFLOPS,
+            "rows_ms": timing["rows"], "rows_tflops": tfr, "rows_frac_mfma": tfr / MFMA_BF16_PEAK_TFLOPS,
+            "reps": reps}
+    return q, ki, vi, kt, vt, rows, out, line
+
+
 def time_launches(torch, fn, reps=20):
     """Average duration (ms) of `reps` back-to-back launches between one pair of HIP events, queued
     behind a spin so that they run back to back (one event pair per launch would add the dispatch of
@@ -389,7 +463,10 @@ def hbm_large(dts, torch, np, syn, dev, state, rows, hbm):
     sc = torch.empty(N, dtype=torch.float32, device=dev)
     out["pcsp_accumulate_2560"] = hbm(4.0 * H * N * Tv + 4.0 * H * N + 4.0 * N,
                                       time_launches(torch, lambda: dts.safe_pcsp_accumulate(x, li, Tv, 0, Tv, sc, False)))
-    del x, li
+    sweep = torch.empty(256 << 20, dtype=torch.float32, device=dev)  # 1 GiB
+    pcsp_cold = cold_line(hbm, 4.0 * H * N * Tv + 4.0 * H * N + 4.0 * N, cold_launch_ms(
+        torch, lambda: dts.safe_pcsp_accumulate(x, li, Tv, 0, Tv, sc, False), sweep))
+    del x, li, sweep
     S = torch.empty(wl.k, dtype=torch.int32, device=dev)
     C = torch.empty(N - wl.k, dtype=torch.int32, device=dev)
     isn = torch.empty(N, dtype=torch.uint8, device=dev)
@@ -410,6 +487,16 @@ def hbm_large(dts, torch, np, syn, dev, state, rows, hbm):
     src = torch.empty(256 << 20, dtype=torch.float32, device=dev).fill_(1.0)  # 1 GiB
     dst = torch.empty_like(src)
     out["torch_copy_1GiB"] = hbm(2.0 * src.numel() * 4, time_launches(torch, lambda: dst.copy_(src), reps=10))
+    # the same stages once more with L2 and MALL swept before each launch (dst is the sweep buffer)
+    out["cold"] = {
+        "pcsp_accumulate_2560": pcsp_cold,
+        "gather_rows_2560": cold_line(hbm, gs, cold_launch_ms(
+            torch, lambda: dts.safe_gather_rows(state, rows, packed), dst)),
+        "scatter_rows_2560": cold_line(hbm, gs, cold_launch_ms(
+            torch, lambda: dts.safe_scatter_rows(packed, rows, state), dst)),
+        "swcfg_combine_3072": cold_line(hbm, 3 * 4.0 * C5 * Hl * Wl + 4.0 * w5.N, cold_launch_ms(
+            torch, lambda: dts.safe_swcfg_combine(eps, s5, w5.side, w5.g_ctx, w5.g_sens, cout), dst)),
+    }
     out["note"] = ("shapes: PCSP x [24,25600,256] fp32 (Tv=120 valid), partition N=25600 k=5120, gather/scatter "
                    "[2,24,25600,64] bf16 k=5120, SW-CFG [2,16,384,384] fp32; torch_copy_1GiB is torch's device copy, a "
                    "reference point rather than the ceiling (a streaming copy with nontemporal loads and stores "

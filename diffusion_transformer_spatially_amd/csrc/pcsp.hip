@@ -47,7 +47,8 @@ __global__ __launch_bounds__(kPcspThreads) void k_pcsp_accumulate(const float* _
   extern __shared__ float part[];  // [kPcspRows][H]
   const int g = threadIdx.x >> 4;
   const int lane = threadIdx.x & 15;
-  const int i0 = blockIdx.x * kPcspRows;
+  // token blocks that share lse_img cache lines (32 tokens per 128-byte line) run on one XCD and its L2
+  const int i0 = static_cast<int>(xcd_remap(blockIdx.x, gridDim.x)) * kPcspRows;
   const int pairs = kPcspRows * H;
   for (int p = g; p < pairs; p += kPcspGroups) {
     const int r = p / H;
@@ -119,7 +120,8 @@ __global__ __launch_bounds__(kPcspThreads) void k_pcsp_accumulate_b(const float*
   extern __shared__ float part[];  // [kPcspRows][H]
   const int g = threadIdx.x >> 4;
   const int lane = threadIdx.x & 15;
-  const int i0 = blockIdx.x * kPcspRows;
+  // token blocks that share lse_img cache lines (32 tokens per 128-byte line) run on one XCD and its L2
+  const int i0 = static_cast<int>(xcd_remap(blockIdx.x, gridDim.x)) * kPcspRows;
   const int pairs = kPcspRows * H;
   for (int pb = g; pb < pairs; pb += kPcspGroups * JB) {
     float4 v[JB][TV4];

@@ -50,11 +50,12 @@ def test_swcfg_shapes_and_closed_forms(lib, C, Hl, Wl, side):
 
 
 # ------------------------------------------------------------------------------------ gather/scatter
+@pytest.mark.parametrize("d", [64, 24, 8])  # rows of 8 / 16 chunks (shift indexing), 3 / 6 chunks, 1 / 2 chunks
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("k", [0, 1, 77, 300])
-def test_gather_scatter_bitwise(lib, dtype, k):
+def test_gather_scatter_bitwise(lib, dtype, k, d):
     t = torch()
-    B, H, N, d = 2, 3, 300, 64
+    B, H, N = 2, 3, 300
     r = np.random.default_rng(k)
     tdt = t.bfloat16 if dtype == "bf16" else t.float32
     state = t.from_numpy(r.standard_normal((B, H, N, d)).astype(np.float32)).to(tdt).cuda()
