@@ -333,7 +333,25 @@ def main():
         tax["dense_2560_elided_ms"] = line["dense_ms"]
         tax["dense_2560_kept_bool_ms"] = kept
         tax["tax_2560_bool"] = kept / line["dense_ms"]
+        # the elision check itself on the 655 MB bool mask (verdict only, launch form, device flag)
+        lflag = torch.zeros(1, dtype=torch.int32, device=dev)
+        chk = {"bool_ms": time_launches(torch, lambda: dts.safe_mask_check_launch(lmask, wl.N, wl.T, wl.tv, lflag),
+                                        reps=5)}
         del lmask
+        lfmask = torch.zeros((1, 1, wl.N, wl.N), dtype=torch.float32, device=dev)  # 2.6 GB
+        chk["f32_ms"] = time_launches(torch, lambda: dts.safe_mask_check_launch(lfmask, wl.N, wl.T, wl.tv, lflag),
+                                      reps=5)
+        kept32 = time_launches(torch, lambda: dts.safe_attn_dense(lq, lki, lvi, lkt, lvt, wl.tv, lout, mask=lfmask),
+                               reps=2)
+        tax["dense_2560_kept_f32_ms"] = kept32
+        tax["tax_2560_f32"] = kept32 / line["dense_ms"]
+        del lfmask
+        nb = float(wl.N) * wl.N
+        chk.update({"bool_frac_hbm": nb / (chk["bool_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                    "f32_frac_hbm": 4 * nb / (chk["f32_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                    "workload": "srsu_2560 all-valid image mask [1,1,25600,25600]: 655 MB bool / 2.62 GB fp32 zeros; "
+                                "verdict-only scan, 5 back-to-back launches"})
+        result["mask_check_2560"] = chk
         del lq, lki, lvi, lkt, lvt, lout, lrows
         result["attention_3072"] = attention_large(dts, torch, syn, dev, syn.WORKLOADS["traj_3072"], stream,
                                                    reps=3)[-1]

@@ -20,7 +20,7 @@ import numpy as np
 # One independent stream per tensor role, spawned from the workload seed.
 _STREAMS = {
     "q": 0, "k_img": 1, "v_img": 2, "k_txt": 3, "v_txt": 4,
-    "x": 5, "blobs": 6, "eps": 7, "mask": 8, "state": 9, "scores": 10,
+    "x": 5, "blobs": 6, "eps": 7, "mask": 8, "state": 9, "scores": 10, "aes_sel": 11, "stepcache": 12,
 }
 
 
@@ -207,6 +207,28 @@ def mask_row_constant_f32(w: Workload, n_cols: int, lo: float = -5.0, hi: float 
     return np.broadcast_to(c[None, None, :, None], (1, 1, w.N, n_cols)).copy()
 
 
+def aesthetic_selection(w: Workload, count: int = 8) -> np.ndarray:
+    """u8 [T]: `count` distinct text slots among the first valid ones marked 1 (a stand-in for the
+    aesthetic prompt tokens a text-encoder match would pick)."""
+    tv = min(w.tv)
+    sel = np.zeros(w.T, dtype=np.uint8)
+    if tv > 0:
+        sel[rng_for(w.seed, "aes_sel").choice(tv, size=min(count, tv), replace=False)] = 1
+    return sel
+
+
+def stepcache_predictions(w: Workload, steps: int) -> np.ndarray:
+    """fp32 [steps, C, Hl, Wl]: a smooth per-pixel trajectory (a random start plus a random drift per step
+    and a small random curvature) standing in for a model's noise predictions across steps."""
+    C, Hl, Wl = w.latent
+    rng = rng_for(w.seed, "stepcache")
+    e0 = rng.standard_normal((C, Hl, Wl)).astype(np.float32)
+    d1 = (0.1 * rng.standard_normal((C, Hl, Wl))).astype(np.float32)
+    d2 = (0.01 * rng.standard_normal((C, Hl, Wl))).astype(np.float32)
+    s = np.arange(steps, dtype=np.float32)[:, None, None, None]
+    return (e0[None] + s * d1[None] + s * s * d2[None]).astype(np.float32)
+
+
 def sample_rows(n: int, count: int, seed: int) -> np.ndarray:
     """Ascending sample of query rows used when a full-size result is checked row by row."""
     rng = np.random.Generator(np.random.PCG64(seed))
@@ -214,7 +236,7 @@ def sample_rows(n: int, count: int, seed: int) -> np.ndarray:
 
 
 __all__ = [
-    "Workload", "WORKLOADS", "scaled", "rng_for", "f32_to_bf16_bits", "bf16_bits_to_f32", "round_to_bf16",
+    "Workload", "WORKLOADS", "scaled", "rng_for", "aesthetic_selection", "stepcache_predictions", "f32_to_bf16_bits", "bf16_bits_to_f32", "round_to_bf16",
     "attention_inputs", "blob_centres", "blob_bias", "pcsp_logits", "latent_eps", "initial_state",
     "random_rows", "mask_all_valid_bool", "mask_zeros_f32", "mask_row_constant_f32", "sample_rows",
 ]
