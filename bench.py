@@ -357,6 +357,7 @@ def main():
                                                    reps=3)[-1]
 
     result["mask_tax"] = tax
+    result["aesmask_stepcache"] = next_rows(dts, torch, np, syn, dev, hbm, not args.no_large)
 
     if args.copy_calibration:
         src = torch.empty(64 << 20, dtype=torch.float32, device=dev).fill_(1.0)
@@ -519,6 +520,49 @@ def hbm_large(dts, torch, np, syn, dev, state, rows, hbm):
                    "[2,24,25600,64] bf16 k=5120, SW-CFG [2,16,384,384] fp32; torch_copy_1GiB is torch's device copy, a "
                    "reference point rather than the ceiling (a streaming copy with nontemporal loads and stores "
                    "moves about 6.4 TB/s on this part)")
+    return out
+
+
+def next_rows(dts, torch, np, syn, dev, hbm, large: bool):
+    """AesMask (affinity over the selected aesthetic text slots -> percentile count -> top-k mask) and
+    StepCache (linear extrapolation of the prediction between full steps): warm and cold-cache timings."""
+    out = {}
+    sweep = torch.empty(256 << 20, dtype=torch.float32, device=dev)  # 1 GiB
+    for name in (("srsu_1024", "srsu_2560") if large else ("srsu_1024",)):
+        w = syn.WORKLOADS[name]
+        H, N, T, Tv = w.H, w.N, w.T, w.tv[0]
+        inp = syn.pcsp_logits(w, 0)
+        x, li = torch.from_numpy(inp["x"]).to(dev), torch.from_numpy(inp["lse_img"]).to(dev)
+        del inp
+        sel = torch.from_numpy(syn.aesthetic_selection(w)).to(dev)
+        sc = torch.empty(N, dtype=torch.float32, device=dev)
+        k = dts.safe_percentile_count(N, 8000)
+        S = torch.empty(k, dtype=torch.int32, device=dev)
+        C = torch.empty(N - k, dtype=torch.int32, device=dev)
+        isn = torch.empty(N, dtype=torch.uint8, device=dev)
+        nbytes = 4.0 * H * N * Tv + 4.0 * H * N + 4.0 * N
+        aff = lambda: dts.safe_affinity_accumulate(x, li, Tv, sel, sc, False)
+        line = {"affinity_warm": hbm(nbytes, time_launches(torch, aff)),
+                "affinity_cold": cold_line(hbm, nbytes, cold_launch_ms(torch, aff, sweep)),
+                "mask_ms": time_launches(torch, lambda: (aff(), dts.safe_pcsp_partition(sc, k, S, C, isn))),
+                "k": k,
+                "workload": f"{name}: x [{H},{N},{T}] fp32 (Tv={Tv}), 8 selected slots, 80th percentile (k={k})"}
+        out["aesmask_" + name.split("_")[1]] = line
+        del x, li
+    for name in (("srsu_1024", "traj_3072") if large else ("srsu_1024",)):
+        w = syn.WORKLOADS[name]
+        preds = torch.from_numpy(syn.stepcache_predictions(w, 2)).to(dev)
+        o = torch.empty_like(preds[0])
+        n = o.numel()
+        ex = lambda: dts.safe_stepcache_extrapolate(preds[0], preds[1], 1.0 / 3.0, o)
+        C_, Hl, Wl = w.latent
+        out["stepcache_" + name.split("_")[1]] = {
+            "warm": hbm(12.0 * n, time_launches(torch, ex)),
+            "cold": cold_line(hbm, 12.0 * n, cold_launch_ms(torch, ex, sweep)),
+            "workload": f"{name}: prediction [{C_},{Hl},{Wl}] fp32, w = 1/3"}
+    out["note"] = ("warm: 20 back-to-back launches between one event pair; cold: each launch after a 1 GiB write "
+                   "and a 1 GiB read, its own event pair minus an empty pair; mask_ms: affinity + partition")
+    del sweep
     return out
 
 

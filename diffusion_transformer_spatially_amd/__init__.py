@@ -16,9 +16,12 @@ LIB_PATH = os.path.join(_HERE, "libsafe_attn.so")
 
 SAFE_DTYPE_BF16, SAFE_DTYPE_F32, SAFE_DTYPE_BOOL = 0, 1, 2
 SAFE_MAX_BATCH = 64
+SAFE_STEP_DENSE, SAFE_STEP_ROWS = 0, 1
 EXPORTS = ("safe_attn_dense", "safe_attn_rows", "safe_mask_is_row_constant", "safe_mask_check_launch",
            "safe_pcsp_accumulate",
            "safe_pcsp_partition", "safe_swcfg_combine", "safe_gather_rows", "safe_scatter_rows",
+           "safe_affinity_accumulate", "safe_percentile_count", "safe_stepcache_extrapolate",
+           "safe_stepcache_plan", "safe_trajectory_plan",
            "safe_status_string", "safe_version")
 
 
@@ -68,6 +71,11 @@ def load(path: Optional[str] = None):
     lib.safe_swcfg_combine.argtypes = [vp, vp, i32, i32, i32, i32, f32, f32, vp, vp]
     lib.safe_gather_rows.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, vp, vp]
     lib.safe_scatter_rows.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, vp, vp]
+    lib.safe_affinity_accumulate.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, i32, vp]
+    lib.safe_percentile_count.argtypes = [i32, i32, P(i32)]
+    lib.safe_stepcache_extrapolate.argtypes = [vp, vp, ctypes.c_int64, f32, vp, vp]
+    lib.safe_stepcache_plan.argtypes = [i32, i32, P(i32), P(i32), P(f32)]
+    lib.safe_trajectory_plan.argtypes = [i32, i32, P(i32)]
     for name in EXPORTS[:-2]:
         getattr(lib, name).restype = i32
     lib.safe_status_string.argtypes = [i32]
@@ -234,6 +242,48 @@ def safe_scatter_rows(packed, rows, state, stream=None):
     _check(load().safe_scatter_rows(_ptr(packed), _ptr(rows), rows.numel(), B, H, N, d, _dtype_code(state),
                                     _ptr(state), _stream(stream)), "safe_scatter_rows")
     return state
+
+
+def safe_affinity_accumulate(x, lse_img, Tv: int, sel, scores, accumulate: bool, stream=None):
+    """scores (+)= per-token attention mass on the selected text slots, summed over heads
+    (safe_affinity_accumulate).  sel: device u8 [T]."""
+    H, N, T = x.shape
+    if sel.numel() != T:
+        raise ValueError("sel must have one entry per text slot")
+    _check(load().safe_affinity_accumulate(_ptr(x), _ptr(lse_img), H, N, T, Tv, _ptr(sel), _ptr(scores),
+                                           1 if accumulate else 0, _stream(stream)), "safe_affinity_accumulate")
+    return scores
+
+
+def safe_percentile_count(N: int, pct_bp: int) -> int:
+    """Tokens kept at the (pct_bp / 100)-th percentile (safe_percentile_count; host only)."""
+    k = ctypes.c_int32(0)
+    _check(load().safe_percentile_count(int(N), int(pct_bp), ctypes.byref(k)), "safe_percentile_count")
+    return int(k.value)
+
+
+def safe_stepcache_extrapolate(eps_a, eps_b, w: float, out, stream=None):
+    """out = eps_b + w (eps_b - eps_a), elementwise over fp32 tensors (safe_stepcache_extrapolate)."""
+    n = out.numel()
+    if eps_a.numel() != n or eps_b.numel() != n:
+        raise ValueError("eps_a, eps_b and out must have the same number of elements")
+    _check(load().safe_stepcache_extrapolate(_ptr(eps_a), _ptr(eps_b), n, float(w), _ptr(out), _stream(stream)),
+           "safe_stepcache_extrapolate")
+    return out
+
+
+def safe_stepcache_plan(steps: int, delta: int):
+    """[(full, src_a, src_b, w)] per step (safe_stepcache_plan; host only)."""
+    a, b, w = (ctypes.c_int32 * max(steps, 1))(), (ctypes.c_int32 * max(steps, 1))(), (ctypes.c_float * max(steps, 1))()
+    _check(load().safe_stepcache_plan(int(steps), int(delta), a, b, w), "safe_stepcache_plan")
+    return [(a[s] < 0, int(a[s]), int(b[s]), float(w[s])) for s in range(steps)]
+
+
+def safe_trajectory_plan(steps: int, anchor_every: int):
+    """Per step SAFE_STEP_DENSE or SAFE_STEP_ROWS (safe_trajectory_plan; host only)."""
+    k = (ctypes.c_int32 * max(steps, 1))()
+    _check(load().safe_trajectory_plan(int(steps), int(anchor_every), k), "safe_trajectory_plan")
+    return [int(k[t]) for t in range(steps)]
 
 
 def safe_version() -> int:

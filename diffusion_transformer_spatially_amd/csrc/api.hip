@@ -160,6 +160,65 @@ safe_status safe_pcsp_accumulate(const float* x, const float* lse_img, int32_t H
   return from_hip(launch_pcsp_accumulate(x, lse_img, H, N, T, Tv, c0, c1, scores, accumulate, stream));
 }
 
+safe_status safe_affinity_accumulate(const float* x, const float* lse_img, int32_t H, int32_t N, int32_t T,
+                                     int32_t Tv, const uint8_t* sel, float* scores, int32_t accumulate,
+                                     hipStream_t stream) {
+  if (x == nullptr || scores == nullptr || sel == nullptr) return SAFE_ERR_NULL;
+  if (H < 1 || N < 1 || T < 1) return SAFE_ERR_SHAPE;
+  if (Tv < 0 || Tv > T) return SAFE_ERR_RANGE;
+  if (static_cast<double>(H) * 4 > 48.0 * 1024) return SAFE_ERR_UNSUPPORTED;  // LDS per workgroup
+  if ((reinterpret_cast<uintptr_t>(x) & 3u) != 0) return SAFE_ERR_ALIGN;
+  return from_hip(launch_affinity_accumulate(x, lse_img, H, N, T, Tv, sel, scores, accumulate, stream));
+}
+
+safe_status safe_percentile_count(int32_t N, int32_t pct_bp, int32_t* k_out) {
+  if (k_out == nullptr) return SAFE_ERR_NULL;
+  if (N < 0) return SAFE_ERR_SHAPE;
+  if (pct_bp < 0 || pct_bp > 10000) return SAFE_ERR_RANGE;
+  if (N == 0) {
+    *k_out = 0;
+    return SAFE_OK;
+  }
+  const int64_t num = static_cast<int64_t>(pct_bp) * (N - 1);  // p (N - 1) / 100 = num / 10000, exactly
+  *k_out = static_cast<int32_t>(N - (num + 9999) / 10000);
+  return SAFE_OK;
+}
+
+safe_status safe_stepcache_extrapolate(const float* eps_a, const float* eps_b, int64_t n, float w, float* out,
+                                       hipStream_t stream) {
+  if (n < 0 || n >= (int64_t(1) << 40)) return SAFE_ERR_SHAPE;
+  if (n == 0) return SAFE_OK;
+  if (eps_a == nullptr || eps_b == nullptr || out == nullptr) return SAFE_ERR_NULL;
+  return from_hip(launch_stepcache(eps_a, eps_b, static_cast<size_t>(n), w, out, stream));
+}
+
+safe_status safe_stepcache_plan(int32_t steps, int32_t delta, int32_t* src_a, int32_t* src_b, float* w) {
+  if (steps < 0 || delta < 1) return SAFE_ERR_SHAPE;
+  if (steps > 0 && (src_a == nullptr || src_b == nullptr || w == nullptr)) return SAFE_ERR_NULL;
+  for (int32_t s = 0; s < steps; ++s) {
+    const int32_t b = delta * (s / delta);
+    if (s == b) {
+      src_a[s] = src_b[s] = -1;
+      w[s] = 0.f;
+    } else if (b == 0) {
+      src_a[s] = src_b[s] = 0;
+      w[s] = 0.f;
+    } else {
+      src_a[s] = b - delta;
+      src_b[s] = b;
+      w[s] = static_cast<float>(static_cast<double>(s - b) / delta);
+    }
+  }
+  return SAFE_OK;
+}
+
+safe_status safe_trajectory_plan(int32_t steps, int32_t anchor_every, int32_t* kinds) {
+  if (steps < 0 || anchor_every < 1) return SAFE_ERR_SHAPE;
+  if (steps > 0 && kinds == nullptr) return SAFE_ERR_NULL;
+  for (int32_t t = 0; t < steps; ++t) kinds[t] = (t % anchor_every == 0) ? SAFE_STEP_DENSE : SAFE_STEP_ROWS;
+  return SAFE_OK;
+}
+
 safe_status safe_pcsp_partition(const float* scores, int32_t N, int32_t k, int32_t* S, int32_t* C, uint8_t* is_sens,
                                 float* s01, hipStream_t stream) {
   if (scores == nullptr || is_sens == nullptr) return SAFE_ERR_NULL;
@@ -218,6 +277,6 @@ const char* safe_status_string(safe_status s) {
   }
 }
 
-int32_t safe_version(void) { return 100; }
+int32_t safe_version(void) { return 200; }
 
 }  // extern "C"

@@ -58,6 +58,9 @@ hipError_t launch_pcsp_partition(const float* scores, int N, int k, int32_t* S, 
                                  float* s01, hipStream_t s);
 hipError_t launch_swcfg(const float* eps, const float* sv, int C, int Hl, int Wl, int side, float g_ctx, float g_sens,
                         float* out, hipStream_t s);
+hipError_t launch_affinity_accumulate(const float* x, const float* lse_img, int H, int N, int T, int Tv,
+                                      const uint8_t* sel, float* scores, int accumulate, hipStream_t s);
+hipError_t launch_stepcache(const float* eps_a, const float* eps_b, size_t n, float w, float* out, hipStream_t s);
 hipError_t launch_rows_copy(const void* src, void* dst, const int32_t* rows, int k, int B, int H, int N,
                             int row_bytes, bool scatter, hipStream_t s);
 

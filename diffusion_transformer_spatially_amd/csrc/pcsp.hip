@@ -38,10 +38,13 @@ __device__ __forceinline__ float group16_sum(float v) {
   return v + dpp_mov<kDppMirror>(v);
 }
 
-template <bool VEC>
+// SEL: the content slots are the valid slots t with sel[t] != 0 (the AesMask affinity) instead of the
+// range [c0, c1) (the PCSP score).
+template <bool VEC, bool SEL>
 __global__ __launch_bounds__(kPcspThreads) void k_pcsp_accumulate(const float* __restrict__ x,
                                                                   const float* __restrict__ lse_img, int H, int N,
                                                                   int T, int Tv, int c0, int c1,
+                                                                  const uint8_t* __restrict__ sel,
                                                                   float* __restrict__ scores, int accumulate,
                                                                   int H_alloc) {
   extern __shared__ float part[];  // [kPcspRows][H]
@@ -88,9 +91,14 @@ __global__ __launch_bounds__(kPcspThreads) void k_pcsp_accumulate(const float* _
         const float hi = fmaxf(li, lse), lo = fminf(li, lse);
         lse = (hi == -INFINITY) ? -INFINITY : hi + log1pf(expf(lo - hi));
       }
-      // pass 2: mass on the content slots [c0, c1)
+      // pass 2: mass on the content slots
       float c = 0.f;
-      for (int t = c0 + lane; t < c1; t += 16) c += expf(row[t] - lse);
+      if (SEL) {
+        for (int t = lane; t < Tv; t += 16)
+          if (sel[t] != 0) c += expf(row[t] - lse);
+      } else {
+        for (int t = c0 + lane; t < c1; t += 16) c += expf(row[t] - lse);
+      }
       contrib = group16_sum(c);
     }
     if (lane == 0) part[r * H_alloc + h] = contrib;
@@ -111,15 +119,22 @@ __global__ __launch_bounds__(kPcspThreads) void k_pcsp_accumulate(const float* _
 // HBM latency is paid once per batch instead of once per row.  The loads are unconditional (addresses
 // of padded slots and of pairs past the end are clamped to valid memory and their values discarded
 // afterwards), so no load sits under divergent control flow and the waits stay exact.
-template <int TV4>
+template <int TV4, bool SEL>
 __global__ __launch_bounds__(kPcspThreads) void k_pcsp_accumulate_b(const float* __restrict__ x,
                                                                    const float* __restrict__ lse_img, int H, int N,
                                                                    int T, int Tv, int c0, int c1,
+                                                                   const uint8_t* __restrict__ sel,
                                                                    float* __restrict__ scores, int accumulate) {
   constexpr int JB = 3;
   extern __shared__ float part[];  // [kPcspRows][H]
   const int g = threadIdx.x >> 4;
   const int lane = threadIdx.x & 15;
+  // SEL: a lane's slots are the same in every row, so its selection bytes (4 per float4 of slots; the
+  // host passes sel 4-byte aligned with T a multiple of 4) are loaded once
+  uint32_t selw[TV4];
+#pragma unroll
+  for (int c = 0; c < TV4; ++c)
+    selw[c] = (SEL && lane * 4 + 64 * c < Tv) ? reinterpret_cast<const uint32_t*>(sel)[lane + 16 * c] : 0u;
   // token blocks that share lse_img cache lines (32 tokens per 128-byte line) run on one XCD and its L2
   const int i0 = static_cast<int>(xcd_remap(blockIdx.x, gridDim.x)) * kPcspRows;
   const int pairs = kPcspRows * H;
@@ -171,7 +186,8 @@ __global__ __launch_bounds__(kPcspThreads) void k_pcsp_accumulate_b(const float*
           const int t = lane * 4 + 64 * c + q;
           const float ev = __builtin_amdgcn_exp2f(fmaf(e[4 * c + q], kLog2e, -gml));
           sum += ev;
-          cs += (t >= c0 && t < c1) ? ev : 0.f;
+          const bool content = SEL ? ((selw[c] >> (8 * q)) & 0xffu) != 0u : (t >= c0 && t < c1);
+          cs += content ? ev : 0.f;
         }
       sum = group16_sum(sum);
       cs = group16_sum(cs);
@@ -192,23 +208,36 @@ __global__ __launch_bounds__(kPcspThreads) void k_pcsp_accumulate_b(const float*
   }
 }
 
-hipError_t launch_pcsp_accumulate(const float* x, const float* lse_img, int H, int N, int T, int Tv, int c0, int c1,
-                                  float* scores, int accumulate, hipStream_t s) {
+template <bool SEL>
+static void pcsp_launch(const float* x, const float* lse_img, int H, int N, int T, int Tv, int c0, int c1,
+                        const uint8_t* sel, float* scores, int accumulate, hipStream_t s) {
   const int blocks = (N + kPcspRows - 1) / kPcspRows;
   const size_t lds = sizeof(float) * kPcspRows * H;
-  const bool vec = (T % 4 == 0) && (reinterpret_cast<uintptr_t>(x) % 16 == 0);
+  const bool vec = (T % 4 == 0) && (reinterpret_cast<uintptr_t>(x) % 16 == 0) &&
+                   (!SEL || reinterpret_cast<uintptr_t>(sel) % 4 == 0);
   if (vec && Tv <= 256) {
     const int tv4 = Tv <= 64 ? 1 : Tv <= 128 ? 2 : Tv <= 192 ? 3 : 4;
     switch (tv4) {
-      case 1: k_pcsp_accumulate_b<1><<<blocks, kPcspThreads, lds, s>>>(x, lse_img, H, N, T, Tv, c0, c1, scores, accumulate); break;
-      case 2: k_pcsp_accumulate_b<2><<<blocks, kPcspThreads, lds, s>>>(x, lse_img, H, N, T, Tv, c0, c1, scores, accumulate); break;
-      case 3: k_pcsp_accumulate_b<3><<<blocks, kPcspThreads, lds, s>>>(x, lse_img, H, N, T, Tv, c0, c1, scores, accumulate); break;
-      default: k_pcsp_accumulate_b<4><<<blocks, kPcspThreads, lds, s>>>(x, lse_img, H, N, T, Tv, c0, c1, scores, accumulate); break;
+      case 1: k_pcsp_accumulate_b<1, SEL><<<blocks, kPcspThreads, lds, s>>>(x, lse_img, H, N, T, Tv, c0, c1, sel, scores, accumulate); break;
+      case 2: k_pcsp_accumulate_b<2, SEL><<<blocks, kPcspThreads, lds, s>>>(x, lse_img, H, N, T, Tv, c0, c1, sel, scores, accumulate); break;
+      case 3: k_pcsp_accumulate_b<3, SEL><<<blocks, kPcspThreads, lds, s>>>(x, lse_img, H, N, T, Tv, c0, c1, sel, scores, accumulate); break;
+      default: k_pcsp_accumulate_b<4, SEL><<<blocks, kPcspThreads, lds, s>>>(x, lse_img, H, N, T, Tv, c0, c1, sel, scores, accumulate); break;
     }
-  } else if (vec)
-    k_pcsp_accumulate<true><<<blocks, kPcspThreads, lds, s>>>(x, lse_img, H, N, T, Tv, c0, c1, scores, accumulate, H);
+  } else if (T % 4 == 0 && reinterpret_cast<uintptr_t>(x) % 16 == 0)
+    k_pcsp_accumulate<true, SEL><<<blocks, kPcspThreads, lds, s>>>(x, lse_img, H, N, T, Tv, c0, c1, sel, scores, accumulate, H);
   else
-    k_pcsp_accumulate<false><<<blocks, kPcspThreads, lds, s>>>(x, lse_img, H, N, T, Tv, c0, c1, scores, accumulate, H);
+    k_pcsp_accumulate<false, SEL><<<blocks, kPcspThreads, lds, s>>>(x, lse_img, H, N, T, Tv, c0, c1, sel, scores, accumulate, H);
+}
+
+hipError_t launch_pcsp_accumulate(const float* x, const float* lse_img, int H, int N, int T, int Tv, int c0, int c1,
+                                  float* scores, int accumulate, hipStream_t s) {
+  pcsp_launch<false>(x, lse_img, H, N, T, Tv, c0, c1, nullptr, scores, accumulate, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_affinity_accumulate(const float* x, const float* lse_img, int H, int N, int T, int Tv,
+                                      const uint8_t* sel, float* scores, int accumulate, hipStream_t s) {
+  pcsp_launch<true>(x, lse_img, H, N, T, Tv, 0, 0, sel, scores, accumulate, s);
   return hipGetLastError();
 }
 

@@ -191,6 +191,57 @@ safe_status safe_gather_rows(const void* state, const int32_t* rows, int32_t k, 
 safe_status safe_scatter_rows(const void* packed, const int32_t* rows, int32_t k, int32_t B, int32_t H, int32_t N,
                               int32_t d, int32_t dtype, void* state, hipStream_t stream);
 
+/*
+ * AesMask affinity (AccelAes summary, 2. Methodology B.1: the attention between chosen aesthetic prompt
+ * tokens and the image tokens, aggregated into an affinity map).  The PCSP quantity above with the
+ * content set given by a selection of text slots instead of a range:
+ *   a_i = sum_h sum_{t < Tv, sel[t] != 0} exp(x[h,i,t] - LSE),   LSE as for safe_pcsp_accumulate,
+ * scores[i] = (accumulate ? scores[i] : 0) + a_i.  sel: device u8 [T] (which slots are aesthetic tokens
+ * is the caller's choice); other arguments, layouts and errors as safe_pcsp_accumulate.  The binary
+ * mask of the method is then safe_pcsp_partition with k from safe_percentile_count (is_sens = mask).
+ */
+safe_status safe_affinity_accumulate(const float* x, const float* lse_img, int32_t H, int32_t N, int32_t T,
+                                     int32_t Tv, const uint8_t* sel, float* scores, int32_t accumulate,
+                                     hipStream_t stream);
+
+/*
+ * Token count of a percentile threshold (AccelAes summary, Methodology B.1: the mask keeps the tokens
+ * above a percentile of the affinity map).  *k_out = N - ceil(p (N - 1) / 100) with p = pct_bp / 100
+ * (pct_bp in hundredths of a percent, 0..10000): for distinct scores, the number of tokens at or above
+ * numpy's linearly interpolated p-th percentile.  Host only; no GPU work.  N >= 0; SAFE_ERR_RANGE for
+ * pct_bp outside [0, 10000]; SAFE_ERR_NULL for k_out == NULL.
+ */
+safe_status safe_percentile_count(int32_t N, int32_t pct_bp, int32_t* k_out);
+
+/*
+ * StepCache extrapolation (AccelAes summary, 2. Methodology B.3: full model runs at a step interval,
+ * linear extrapolation of the noise prediction in between):
+ *   out[i] = eps_b[i] + w * (eps_b[i] - eps_a[i]),   i < n,
+ * eps_a the older and eps_b the newer full prediction, w the step offset past eps_b in units of the
+ * interval (safe_stepcache_plan gives it).  Device fp32 arrays of n elements, any layout; out may alias
+ * eps_a or eps_b element for element.  n >= 0 (0: nothing is launched), n < 2^40.
+ */
+safe_status safe_stepcache_extrapolate(const float* eps_a, const float* eps_b, int64_t n, float w, float* out,
+                                       hipStream_t stream);
+
+/*
+ * StepCache plan (AccelAes summary, Methodology B.3).  Host only.  For step s < steps: s % delta == 0
+ * is a full step (src_a[s] = src_b[s] = -1, w[s] = 0); otherwise, with b = delta * (s / delta),
+ * src_b[s] = b and, when b > 0, src_a[s] = b - delta and w[s] = (s - b) / delta (the line through the
+ * last two full predictions), or, before the second full step, src_a[s] = b = 0 and w[s] = 0 (the one
+ * full prediction reused).  Host arrays of `steps` entries; steps >= 0, delta >= 1.
+ */
+safe_status safe_stepcache_plan(int32_t steps, int32_t delta, int32_t* src_a, int32_t* src_b, float* w);
+
+/*
+ * Trajectory plan (SAFE-DiT summary, Methodology 2-3: after the warmup aggregation and the fixed
+ * partition, periodic dense anchor refreshes and sensitive-row updates in between).  Host only.
+ * kinds[t] = SAFE_STEP_DENSE when t % anchor_every == 0, else SAFE_STEP_ROWS, for t < steps (the warmup
+ * steps come before step 0).  kinds: host int32 [steps]; steps >= 0, anchor_every >= 1.
+ */
+enum { SAFE_STEP_DENSE = 0, SAFE_STEP_ROWS = 1 };
+safe_status safe_trajectory_plan(int32_t steps, int32_t anchor_every, int32_t* kinds);
+
 /* Human-readable name of a status code (static storage). */
 const char* safe_status_string(safe_status s);
 /* Library version: major*10000 + minor*100 + patch. */

@@ -28,7 +28,7 @@ def test_library_loads_and_exports_every_symbol():
     lib = dts.load()
     for name in _declared():
         assert hasattr(lib, name), name
-    assert lib.safe_version() == 100
+    assert lib.safe_version() == 200
     for code, name in [(0, b"SAFE_OK"), (2, b"SAFE_ERR_SHAPE"), (8, b"SAFE_ERR_ALIGN"), (99, b"SAFE_ERR_UNKNOWN")]:
         assert lib.safe_status_string(code) == name
 
@@ -149,3 +149,59 @@ def test_gpu_errors_leave_outputs_untouched(lib):
     assert e.value.name == "SAFE_ERR_UNSUPPORTED"
     torch.cuda.synchronize()
     assert torch.all(out == 3.0).item()
+
+
+def test_aesmask_and_stepcache_validation():
+    _cpu_only()
+    lib = dts.load()
+    f = 0x10000
+    aff = lib.safe_affinity_accumulate
+    assert aff(None, None, 2, 8, 16, 4, f, f, 0, None) == NULL
+    assert aff(f, None, 2, 8, 16, 4, None, f, 0, None) == NULL
+    assert aff(f, None, 2, 8, 16, 4, f, None, 0, None) == NULL
+    assert aff(f, None, 2, 8, 16, 17, f, f, 0, None) == RANGE
+    assert aff(f, None, 2, 8, 16, -1, f, f, 0, None) == RANGE
+    assert aff(f, None, 0, 8, 16, 4, f, f, 0, None) == SHAPE
+    assert aff(f + 2, None, 2, 8, 16, 4, f, f, 0, None) == ALIGN
+    ex = lib.safe_stepcache_extrapolate
+    assert ex(None, f, 10, ctypes.c_float(0.5), f, None) == NULL
+    assert ex(f, f, 10, ctypes.c_float(0.5), None, None) == NULL
+    assert ex(f, f, -1, ctypes.c_float(0.5), f, None) == SHAPE
+    assert ex(f, f, 1 << 40, ctypes.c_float(0.5), f, None) == SHAPE
+    assert ex(None, None, 0, ctypes.c_float(0.5), None, None) == OK  # n = 0: nothing to do
+
+
+def test_host_plans_and_percentile_count_match_the_oracle():
+    """Host-only entry points (no GPU work): the library's trajectory and StepCache plans and its
+    percentile count against the oracle's."""
+    from oracle import aesmask as OA
+    from oracle import schedule as OS
+    from oracle import stepcache as OSC
+    for steps in (0, 1, 5, 10, 37):
+        for every in (1, 2, 4, 7, 50):
+            got = dts.safe_trajectory_plan(steps, every)
+            want = [dts.SAFE_STEP_DENSE if k == "dense" else dts.SAFE_STEP_ROWS for k in OS.plan(steps, every)]
+            assert got == want
+            got = dts.safe_stepcache_plan(steps, every)
+            ref = OSC.plan(steps, every)
+            assert [g[:3] for g in got] == [r[:3] for r in ref]
+            assert [g[3] for g in got] == [float(np.float32(r[3])) for r in ref]
+    for N in (0, 1, 2, 5, 97, 4096, 25600, 36864):
+        for bp in (0, 1, 2500, 3333, 5000, 8000, 9999, 10000):
+            assert dts.safe_percentile_count(N, bp) == OA.percentile_count(N, bp)
+    lib = dts.load()
+    k = ctypes.c_int32(-5)
+    assert lib.safe_percentile_count(10, -1, ctypes.byref(k)) == RANGE
+    assert lib.safe_percentile_count(10, 10001, ctypes.byref(k)) == RANGE
+    assert lib.safe_percentile_count(-1, 5000, ctypes.byref(k)) == SHAPE
+    assert lib.safe_percentile_count(10, 5000, None) == NULL
+    assert k.value == -5
+    arr = (ctypes.c_int32 * 4)()
+    warr = (ctypes.c_float * 4)()
+    assert lib.safe_trajectory_plan(4, 0, arr) == SHAPE
+    assert lib.safe_trajectory_plan(-1, 4, arr) == SHAPE
+    assert lib.safe_trajectory_plan(4, 4, None) == NULL
+    assert lib.safe_trajectory_plan(0, 4, None) == OK
+    assert lib.safe_stepcache_plan(4, 0, arr, arr, warr) == SHAPE
+    assert lib.safe_stepcache_plan(4, 2, None, arr, warr) == NULL
+    assert lib.safe_stepcache_plan(0, 2, None, None, None) == OK

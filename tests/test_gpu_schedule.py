@@ -20,9 +20,10 @@ def _gpu_trajectory(lib, w, step_inputs, warm, state0):
     lib.safe_pcsp_partition(sc, w.k, S, C, isn)
     state = t.from_numpy(state0).to(t.bfloat16).cuda()
     snaps = []
-    for step, kind in enumerate(OS.plan(w.steps, w.anchor_every)):
+    # the library's own plan (checked against the oracle's on the CPU) orders the launches
+    for step, kind in enumerate(lib.safe_trajectory_plan(w.steps, w.anchor_every)):
         q, ki, vi, kt, vt = step_inputs(step)
-        if kind == "dense":
+        if kind == lib.SAFE_STEP_DENSE:
             lib.safe_attn_dense(q, ki, vi, kt, vt, w.tv, state)
         else:
             lib.safe_attn_rows(q, ki, vi, kt, vt, w.tv, S, state)
