@@ -21,6 +21,7 @@ import numpy as np
 _STREAMS = {
     "q": 0, "k_img": 1, "v_img": 2, "k_txt": 3, "v_txt": 4,
     "x": 5, "blobs": 6, "eps": 7, "mask": 8, "state": 9, "scores": 10, "aes_sel": 11, "stepcache": 12,
+    "hidden": 13, "w_ffn1": 14, "w_ffn2": 15, "w_qkv": 16, "cache": 17,
 }
 
 
@@ -229,6 +230,24 @@ def stepcache_predictions(w: Workload, steps: int) -> np.ndarray:
     return (e0[None] + s * d1[None] + s * s * d2[None]).astype(np.float32)
 
 
+def hidden_states(w: Workload) -> np.ndarray:
+    """bf16-representable fp32 [B, N, D] token-major hidden states, N(0,1), D = H * d."""
+    return round_to_bf16(rng_for(w.seed, "hidden").standard_normal((w.B, w.N, w.H * w.d), dtype=np.float32))
+
+
+def block_weights(w: Workload, ffn_mult: int = 4) -> Dict[str, np.ndarray]:
+    """Random-init linear layers of one block in nn.Linear layout [out, in] (bf16-representable fp32,
+    N(0, 1/in) weights, N(0, 0.02^2) biases): w1/b1 D->F, w2/b2 F->D, wqkv/bqkv D->3D; F = ffn_mult * D."""
+    D = w.H * w.d
+    F = ffn_mult * D
+    out = {}
+    for role, name, o, i in (("w_ffn1", "1", F, D), ("w_ffn2", "2", D, F), ("w_qkv", "qkv", 3 * D, D)):
+        rng = rng_for(w.seed, role)
+        out["w" + name] = round_to_bf16((rng.standard_normal((o, i), dtype=np.float32) / np.sqrt(i)).astype(np.float32))
+        out["b" + name] = (0.02 * rng.standard_normal(o)).astype(np.float32)
+    return out
+
+
 def sample_rows(n: int, count: int, seed: int) -> np.ndarray:
     """Ascending sample of query rows used when a full-size result is checked row by row."""
     rng = np.random.Generator(np.random.PCG64(seed))
@@ -236,7 +255,7 @@ def sample_rows(n: int, count: int, seed: int) -> np.ndarray:
 
 
 __all__ = [
-    "Workload", "WORKLOADS", "scaled", "rng_for", "aesthetic_selection", "stepcache_predictions", "f32_to_bf16_bits", "bf16_bits_to_f32", "round_to_bf16",
+    "Workload", "WORKLOADS", "scaled", "rng_for", "aesthetic_selection", "stepcache_predictions", "hidden_states", "block_weights", "f32_to_bf16_bits", "bf16_bits_to_f32", "round_to_bf16",
     "attention_inputs", "blob_centres", "blob_bias", "pcsp_logits", "latent_eps", "initial_state",
     "random_rows", "mask_all_valid_bool", "mask_zeros_f32", "mask_row_constant_f32", "sample_rows",
 ]
