@@ -358,6 +358,7 @@ def main():
 
     result["mask_tax"] = tax
     result["aesmask_stepcache"] = next_rows(dts, torch, np, syn, dev, hbm, not args.no_large)
+    result["srsu_block"] = srsu_block(dts, torch, np, syn, dev)
 
     if args.copy_calibration:
         src = torch.empty(64 << 20, dtype=torch.float32, device=dev).fill_(1.0)
@@ -564,6 +565,32 @@ def next_rows(dts, torch, np, syn, dev, hbm, large: bool):
                    "and a 1 GiB read, its own event pair minus an empty pair; mask_ms: affinity + partition")
     del sweep
     return out
+
+
+def srsu_block(dts, torch, np, syn, dev):
+    """The rest of a sensitive-row update on the 1024^2 shapes (B = 2, N = 4096, D = 1536, F = 6144, |S| = 1229):
+    the FFN of the S rows into the cache (two products) and the QKV projection into the attention tensors."""
+    w = syn.WORKLOADS["srsu_1024"]
+    bf = lambda a: torch.from_numpy(syn.f32_to_bf16_bits(a).view(np.int16)).view(torch.bfloat16).to(dev)
+    x = bf(syn.hidden_states(w))
+    bw = syn.block_weights(w)
+    w1, w2, wq = bf(bw["w1"]), bf(bw["w2"]), bf(bw["wqkv"])
+    b1, b2, bq = (torch.from_numpy(bw[n]).to(dev) for n in ("b1", "b2", "bqkv"))
+    rows = torch.from_numpy(syn.random_rows(w)).to(dev)
+    D, F, T = w.H * w.d, bw["w1"].shape[0], w.B * w.k
+    cache = torch.zeros_like(x)
+    ws = torch.empty(dts.safe_rows_ffn_workspace_bytes(w.B, w.k, F) // 2, dtype=torch.bfloat16, device=dev)
+    q = torch.zeros((w.B, w.H, w.N, w.d), dtype=torch.bfloat16, device=dev)
+    kc, vc = torch.zeros_like(q), torch.zeros_like(q)
+    ffn_ms = time_launches(torch, lambda: dts.safe_rows_ffn(x, rows, w1, b1, w2, b2, cache, ws))
+    qkv_ms = time_launches(torch, lambda: dts.safe_rows_qkv(x, rows, wq, bq, q, kc, vc))
+    ffn_fl, qkv_fl = 4.0 * T * D * F, 2.0 * T * D * 3 * D
+    return {"ffn": {"ms": ffn_ms, "tflops": ffn_fl / (ffn_ms * 1e-3) / 1e12,
+                    "frac_mfma": ffn_fl / (ffn_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, "flops": ffn_fl},
+            "qkv": {"ms": qkv_ms, "tflops": qkv_fl / (qkv_ms * 1e-3) / 1e12,
+                    "frac_mfma": qkv_fl / (qkv_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, "flops": qkv_fl},
+            "workload": f"srsu_1024: x [2,4096,{D}] bf16, |S|={w.k} rows per batch entry (T={T} tokens), F={F}; "
+                        "FFN = gathered D->F + GELU, then F->D scattered into the cache; QKV D->3D into [B,H,N,d]"}
 
 
 def cpu_other_stages(w, x, syn):

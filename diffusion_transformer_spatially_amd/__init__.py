@@ -21,7 +21,8 @@ EXPORTS = ("safe_attn_dense", "safe_attn_rows", "safe_mask_is_row_constant", "sa
            "safe_pcsp_accumulate",
            "safe_pcsp_partition", "safe_swcfg_combine", "safe_gather_rows", "safe_scatter_rows",
            "safe_affinity_accumulate", "safe_percentile_count", "safe_stepcache_extrapolate",
-           "safe_stepcache_plan", "safe_trajectory_plan",
+           "safe_stepcache_plan", "safe_trajectory_plan", "safe_rows_ffn", "safe_rows_ffn_workspace_bytes",
+           "safe_rows_qkv",
            "safe_status_string", "safe_version")
 
 
@@ -76,8 +77,12 @@ def load(path: Optional[str] = None):
     lib.safe_stepcache_extrapolate.argtypes = [vp, vp, ctypes.c_int64, f32, vp, vp]
     lib.safe_stepcache_plan.argtypes = [i32, i32, P(i32), P(i32), P(f32)]
     lib.safe_trajectory_plan.argtypes = [i32, i32, P(i32)]
+    lib.safe_rows_ffn.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.safe_rows_ffn_workspace_bytes.argtypes = [i32, i32, i32]
+    lib.safe_rows_qkv.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp]
     for name in EXPORTS[:-2]:
         getattr(lib, name).restype = i32
+    lib.safe_rows_ffn_workspace_bytes.restype = ctypes.c_size_t
     lib.safe_status_string.argtypes = [i32]
     lib.safe_status_string.restype = ctypes.c_char_p
     lib.safe_version.argtypes = []
@@ -284,6 +289,30 @@ def safe_trajectory_plan(steps: int, anchor_every: int):
     k = (ctypes.c_int32 * max(steps, 1))()
     _check(load().safe_trajectory_plan(int(steps), int(anchor_every), k), "safe_trajectory_plan")
     return [int(k[t]) for t in range(steps)]
+
+
+def safe_rows_ffn_workspace_bytes(B: int, k: int, F: int) -> int:
+    return int(load().safe_rows_ffn_workspace_bytes(int(B), int(k), int(F)))
+
+
+def safe_rows_ffn(x, rows, w1, b1, w2, b2, cache, ws, stream=None):
+    """cache[:, rows] = FFN(x[:, rows]) (safe_rows_ffn).  x, cache: bf16 [B, N, D]; w1 [F, D], w2 [D, F]
+    bf16; b1 / b2 fp32 or None; ws: device workspace tensor of at least safe_rows_ffn_workspace_bytes."""
+    B, N, D = x.shape
+    F = w1.shape[0]
+    _check(load().safe_rows_ffn(_ptr(x), _ptr(rows), rows.numel(), B, N, D, F, _ptr(w1), _ptr(b1), _ptr(w2),
+                                _ptr(b2), _ptr(cache), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "safe_rows_ffn")
+    return cache
+
+
+def safe_rows_qkv(x, rows, wqkv, bqkv, q, k_cache, v_cache, stream=None):
+    """Rows S of q / k_cache / v_cache [B, H, N, d] from the projection of x[:, rows] (safe_rows_qkv)."""
+    B, N, _ = x.shape
+    _, H, _, d = q.shape
+    _check(load().safe_rows_qkv(_ptr(x), _ptr(rows), rows.numel(), B, N, H, d, _ptr(wqkv), _ptr(bqkv), _ptr(q),
+                                _ptr(k_cache), _ptr(v_cache), _stream(stream)), "safe_rows_qkv")
+    return q, k_cache, v_cache
 
 
 def safe_version() -> int:

@@ -219,6 +219,50 @@ safe_status safe_trajectory_plan(int32_t steps, int32_t anchor_every, int32_t* k
   return SAFE_OK;
 }
 
+
+size_t safe_rows_ffn_workspace_bytes(int32_t B, int32_t k, int32_t F) {
+  if (B < 0 || k < 0 || F < 0) return 0;
+  return static_cast<size_t>(B) * static_cast<size_t>(k) * static_cast<size_t>(F) * 2;
+}
+
+safe_status safe_rows_ffn(const void* x, const int32_t* rows, int32_t k, int32_t B, int32_t N, int32_t D, int32_t F,
+                          const void* w1, const float* b1, const void* w2, const float* b2, void* cache, void* ws,
+                          size_t ws_bytes, hipStream_t stream) {
+  if (B < 1 || N < 1 || D < 1 || F < 1) return SAFE_ERR_SHAPE;
+  if (k < 0 || k > N) return SAFE_ERR_RANGE;
+  if (k == 0) return SAFE_OK;
+  if (x == nullptr || rows == nullptr || w1 == nullptr || w2 == nullptr || cache == nullptr || ws == nullptr)
+    return SAFE_ERR_NULL;
+  if (D % 128 != 0 || F % 128 != 0) return SAFE_ERR_UNSUPPORTED;
+  if (static_cast<double>(B) * N * D > 2.0e9 || static_cast<double>(B) * k * F > 2.0e9) return SAFE_ERR_SHAPE;
+  if (ws_bytes < safe_rows_ffn_workspace_bytes(B, k, F)) return SAFE_ERR_WORKSPACE;
+  if (!aligned16(x) || !aligned16(w1) || !aligned16(w2) || !aligned16(cache) || !aligned16(ws) ||
+      (b1 != nullptr && !aligned16(b1)) || (b2 != nullptr && !aligned16(b2)))
+    return SAFE_ERR_ALIGN;
+  return from_hip(launch_rows_ffn(static_cast<const uint16_t*>(x), rows, k, B, N, D, F,
+                                  static_cast<const uint16_t*>(w1), b1, static_cast<const uint16_t*>(w2), b2,
+                                  static_cast<uint16_t*>(cache), static_cast<uint16_t*>(ws), stream));
+}
+
+safe_status safe_rows_qkv(const void* x, const int32_t* rows, int32_t k, int32_t B, int32_t N, int32_t H, int32_t d,
+                          const void* wqkv, const float* bqkv, void* q, void* k_cache, void* v_cache,
+                          hipStream_t stream) {
+  if (B < 1 || N < 1 || H < 1 || d < 1) return SAFE_ERR_SHAPE;
+  if (k < 0 || k > N) return SAFE_ERR_RANGE;
+  if (k == 0) return SAFE_OK;
+  if (x == nullptr || rows == nullptr || wqkv == nullptr || q == nullptr || k_cache == nullptr || v_cache == nullptr)
+    return SAFE_ERR_NULL;
+  const int64_t D = static_cast<int64_t>(H) * d;
+  if (D % 128 != 0 || d % 16 != 0) return SAFE_ERR_UNSUPPORTED;
+  if (static_cast<double>(B) * N * D > 2.0e9) return SAFE_ERR_SHAPE;
+  if (!aligned16(x) || !aligned16(wqkv) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) ||
+      (bqkv != nullptr && !aligned16(bqkv)))
+    return SAFE_ERR_ALIGN;
+  return from_hip(launch_rows_qkv(static_cast<const uint16_t*>(x), rows, k, B, N, H, d,
+                                  static_cast<const uint16_t*>(wqkv), bqkv, static_cast<uint16_t*>(q),
+                                  static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache), stream));
+}
+
 safe_status safe_pcsp_partition(const float* scores, int32_t N, int32_t k, int32_t* S, int32_t* C, uint8_t* is_sens,
                                 float* s01, hipStream_t stream) {
   if (scores == nullptr || is_sens == nullptr) return SAFE_ERR_NULL;

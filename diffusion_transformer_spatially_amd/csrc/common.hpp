@@ -61,6 +61,12 @@ hipError_t launch_swcfg(const float* eps, const float* sv, int C, int Hl, int Wl
 hipError_t launch_affinity_accumulate(const float* x, const float* lse_img, int H, int N, int T, int Tv,
                                       const uint8_t* sel, float* scores, int accumulate, hipStream_t s);
 hipError_t launch_stepcache(const float* eps_a, const float* eps_b, size_t n, float w, float* out, hipStream_t s);
+hipError_t launch_rows_ffn(const uint16_t* x, const int32_t* rows, int k, int B, int N, int D, int F,
+                           const uint16_t* w1, const float* b1, const uint16_t* w2, const float* b2, uint16_t* cache,
+                           uint16_t* hidden, hipStream_t s);
+hipError_t launch_rows_qkv(const uint16_t* x, const int32_t* rows, int k, int B, int N, int H, int d,
+                           const uint16_t* wqkv, const float* bqkv, uint16_t* q, uint16_t* kc, uint16_t* vc,
+                           hipStream_t s);
 hipError_t launch_rows_copy(const void* src, void* dst, const int32_t* rows, int k, int B, int H, int N,
                             int row_bytes, bool scatter, hipStream_t s);
 

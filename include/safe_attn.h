@@ -242,6 +242,35 @@ safe_status safe_stepcache_plan(int32_t steps, int32_t delta, int32_t* src_a, in
 enum { SAFE_STEP_DENSE = 0, SAFE_STEP_ROWS = 1 };
 safe_status safe_trajectory_plan(int32_t steps, int32_t anchor_every, int32_t* kinds);
 
+/*
+ * Sensitive-row FFN with the context rows cached (SAFE-DiT summary, Methodology 3: only the rows of S
+ * are recomputed in a non-anchor step; AccelAes summary, Methodology B.2 SkipSparse: the FFN of the
+ * background tokens is skipped and its cached output reused).  For every batch entry b and r < k:
+ *   cache[b, rows[r], :] = gelu_tanh(x[b, rows[r], :] W1^T + b1) W2^T + b2,
+ * other rows of cache untouched.  x: device bf16 [B, N, D] hidden states; W1: bf16 [F, D]; W2: bf16
+ * [D, F] (nn.Linear layout [out, in]); b1: fp32 [F] or NULL; b2: fp32 [D] or NULL; cache: bf16 [B, N, D]
+ * (may be x itself only if no later row reads a row already written: pass a separate buffer);
+ * rows: device int32 [k] in [0, N) (entries outside are skipped); ws: device workspace of at least
+ * safe_rows_ffn_workspace_bytes(B, k, F) bytes (the bf16 hidden activation of the k rows).
+ * D and F multiples of 128; x, W1, W2, cache, ws 16-byte aligned, b1 / b2 16-byte aligned.  k = 0: no-op.
+ */
+safe_status safe_rows_ffn(const void* x, const int32_t* rows, int32_t k, int32_t B, int32_t N, int32_t D, int32_t F,
+                          const void* w1, const float* b1, const void* w2, const float* b2, void* cache, void* ws,
+                          size_t ws_bytes, hipStream_t stream);
+size_t safe_rows_ffn_workspace_bytes(int32_t B, int32_t k, int32_t F);
+
+/*
+ * Sensitive-row QKV projection (SAFE-DiT summary, Methodology 3: fresh projections for the rows of S,
+ * K / V of the context rows kept from the cache): y = x[b, rows[r], :] Wqkv^T + bqkv, feature j of y goes
+ * to tensor j / D (0: q, 1: k_cache, 2: v_cache), head (j % D) / d, channel j % d, at row rows[r] of the
+ * head-major [B, H, N, d] tensors (the layout safe_attn_* read).  x: device bf16 [B, N, D], D = H * d;
+ * Wqkv: bf16 [3D, D]; bqkv: fp32 [3D] or NULL; q / k_cache / v_cache: bf16 [B, H, N, d], other rows
+ * untouched.  D a multiple of 128, d a multiple of 16; pointers 16-byte aligned.  k = 0: no-op.
+ */
+safe_status safe_rows_qkv(const void* x, const int32_t* rows, int32_t k, int32_t B, int32_t N, int32_t H, int32_t d,
+                          const void* wqkv, const float* bqkv, void* q, void* k_cache, void* v_cache,
+                          hipStream_t stream);
+
 /* Human-readable name of a status code (static storage). */
 const char* safe_status_string(safe_status s);
 /* Library version: major*10000 + minor*100 + patch. */

@@ -205,3 +205,28 @@ def test_host_plans_and_percentile_count_match_the_oracle():
     assert lib.safe_stepcache_plan(4, 0, arr, arr, warr) == SHAPE
     assert lib.safe_stepcache_plan(4, 2, None, arr, warr) == NULL
     assert lib.safe_stepcache_plan(0, 2, None, None, None) == OK
+
+
+def test_rows_block_validation():
+    _cpu_only()
+    lib = dts.load()
+    f = 0x10000
+    ffn = lib.safe_rows_ffn
+    ws = 2 * 5 * 256 * 2
+    assert ffn(f, f, 5, 0, 64, 128, 256, f, None, f, None, f, f, ws, None) == SHAPE
+    assert ffn(f, f, 65, 2, 64, 128, 256, f, None, f, None, f, f, ws, None) == RANGE
+    assert ffn(None, None, 0, 2, 64, 128, 256, None, None, None, None, None, None, 0, None) == OK  # k = 0
+    assert ffn(None, f, 5, 2, 64, 128, 256, f, None, f, None, f, f, ws, None) == NULL
+    assert ffn(f, f, 5, 2, 64, 96, 256, f, None, f, None, f, f, ws, None) == UNSUP
+    assert ffn(f, f, 5, 2, 64, 128, 200, f, None, f, None, f, f, ws, None) == UNSUP
+    assert ffn(f, f, 5, 2, 64, 128, 256, f, None, f, None, f, f, ws - 1, None) == WS
+    assert ffn(f + 8, f, 5, 2, 64, 128, 256, f, None, f, None, f, f, ws, None) == ALIGN
+    assert ffn(f, f, 5, 2, 64, 128, 256, f, f + 4, f, None, f, f, ws, None) == ALIGN
+    assert lib.safe_rows_ffn_workspace_bytes(2, 5, 256) == ws
+    qkv = lib.safe_rows_qkv
+    assert qkv(f, f, 5, 2, 64, 0, 64, f, None, f, f, f, None) == SHAPE
+    assert qkv(f, f, 65, 2, 64, 2, 64, f, None, f, f, f, None) == RANGE
+    assert qkv(f, f, 5, 2, 64, 3, 64, f, None, f, f, f, None) == UNSUP  # D = 192
+    assert qkv(f, f, 5, 2, 64, 2, 64, f, None, None, f, f, None) == NULL
+    assert qkv(f, f, 5, 2, 64, 2, 64, f, None, f, f, f + 2, None) == ALIGN
+    assert qkv(None, None, 0, 2, 64, 2, 64, None, None, None, None, None, None) == OK
