@@ -4,6 +4,7 @@
 #include <cstring>
 
 #include "common.hpp"
+#include "launch.hpp"
 
 using namespace safe;
 
