@@ -42,7 +42,8 @@ def _ffn(lib, p, cache0, with_bias=True):
 
 
 @pytest.mark.parametrize("B,N,H,d,k,mult", [(1, 40, 2, 64, 1, 4), (2, 300, 2, 64, 77, 4), (2, 300, 2, 64, 300, 4),
-                                            (2, 500, 4, 64, 129, 2), (3, 257, 2, 64, 200, 1)])
+                                            (2, 500, 4, 64, 129, 2), (3, 257, 2, 64, 200, 1),
+                                            (2, 300, 8, 64, 77, 4), (1, 600, 8, 64, 299, 4)])  # F = 2048: 256 x 256 tiles
 def test_rows_ffn_parity_and_cache_untouched(lib, B, N, H, d, k, mult):
     p = _inputs(B, N, H, d, k, seed=N + k, ffn_mult=mult)
     cache0 = syn.round_to_bf16(np.random.default_rng(k).standard_normal((B, N, p["D"])).astype(np.float32))
@@ -65,7 +66,8 @@ def _qkv(lib, p, H, d, q0, k0, v0):
     return host(q), host(kc), host(vc)
 
 
-@pytest.mark.parametrize("B,N,H,d,k", [(1, 40, 2, 64, 1), (2, 300, 2, 64, 77), (2, 200, 6, 64, 200)])
+@pytest.mark.parametrize("B,N,H,d,k", [(1, 40, 2, 64, 1), (2, 300, 2, 64, 77), (2, 200, 6, 64, 200),
+                                       (2, 200, 12, 64, 131)])  # 3D = 2304: 256 x 256 tiles
 def test_rows_qkv_parity_and_context_untouched(lib, B, N, H, d, k):
     p = _inputs(B, N, H, d, k, seed=3 * N + k)
     r = np.random.default_rng(k)
