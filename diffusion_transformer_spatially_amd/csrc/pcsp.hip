@@ -125,7 +125,7 @@ __global__ __launch_bounds__(kPcspThreads) void k_pcsp_accumulate_b(const float*
                                                                    int T, int Tv, int c0, int c1,
                                                                    const uint8_t* __restrict__ sel,
                                                                    float* __restrict__ scores, int accumulate) {
-  constexpr int JB = 3;
+  constexpr int JB = 6;  // 16 groups x 6 rows: the 4 tokens x 24 heads of a workgroup in one round of loads
   extern __shared__ float part[];  // [kPcspRows][H]
   const int g = threadIdx.x >> 4;
   const int lane = threadIdx.x & 15;
