@@ -48,7 +48,7 @@ def parse():
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs the attention step on exactly one GPU; "
+        print("bench.py: the attention step runs on exactly one GPU; "
               "--gpus above 1 is not supported (no multi-GPU path).", file=sys.stderr)
         sys.exit(2)
 

@@ -58,8 +58,7 @@ def load(path: Optional[str] = None):
         return _lib
     p = path or LIB_PATH
     if not os.path.exists(p):
-        raise RuntimeError(f"{p} is missing: build it with __graft_entry__.build() "
-                           "(python diffusion_transformer_spatially_amd/build.py)")
+        raise RuntimeError(f"{p} is missing: build it with python diffusion_transformer_spatially_amd/build.py")
     lib = ctypes.CDLL(p)
     vp, i32, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
     P = ctypes.POINTER

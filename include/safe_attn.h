@@ -40,7 +40,7 @@ enum {
   SAFE_ERR_DTYPE = 3,       /* unknown dtype code */
   SAFE_ERR_RANGE = 4,       /* k > N, Tv > T, c0 > c1, ... */
   SAFE_ERR_WORKSPACE = 5,   /* a workspace is missing or too small */
-  SAFE_ERR_UNSUPPORTED = 6, /* valid request this build does not implement (e.g. d != 64) */
+  SAFE_ERR_UNSUPPORTED = 6, /* valid request the library does not implement (e.g. d != 64) */
   SAFE_ERR_HIP = 7,         /* a HIP runtime call failed */
   SAFE_ERR_ALIGN = 8        /* a pointer lacks the alignment stated for it */
 };

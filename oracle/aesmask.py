@@ -8,7 +8,7 @@ an affinity map, and a percentile threshold turns the map into a binary mask (1 
 per generation and without training.  Choosing the tokens (CLIP similarity against a fixed anchor word
 list) needs a text encoder and is an input here: a 0/1 vector over the text slots.
 
-Readings taken (the design doc lists them):
+Readings taken where the pages are silent or ambiguous:
 - the weight between image token i and text slot t is the entry of the joint softmax row of i (image
   keys and valid text keys together), the quantity the PCSP aggregation of the SAFE-DiT pages uses:
   LSE = log(exp(lse_img) + sum_{t<Tv} exp(x_t)), a_i = sum_h sum_{t<Tv, sel_t = 1} exp(x_t - LSE);

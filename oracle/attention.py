@@ -12,7 +12,7 @@ What it follows:
 - AccelAes summary (gist.science, Korean page), Method B.2 SkipSparse: queries only for focus
   tokens, keys and values from the whole image.
 
-Readings where the pages are silent (listed in the design doc): one joint softmax over the image keys
+Readings where the pages are silent: one joint softmax over the image keys
 followed by the text keys; scale 1/sqrt(d); trailing text padding given per batch entry as a valid
 length Tv[b], padded keys taking no part in the sum whatever they hold; a fully masked row gives a
 zero output and a log-sum-exp of -inf.

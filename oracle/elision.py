@@ -7,7 +7,7 @@ Key Contributions 2: an additive mask that only shifts each logit row by a const
 normalised attention unchanged and may be removed; text padding, causal masks and non-uniform biases
 are kept.
 
-Reading taken (the design doc lists it): the criterion is checked per mask slice and row, over the keys
+Reading taken where the pages are silent: the criterion is checked per mask slice and row, over the keys
 the row actually attends to, i.e. the image block and the valid text slots of every batch entry that
 uses the slice (padded slots are masked anyway).  Entries must be bitwise-equal under IEEE ==
 (+0 == -0) to one finite constant; NaN or an infinity among them makes the row non-removable.  A

@@ -7,7 +7,7 @@ during a short warmup the attention weights from image tokens to text content to
 aggregated, and the image tokens are split into a sensitive set S and a context set C that stays
 fixed for the rest of the trajectory.  Methodology 4 takes the sensitivity scores s_i from PCSP.
 
-Readings taken (the design doc lists them):
+Readings taken where the pages are silent or ambiguous:
 - the aggregated weight is the text-block mass of the joint softmax row: for head h and image row i,
   LSE = log(exp(lse_img) + sum_{t<Tv} exp(x_t)), a_i += sum_h sum_{t in [c0,c1)} exp(x_t - LSE);
   without lse_img the softmax is over the valid text slots only;

@@ -6,7 +6,7 @@ Follows the SAFE-DiT technical summary (gist.science, Korean and Italian pages),
 (scores aggregated over a short warmup, partition then fixed for the trajectory) and Methodology 3
 (sensitive-row updates in non-anchor steps, a dense refresh in periodic anchor steps).
 
-Reading taken (the design doc lists it): the warmup steps precede the scheduled steps; step t is an anchor
+Reading taken where the pages are silent: the warmup steps precede the scheduled steps; step t is an anchor
 when t % anchor_every == 0, a sensitive-row step otherwise (anchors at 0, 4, 8 of 10 steps).
 """
 from __future__ import annotations

@@ -8,7 +8,7 @@ sensitive rows S are recomputed; the context rows keep cached values) and the Ac
 summary, 2. Methodology B.2 SkipSparse (queries of the focus tokens only, keys and values global; the
 FFN of background tokens skipped and its most recent cached output reused).
 
-Readings taken (the design doc lists them):
+Readings taken where the pages are silent or ambiguous:
 - hidden states are token-major [B, N, D] with D = H * d; a linear layer stores its weight as
   [out_features, in_features] and computes y = x W^T + b;
 - the FFN is Linear(D -> F) -> GELU (tanh form) -> Linear(F -> D), the DiT block's FFN; its output for

@@ -6,7 +6,7 @@ Follows the AccelAes technical summary (Korean), gist.science, 2. Methodology B.
 transformer runs only at a fixed step interval, and the steps between reuse the noise prediction by
 linear extrapolation; the module does not depend on the model's architecture.
 
-Readings taken (the design doc lists them):
+Readings taken where the pages are silent or ambiguous:
 - the full steps are s = 0, delta, 2 delta, ...;
 - a step s strictly between full steps j*delta and (j+1)*delta, j >= 1, takes the line through the last
   two full predictions, in step units: eps_s = eps_b + w (eps_b - eps_a) with a = (j-1) delta,

@@ -7,7 +7,7 @@ guidance scale is set per token, gamma_i = gamma_ctx + (gamma_sens - gamma_ctx) 
 to the prediction after the forward pass.  The AccelAes summary (Method B.2, spatial CFG) is the
 binary-s special case.
 
-Readings taken (the design doc lists them): the guided prediction is eps_u + gamma_i (eps_c - eps_u) with
+Readings taken where the pages are silent or ambiguous: the guided prediction is eps_u + gamma_i (eps_c - eps_u) with
 eps[0] the conditional and eps[1] the unconditional prediction; a latent pixel (y, x) belongs to the
 token (y // ph) * side + x // pw of the side x side grid, ph = Hl / side, pw = Wl / side.
 """
