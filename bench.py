@@ -294,7 +294,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": dense_tf, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": dense_tf / MFMA_BF16_PEAK_TFLOPS, "traffic": profiled_traffic(),
                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE/WRITE_SIZE, copy-calibrated)",
-                     "kernel": "k_attn_mfma<false, 2, false, 0, 1> (dense anchor attention)",
+                     "kernel": "k_attn_mfma<false, 2, false, 0, 1, 64> (dense anchor attention)",
                      "flops_per_launch": w.flops_dense, "avg_launch_ms": avg_ms["attn_dense"],
                      "sclk_mhz": sclk, "peak_at_sclk": peak_sclk,
                      "frac_at_sclk": (dense_tf / peak_sclk) if peak_sclk else None,
@@ -357,6 +357,9 @@ def main():
                                                    reps=3)[-1]
 
     result["mask_tax"] = tax
+    # head dim 128 at the 1024^2 grid (24 heads x 128): the same path at the other head dim the library takes
+    result["attention_d128_1024"] = attention_large(dts, torch, syn, dev, syn.WORKLOADS["dense_1024_d128"], stream,
+                                                    reps=10)[-1]
     result["aesmask_stepcache"] = next_rows(dts, torch, np, syn, dev, hbm, not args.no_large)
     result["srsu_block"] = srsu_block(dts, torch, np, syn, dev)
 

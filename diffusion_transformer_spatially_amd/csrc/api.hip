@@ -19,7 +19,7 @@ safe_status check_attn(const safe_attn_desc* d) {
   if (d->dtype != SAFE_DTYPE_BF16 && d->dtype != SAFE_DTYPE_F32) return SAFE_ERR_DTYPE;
   if (d->B < 1 || d->H < 1 || d->N < 1 || d->T < 0 || d->d < 1) return SAFE_ERR_SHAPE;
   if (d->B > SAFE_MAX_BATCH) return SAFE_ERR_UNSUPPORTED;
-  if (d->d != 64) return SAFE_ERR_UNSUPPORTED;
+  if (d->d != 64 && d->d != 128) return SAFE_ERR_UNSUPPORTED;
   if (d->q == nullptr || d->k_img == nullptr || d->v_img == nullptr || d->out == nullptr ||
       d->text_valid_len == nullptr)
     return SAFE_ERR_NULL;
@@ -74,19 +74,21 @@ AttnArgs make_args(const safe_attn_desc* d, const int32_t* rows, int R) {
 }
 
 // A kept mask runs on the MFMA kernel when each lane's 16-entry mask chunks are aligned and never cross a
-// mask row (N and the row length multiples of 16, 16-byte aligned base) and no emission is asked (the
-// emission of masked logits stays on the generic kernel); otherwise on the generic kernel.
+// mask row (N and the row length multiples of 16, 16-byte aligned base), no emission is asked (the
+// emission of masked logits stays on the generic kernel) and, at head dim 128, the mask is bool (fp32
+// mask chunks do not fit in registers beside a 128-dim block's accumulators); otherwise on the generic
+// kernel.
 bool mfma_takes_mask(const safe_attn_desc* d) {
   return d->xattn_out == nullptr && d->lse_img_out == nullptr && d->N % 16 == 0 && d->mask_cols % 16 == 0 &&
-         (reinterpret_cast<uintptr_t>(d->mask) & 15u) == 0;
+         (reinterpret_cast<uintptr_t>(d->mask) & 15u) == 0 && (d->d == 64 || d->mask_dtype == SAFE_DTYPE_BOOL);
 }
 
 safe_status run_attn(const safe_attn_desc* d, const int32_t* rows, int R, hipStream_t s) {
   const AttnArgs a = make_args(d, rows, R);
   if (R == 0) return SAFE_OK;
   if (d->dtype == SAFE_DTYPE_BF16 && (d->mask == nullptr || mfma_takes_mask(d)))
-    return from_hip(launch_attn_mfma_bf16(a, s));
-  return from_hip(launch_attn_generic(a, d->dtype, s));
+    return from_hip(launch_attn_mfma_bf16(a, d->d, s));
+  return from_hip(launch_attn_generic(a, d->dtype, d->d, s));
 }
 
 }  // namespace
@@ -322,6 +324,6 @@ const char* safe_status_string(safe_status s) {
   }
 }
 
-int32_t safe_version(void) { return 200; }
+int32_t safe_version(void) { return 210; }
 
 }  // extern "C"

@@ -7,14 +7,16 @@
 // over the image keys then the valid text keys (padded text slots never enter), logits scaled by
 // `scale`, kept mask added; a fully masked row yields 0 and lse = -inf.
 //
-// Layout: one thread per query row (q and the 64 output accumulators in registers), 256 rows per
-// workgroup; 32-key tiles of K and V are staged in LDS as fp32 and read as broadcasts.
+// Layout: D / 64 threads per query row, each holding 64 dims of q and of the output accumulators in
+// registers (head dim 64: one thread per row, 256 rows per workgroup; head dim 128: two adjacent threads
+// per row, 128 rows per workgroup, their partial dot products summed with one lane exchange); 32-key
+// tiles of K and V are staged in LDS as fp32 and read as broadcasts.
 #include "common.hpp"
 
 namespace safe {
 
 constexpr int kGenThreads = 256;
-constexpr int kGenD = 64;
+constexpr int kGenPart = 64;  // head dims per thread
 constexpr int kGenTile = 32;
 
 template <typename T>
@@ -31,30 +33,34 @@ __device__ __forceinline__ void st<float>(float* p, size_t i, float v) { p[i] = 
 template <>
 __device__ __forceinline__ void st<uint16_t>(uint16_t* p, size_t i, float v) { p[i] = f32_to_bf16_rne(v); }
 
-template <typename T, bool HAS_MASK>
+template <typename T, bool HAS_MASK, int D>
 __global__ __launch_bounds__(kGenThreads) void k_attn_generic(AttnArgs a) {
-  __shared__ float ks[kGenTile][kGenD];
-  __shared__ float vs[kGenTile][kGenD];
-  const int nqb = (a.R + kGenThreads - 1) / kGenThreads;
+  constexpr int kLpr = D / kGenPart;             // threads per query row
+  constexpr int kRows = kGenThreads / kLpr;      // query rows per workgroup
+  __shared__ float ks[kGenTile][D];
+  __shared__ float vs[kGenTile][D];
+  const int nqb = (a.R + kRows - 1) / kRows;
   const int bh = blockIdx.x / nqb;
   const int qb = blockIdx.x - bh * nqb;
   const int b = bh / a.H, h = bh - b * a.H;
-  const int r = qb * kGenThreads + threadIdx.x;
+  const int part = static_cast<int>(threadIdx.x) % kLpr;  // which 64 dims of the row this thread holds
+  const int c0 = part * kGenPart;
+  const int r = qb * kRows + static_cast<int>(threadIdx.x) / kLpr;
   const bool active = r < a.R;
   int row = active ? (a.rows ? a.rows[r] : r) : 0;
   const bool valid_row = active && row >= 0 && row < a.N;
   if (!valid_row) row = 0;
   const int tv = a.tv[b];
-  const T* Q = static_cast<const T*>(a.q) + static_cast<size_t>(bh) * a.N * kGenD;
-  const T* KI = static_cast<const T*>(a.k_img) + static_cast<size_t>(bh) * a.N * kGenD;
-  const T* VI = static_cast<const T*>(a.v_img) + static_cast<size_t>(bh) * a.N * kGenD;
-  const T* KT = static_cast<const T*>(a.k_txt) + static_cast<size_t>(bh) * a.T * kGenD;
-  const T* VT = static_cast<const T*>(a.v_txt) + static_cast<size_t>(bh) * a.T * kGenD;
+  const T* Q = static_cast<const T*>(a.q) + static_cast<size_t>(bh) * a.N * D;
+  const T* KI = static_cast<const T*>(a.k_img) + static_cast<size_t>(bh) * a.N * D;
+  const T* VI = static_cast<const T*>(a.v_img) + static_cast<size_t>(bh) * a.N * D;
+  const T* KT = static_cast<const T*>(a.k_txt) + static_cast<size_t>(bh) * a.T * D;
+  const T* VT = static_cast<const T*>(a.v_txt) + static_cast<size_t>(bh) * a.T * D;
 
-  float q[kGenD], o[kGenD];
+  float q[kGenPart], o[kGenPart];
 #pragma unroll
-  for (int c = 0; c < kGenD; ++c) {
-    q[c] = ld(Q, static_cast<size_t>(row) * kGenD + c);
+  for (int c = 0; c < kGenPart; ++c) {
+    q[c] = ld(Q, static_cast<size_t>(row) * D + c0 + c);
     o[c] = 0.f;
   }
   // mask row pointer (fp32 entries or bool bytes)
@@ -77,11 +83,11 @@ __global__ __launch_bounds__(kGenThreads) void k_attn_generic(AttnArgs a) {
     const T* Ksrc = txt ? KT : KI;
     const T* Vsrc = txt ? VT : VI;
     __syncthreads();
-    for (int e = threadIdx.x; e < kGenTile * kGenD; e += kGenThreads) {
-      const int jj = e / kGenD, c = e - jj * kGenD;
+    for (int e = threadIdx.x; e < kGenTile * D; e += kGenThreads) {
+      const int jj = e / D, c = e - jj * D;
       const bool ok = jj < nvalid;
-      ks[jj][c] = ok ? ld(Ksrc, static_cast<size_t>(j0 + jj) * kGenD + c) : 0.f;
-      vs[jj][c] = ok ? ld(Vsrc, static_cast<size_t>(j0 + jj) * kGenD + c) : 0.f;
+      ks[jj][c] = ok ? ld(Ksrc, static_cast<size_t>(j0 + jj) * D + c) : 0.f;
+      vs[jj][c] = ok ? ld(Vsrc, static_cast<size_t>(j0 + jj) * D + c) : 0.f;
     }
     __syncthreads();
     // logits of this tile, in log2 units, mask included
@@ -91,7 +97,8 @@ __global__ __launch_bounds__(kGenThreads) void k_attn_generic(AttnArgs a) {
     for (int jj = 0; jj < kGenTile; ++jj) {
       float acc = 0.f;
 #pragma unroll
-      for (int c = 0; c < kGenD; ++c) acc = fmaf(q[c], ks[jj][c], acc);
+      for (int c = 0; c < kGenPart; ++c) acc = fmaf(q[c], ks[jj][c0 + c], acc);
+      if constexpr (kLpr == 2) acc += __shfl_xor(acc, 1);  // the other half of the row's dot product
       float z = acc * a.scale;  // natural-log logit
       if (HAS_MASK) {
         const int col = (txt ? a.N : 0) + j0 + jj;
@@ -102,7 +109,7 @@ __global__ __launch_bounds__(kGenThreads) void k_attn_generic(AttnArgs a) {
         }
         z += mv;
       }
-      if (emit && txt && a.xattn_out != nullptr && valid_row && jj < nvalid)
+      if (emit && txt && a.xattn_out != nullptr && valid_row && jj < nvalid && part == 0)
         a.xattn_out[(static_cast<size_t>(h) * a.N + row) * a.T + j0 + jj] = z;
       s[jj] = jj < nvalid ? z * kLog2e : -INFINITY;
       tmax = fmaxf(tmax, s[jj]);
@@ -112,40 +119,47 @@ __global__ __launch_bounds__(kGenThreads) void k_attn_generic(AttnArgs a) {
       const float alpha = exp2f(m - mnew);
       l *= alpha;
 #pragma unroll
-      for (int c = 0; c < kGenD; ++c) o[c] *= alpha;
+      for (int c = 0; c < kGenPart; ++c) o[c] *= alpha;
 #pragma unroll
       for (int jj = 0; jj < kGenTile; ++jj) {
         const float p = exp2f(s[jj] - mnew);
         l += p;
 #pragma unroll
-        for (int c = 0; c < kGenD; ++c) o[c] = fmaf(p, vs[jj][c], o[c]);
+        for (int c = 0; c < kGenPart; ++c) o[c] = fmaf(p, vs[jj][c0 + c], o[c]);
       }
       m = mnew;
     }
-    if (emit && t == n_img_tiles - 1 && a.lse_img_out != nullptr && valid_row)
+    if (emit && t == n_img_tiles - 1 && a.lse_img_out != nullptr && valid_row && part == 0)
       a.lse_img_out[static_cast<size_t>(h) * a.N + row] = (l > 0.f) ? (m + log2f(l)) * kLn2 : -INFINITY;
   }
   (void)c2;
   if (!valid_row) return;
   const float inv = l > 0.f ? 1.f / l : 0.f;
-  T* O = static_cast<T*>(a.out) + static_cast<size_t>(bh) * a.N * kGenD;
+  T* O = static_cast<T*>(a.out) + static_cast<size_t>(bh) * a.N * D;
 #pragma unroll
-  for (int c = 0; c < kGenD; ++c) st(O, static_cast<size_t>(row) * kGenD + c, o[c] * inv);
-  if (a.lse != nullptr)
+  for (int c = 0; c < kGenPart; ++c) st(O, static_cast<size_t>(row) * D + c0 + c, o[c] * inv);
+  if (a.lse != nullptr && part == 0)
     a.lse[static_cast<size_t>(bh) * a.N + row] = (l > 0.f) ? (m + log2f(l)) * kLn2 : -INFINITY;
 }
 
-hipError_t launch_attn_generic(const AttnArgs& a, int dtype, hipStream_t s) {
-  const int nqb = (a.R + kGenThreads - 1) / kGenThreads;
+template <int D>
+static void launch_generic(const AttnArgs& a, int dtype, hipStream_t s) {
+  constexpr int kRows = kGenThreads / (D / kGenPart);
+  const int nqb = (a.R + kRows - 1) / kRows;
   const uint32_t grid = static_cast<uint32_t>(a.B) * a.H * nqb;
   const bool mask = a.mask != nullptr;
   if (dtype == SAFE_DTYPE_F32) {
-    if (mask) k_attn_generic<float, true><<<grid, kGenThreads, 0, s>>>(a);
-    else k_attn_generic<float, false><<<grid, kGenThreads, 0, s>>>(a);
+    if (mask) k_attn_generic<float, true, D><<<grid, kGenThreads, 0, s>>>(a);
+    else k_attn_generic<float, false, D><<<grid, kGenThreads, 0, s>>>(a);
   } else {
-    if (mask) k_attn_generic<uint16_t, true><<<grid, kGenThreads, 0, s>>>(a);
-    else k_attn_generic<uint16_t, false><<<grid, kGenThreads, 0, s>>>(a);
+    if (mask) k_attn_generic<uint16_t, true, D><<<grid, kGenThreads, 0, s>>>(a);
+    else k_attn_generic<uint16_t, false, D><<<grid, kGenThreads, 0, s>>>(a);
   }
+}
+
+hipError_t launch_attn_generic(const AttnArgs& a, int dtype, int d, hipStream_t s) {
+  if (d == 128) launch_generic<128>(a, dtype, s);
+  else launch_generic<64>(a, dtype, s);
   return hipGetLastError();
 }
 

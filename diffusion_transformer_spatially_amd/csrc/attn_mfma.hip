@@ -51,11 +51,12 @@ typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) uint16_t lds_u16;
 
-constexpr int kD = 64;
 constexpr int kBN = 64;
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-constexpr int kTileElems = kBN * kD;
+// elements of one K or V tile (64 keys x head dim D)
+template <int D>
+constexpr int kTileElems = kBN * D;
 
 __device__ __forceinline__ float swap_halves(float x) {
   // value held by lane L ^ 32
@@ -64,13 +65,22 @@ __device__ __forceinline__ float swap_halves(float x) {
   return __uint_as_float(lane < 32 ? r[1] : r[0]);
 }
 
-// XOR swizzle of the 16-byte chunk index by key row: bits (1, 2, 4) of the row go to chunk bits
-// (2, 1, 0).  With 128-byte rows this spreads both LDS read patterns of a tile step -- 16-byte reads of
-// 16 permuted K rows, and transposing 8-byte reads of 4 consecutive V rows x 64 bytes -- over all 64
-// banks without conflicts.
-__device__ __forceinline__ int swz(int key) { return (((key >> 1) & 1) << 2) | (((key >> 2) & 1) << 1) | ((key >> 4) & 1); }
+// XOR swizzle of the 16-byte chunk index by key row, so that both LDS read patterns of a tile step --
+// 16-byte reads of 16 permuted K rows (rows differing in bits 0, 1, 2 and 4), and transposing 8-byte
+// reads of 4 consecutive V rows -- spread over all 64 banks without conflicts.
+//  D = 64 (128-byte rows, two rows per 256-byte bank window): row bits (1, 2, 4) go to chunk bits
+//  (2, 1, 0); row bit 0 already picks the half of the window.
+//  D = 128 (256-byte rows, one row per window): row bits (2, 4, 0, 1) go to chunk bits (0, 1, 2, 3);
+//  the K pattern needs an injective map of the four varying row bits, the V pattern (4 consecutive
+//  rows x 4 consecutive chunks) needs row bits 0 and 1 on chunk bits 2 and 3.
+template <int D>
+__device__ __forceinline__ int swz(int key) {
+  if constexpr (D == 64) return (((key >> 1) & 1) << 2) | (((key >> 2) & 1) << 1) | ((key >> 4) & 1);
+  else return ((key & 1) << 2) | (((key >> 1) & 1) << 3) | ((key >> 2) & 1) | (((key >> 4) & 1) << 1);
+}
 // LDS element offset of (key row, 16-byte chunk) with the chunk XOR-swizzled by the row.
-__device__ __forceinline__ int lds_off(int key, int chunk) { return key * kD + ((chunk ^ swz(key)) << 3); }
+template <int D>
+__device__ __forceinline__ int lds_off(int key, int chunk) { return key * D + ((chunk ^ swz<D>(key)) << 3); }
 
 struct TileSrc {
   const uint16_t* k;
@@ -78,24 +88,25 @@ struct TileSrc {
   int nvalid;
 };
 
+template <int D>
 __device__ __forceinline__ TileSrc tile_src(const AttnArgs& a, size_t bh, int t, int n_img, int tv) {
   TileSrc s;
   if (t < n_img) {
     const int j0 = t * kBN;
-    s.k = static_cast<const uint16_t*>(a.k_img) + (bh * a.N + j0) * kD;
-    s.v = static_cast<const uint16_t*>(a.v_img) + (bh * a.N + j0) * kD;
+    s.k = static_cast<const uint16_t*>(a.k_img) + (bh * a.N + j0) * D;
+    s.v = static_cast<const uint16_t*>(a.v_img) + (bh * a.N + j0) * D;
     s.nvalid = min(kBN, a.N - j0);
   } else {
     const int j0 = (t - n_img) * kBN;
-    s.k = static_cast<const uint16_t*>(a.k_txt) + (bh * a.T + j0) * kD;
-    s.v = static_cast<const uint16_t*>(a.v_txt) + (bh * a.T + j0) * kD;
+    s.k = static_cast<const uint16_t*>(a.k_txt) + (bh * a.T + j0) * D;
+    s.v = static_cast<const uint16_t*>(a.v_txt) + (bh * a.T + j0) * D;
     s.nvalid = min(kBN, tv - j0);
   }
   return s;
 }
 
 // Direct global -> LDS copies of one tile (no VGPR staging): each wave instruction writes 64
-// consecutive 16-byte LDS slots; slot p holds key row p/8, chunk (p%8) ^ swz(row) (the XOR swizzle), so
+// consecutive 16-byte LDS slots; slot p holds key row p/(D/8), chunk (p%(D/8)) ^ swz(row) (the XOR swizzle), so
 // the global address of each lane is chosen to land its chunk in that slot.  Rows past nvalid are
 // clamped to the last valid row (never read out of bounds, never read padded text); the softmax
 // masks those keys to -inf and their probabilities are exactly 0.
@@ -104,21 +115,23 @@ __device__ __forceinline__ TileSrc tile_src(const AttnArgs& a, size_t bh, int t,
 // through an empty asm, so the compiler cannot treat the LDS destinations derived from it as loop
 // invariants; it recomputes them per tile (two scalar adds) instead of hoisting all of them out of the
 // tile loop, where they were spilled and each reload waited for the tile copies already in flight.
-template <bool OPAQUE>
+template <int D, bool OPAQUE>
 __device__ __forceinline__ void stage_issue(const TileSrc& s, uint16_t* kl, uint16_t* vl) {
+  constexpr int kChunks = D / 8;                // 16-byte chunks per key row
+  constexpr int kChunkShift = D == 64 ? 3 : 4;  // log2(kChunks)
   const int lane = threadIdx.x & 63;
   int wslot = __builtin_amdgcn_readfirstlane(static_cast<int>((threadIdx.x >> 6) & 3)) * 64;
   if (OPAQUE) asm volatile("" : "+s"(wslot));
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
+  for (int u = 0; u < kBN * kChunks / (kWaves * 64); ++u) {
     const int base = u * kWaves * 64 + wslot;  // first slot of this wave instruction
     const int p = base + lane;
-    const int row = p >> 3;
-    const int c = (p & 7) ^ swz(row);
+    const int row = p >> kChunkShift;
+    const int c = (p & (kChunks - 1)) ^ swz<D>(row);
     const int srow = row < s.nvalid ? row : s.nvalid - 1;
-    __builtin_amdgcn_global_load_lds(static_cast<const void*>(s.k + srow * kD + c * 8),
+    __builtin_amdgcn_global_load_lds(static_cast<const void*>(s.k + srow * D + c * 8),
                                      (__attribute__((address_space(3))) void*)(kl + base * 8), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(static_cast<const void*>(s.v + srow * kD + c * 8),
+    __builtin_amdgcn_global_load_lds(static_cast<const void*>(s.v + srow * D + c * 8),
                                      (__attribute__((address_space(3))) void*)(vl + base * 8), 16, 0, 0);
   }
 }
@@ -129,10 +142,10 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 }
 
 // Per-wave running state of QB query blocks.
-template <int QB>
+template <int QB, int D>
 struct WaveState {
-  bf16x8 q[QB][4];   // Q^T operand: lane (q + 32g) holds Q[q][16ks + 8g .. +7]
-  f32x16 o[QB][2];   // O^T accumulators: lane holds query L%32, head dims db*32 + 8(r/4) + 4g + r%4
+  bf16x8 q[QB][D / 16];  // Q^T operand: lane (q + 32g) holds Q[q][16ks + 8g .. +7]
+  f32x16 o[QB][D / 32];  // O^T accumulators: lane holds query L%32, head dims db*32 + 8(r/4) + 4g + r%4
   float m[QB];       // running row max (raw dot-product units)
   float l[QB];       // running row sum of exp2((s - m) * c2), lane-half partial
 };
@@ -186,13 +199,15 @@ __device__ __forceinline__ void mask_apply(f32x16& s, const MaskTile<KM>& mt, in
   }
 }
 
-// Fast path (no lse, no emission): Q was pre-multiplied by scale * log2(e) and rounded to bf16 once, so
-// the logits come out of the MFMA in log2 units, and each tile's logit accumulators start at -m (two
-// 64-bit moves per four registers), so the MFMA output is already s - m and each probability costs a
-// single exp2 instead of an fma and an exp2.  Rounding the scaled Q to bf16 perturbs a logit by about
-// 2^-9 of the root-sum-square of its products, below the bf16 rounding of the probabilities
-// themselves.  The lazy running max and its exact path are as in the general step below (m is kept in
-// log2 units here).
+// Fast path (no lse, no emission), head dim 64: Q was pre-multiplied by scale * log2(e) and rounded to
+// bf16 once, so the logits come out of the MFMA in log2 units, and each tile's logit accumulators start
+// at -m (two 64-bit moves per four registers), so the MFMA output is already s - m and each probability
+// costs a single exp2 instead of an fma and an exp2.  Rounding the scaled Q to bf16 perturbs a logit by
+// about 2^-9 of the root-sum-square of its products, below the bf16 rounding of the probabilities
+// themselves.  Head dim 128 keeps Q exact and takes the fma per logit (s * scale * log2 e - m): with half
+// the vector work per matrix instruction of head dim 64 it has the room, and on sharply peaked rows
+// (logits with a standard deviation near 9) the rounded-Q error there reached the bf16 output tolerance.
+// The lazy running max and its exact path are as in the general step below (m is kept in log2 units).
 
 // One query block's softmax of a tile on the fast path (logits s are log2 units minus m): probabilities
 // p and their bf16 row-sum contribution, with the lazy-max exact path.  Split out so that the two query
@@ -223,15 +238,15 @@ __device__ __forceinline__ float fast_probs(bf16x8 (&p)[2][2], f32x16 (&s)[2], i
 }
 
 // Exact path of one query block (rare): logits again from K in LDS, tile max, rescale, probabilities again.
-template <bool MASKED>
-__device__ __forceinline__ float fast_exact(bf16x8 (&p)[2][2], const bf16x8 (&q)[4], float& m, float& l, f32x16 (&o)[2],
-                                            const uint16_t* kl, int kperm, int g, int nvalid) {
+template <bool MASKED, int D>
+__device__ __forceinline__ float fast_exact(bf16x8 (&p)[2][2], const bf16x8 (&q)[D / 16], float& m, float& l,
+                                            f32x16 (&o)[D / 32], const uint16_t* kl, int kperm, int g, int nvalid) {
   f32x16 sx[2];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kl + lds_off(kb * 32 + kperm, 2 * ks + g));
+    for (int ks = 0; ks < D / 16; ++ks) {
+      const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kl + lds_off<D>(kb * 32 + kperm, 2 * ks + g));
       sx[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, q[ks], ks == 0 ? (f32x16){} : sx[kb], 0, 0, 0);
     }
   if (MASKED) {
@@ -251,7 +266,7 @@ __device__ __forceinline__ float fast_exact(bf16x8 (&p)[2][2], const bf16x8 (&q)
     const float alpha = __builtin_amdgcn_exp2f(m - mnew);
     l *= alpha;
 #pragma unroll
-    for (int db = 0; db < 2; ++db)
+    for (int db = 0; db < D / 32; ++db)
 #pragma unroll
       for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
     m = mnew;
@@ -284,13 +299,13 @@ __device__ __forceinline__ void soft_chunk(uint32_t (&pk)[2][2][4], const f32x16
 // the scheduler otherwise bunches into long vector runs with the matrix core idle.  The lazy-max exact
 // path of a block runs between its softmax and its output update.
 template <bool MASKED>
-__device__ __forceinline__ void tile_step_fast2(WaveState<2>& st, const uint16_t* kl, const uint16_t* vl, int kperm,
+__device__ __forceinline__ void tile_step_fast2(WaveState<2, 64>& st, const uint16_t* kl, const uint16_t* vl, int kperm,
                                                 int g, int li, int dc0, int nvalid) {
   bf16x8 ka[2][4];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) ka[kb][ks] = *reinterpret_cast<const bf16x8*>(kl + lds_off(kb * 32 + kperm, 2 * ks + g));
+    for (int ks = 0; ks < 4; ++ks) ka[kb][ks] = *reinterpret_cast<const bf16x8*>(kl + lds_off<64>(kb * 32 + kperm, 2 * ks + g));
   f32x16 s0[2], s1[2];
   {
     const double n0 = __builtin_bit_cast(double, (f32x2){-st.m[0], -st.m[0]});
@@ -337,7 +352,7 @@ __device__ __forceinline__ void tile_step_fast2(WaveState<2>& st, const uint16_t
 #pragma unroll
     for (int mm = 0; mm < 2; ++mm)
       p0[kb][mm] = __builtin_bit_cast(bf16x8, (uint4){pk0[kb][mm][0], pk0[kb][mm][1], pk0[kb][mm][2], pk0[kb][mm][3]});
-  if (__any(!(t0 <= 65536.f))) t0 = fast_exact<MASKED>(p0, st.q[0], st.m[0], st.l[0], st.o[0], kl, kperm, g, nvalid);
+  if (__any(!(t0 <= 65536.f))) t0 = fast_exact<MASKED, 64>(p0, st.q[0], st.m[0], st.l[0], st.o[0], kl, kperm, g, nvalid);
   st.l[0] += t0;
   // V^T operands (shared by both blocks)
   lds_u16* vl3 = (lds_u16*)(vl);
@@ -350,9 +365,9 @@ __device__ __forceinline__ void tile_step_fast2(WaveState<2>& st, const uint16_t
 #pragma unroll
       for (int db = 0; db < 2; ++db) {
         const int col = db * 32 + dc0 + 4 * (li & 3);
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vl3 + lds_off(key, col >> 3) + (col & 4)));
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vl3 + lds_off<64>(key, col >> 3) + (col & 4)));
         const s16x4 hi =
-            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vl3 + lds_off(key + 4, col >> 3) + (col & 4)));
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vl3 + lds_off<64>(key + 4, col >> 3) + (col & 4)));
         va[kb][mm][db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       }
     }
@@ -376,7 +391,7 @@ __device__ __forceinline__ void tile_step_fast2(WaveState<2>& st, const uint16_t
 #pragma unroll
     for (int mm = 0; mm < 2; ++mm)
       p1[kb][mm] = __builtin_bit_cast(bf16x8, (uint4){pk1[kb][mm][0], pk1[kb][mm][1], pk1[kb][mm][2], pk1[kb][mm][3]});
-  if (__any(!(t1 <= 65536.f))) t1 = fast_exact<MASKED>(p1, st.q[1], st.m[1], st.l[1], st.o[1], kl, kperm, g, nvalid);
+  if (__any(!(t1 <= 65536.f))) t1 = fast_exact<MASKED, 64>(p1, st.q[1], st.m[1], st.l[1], st.o[1], kl, kperm, g, nvalid);
   st.l[1] += t1;
   // output update of block 1
 #pragma unroll
@@ -388,10 +403,12 @@ __device__ __forceinline__ void tile_step_fast2(WaveState<2>& st, const uint16_t
         st.o[1][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[kb][mm][db], p1[kb][mm], st.o[1][db], 0, 0, 0);
 }
 
-template <int QB, bool MASKED, int KM>
-__device__ __forceinline__ void tile_step_fast(WaveState<QB>& st, const uint16_t* kl, const uint16_t* vl, int kperm,
-                                               int g, int li, int dc0, int nvalid, const MaskTile<KM>& mt) {
+template <int QB, bool MASKED, int KM, int D>
+__device__ __forceinline__ void tile_step_fast(WaveState<QB, D>& st, const uint16_t* kl, const uint16_t* vl, int kperm,
+                                               int g, int li, int dc0, float c2, int nvalid, const MaskTile<KM>& mt) {
+  constexpr bool kPre = D == 64;  // Q pre-scaled to log2 units (head dim 64) or exact (head dim 128)
   static_assert(KM == 0 || QB == 1, "a kept mask runs with one query block per wave");
+  static_assert(QB == 1 || D == 64, "two query blocks per wave only at head dim 64");
   if constexpr (QB == 2) {
     tile_step_fast2<MASKED>(st, kl, vl, kperm, g, li, dc0, nvalid);
     return;
@@ -405,19 +422,28 @@ __device__ __forceinline__ void tile_step_fast(WaveState<QB>& st, const uint16_t
       double d[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) d[i] = nm2;
-      s[qb][kb] = __builtin_bit_cast(f32x16, d);
+      if constexpr (kPre) s[qb][kb] = __builtin_bit_cast(f32x16, d);
     }
   }
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
     const int key = kb * 32 + kperm;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kl + lds_off(key, 2 * ks + g));
+    for (int ks = 0; ks < D / 16; ++ks) {
+      const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kl + lds_off<D>(key, 2 * ks + g));
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
-        s[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, st.q[qb][ks], s[qb][kb], 0, 0, 0);
+        s[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, st.q[qb][ks], (!kPre && ks == 0) ? (f32x16){} : s[qb][kb],
+                                                            0, 0, 0);
     }
+  }
+  if constexpr (!kPre) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[qb][kb][i] = fmaf(s[qb][kb][i], c2, -st.m[qb]);
   }
   if (MASKED) {
 #pragma unroll
@@ -460,10 +486,16 @@ __device__ __forceinline__ void tile_step_fast(WaveState<QB>& st, const uint16_t
       for (int kb = 0; kb < 2; ++kb) {
         const int key = kb * 32 + kperm;
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kl + lds_off(key, 2 * ks + g));
+        for (int ks = 0; ks < D / 16; ++ks) {
+          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kl + lds_off<D>(key, 2 * ks + g));
           sx[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, st.q[qb][ks], ks == 0 ? (f32x16){} : sx[kb], 0, 0, 0);
         }
+      }
+      if constexpr (!kPre) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) sx[kb][i] *= c2;
       }
       if (MASKED) {
 #pragma unroll
@@ -486,7 +518,7 @@ __device__ __forceinline__ void tile_step_fast(WaveState<QB>& st, const uint16_t
         const float alpha = __builtin_amdgcn_exp2f(st.m[qb] - mnew);
         st.l[qb] *= alpha;
 #pragma unroll
-        for (int db = 0; db < 2; ++db)
+        for (int db = 0; db < D / 32; ++db)
 #pragma unroll
           for (int i = 0; i < 16; ++i) st.o[qb][db][i] *= alpha;
         st.m[qb] = mnew;
@@ -525,11 +557,11 @@ __device__ __forceinline__ void tile_step_fast(WaveState<QB>& st, const uint16_t
     for (int mm = 0; mm < 2; ++mm) {
       const int key = kb * 32 + 16 * g + 8 * mm + (li >> 2);
 #pragma unroll
-      for (int db = 0; db < 2; ++db) {
+      for (int db = 0; db < D / 32; ++db) {
         const int col = db * 32 + dc0 + 4 * (li & 3);
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vl3 + lds_off(key, col >> 3) + (col & 4)));
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vl3 + lds_off<D>(key, col >> 3) + (col & 4)));
         const s16x4 hi =
-            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vl3 + lds_off(key + 4, col >> 3) + (col & 4)));
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vl3 + lds_off<D>(key + 4, col >> 3) + (col & 4)));
         const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
@@ -541,12 +573,12 @@ __device__ __forceinline__ void tile_step_fast(WaveState<QB>& st, const uint16_t
 
 // One 64-key tile: logits, online softmax, P V.  MASKED handles partial tiles (keys >= nvalid are
 // -inf) and the optional store of the tile's logits (text tiles of the warmup emission).
-template <int QB, bool MASKED, bool EXACT_SUM, int KM>
-__device__ __forceinline__ void tile_step(WaveState<QB>& st, const uint16_t* kl, const uint16_t* vl, int kperm,
+template <int QB, bool MASKED, bool EXACT_SUM, int KM, int D>
+__device__ __forceinline__ void tile_step(WaveState<QB, D>& st, const uint16_t* kl, const uint16_t* vl, int kperm,
                                           int g, int li, int dc0, float c2, int nvalid, float* const (&xo)[QB],
                                           float scale, const MaskTile<KM>& mt) {
   if constexpr (!EXACT_SUM) {
-    tile_step_fast<QB, MASKED, KM>(st, kl, vl, kperm, g, li, dc0, nvalid, mt);
+    tile_step_fast<QB, MASKED, KM, D>(st, kl, vl, kperm, g, li, dc0, c2, nvalid, mt);
     return;
   }
   static_assert(KM == 0 || QB == 1, "a kept mask runs with one query block per wave");
@@ -557,8 +589,8 @@ __device__ __forceinline__ void tile_step(WaveState<QB>& st, const uint16_t* kl,
   for (int kb = 0; kb < 2; ++kb) {
     const int key = kb * 32 + kperm;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kl + lds_off(key, 2 * ks + g));
+    for (int ks = 0; ks < D / 16; ++ks) {
+      const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kl + lds_off<D>(key, 2 * ks + g));
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         if (ks == 0)
@@ -636,8 +668,8 @@ __device__ __forceinline__ void tile_step(WaveState<QB>& st, const uint16_t* kl,
       for (int kb = 0; kb < 2; ++kb) {
         const int key = kb * 32 + kperm;
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kl + lds_off(key, 2 * ks + g));
+        for (int ks = 0; ks < D / 16; ++ks) {
+          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kl + lds_off<D>(key, 2 * ks + g));
           sx[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, st.q[qb][ks], ks == 0 ? (f32x16){} : sx[kb], 0, 0, 0);
         }
       }
@@ -662,7 +694,7 @@ __device__ __forceinline__ void tile_step(WaveState<QB>& st, const uint16_t* kl,
         const float alpha = __builtin_amdgcn_exp2f((st.m[qb] - mnew) * c2);
         st.l[qb] *= alpha;
 #pragma unroll
-        for (int db = 0; db < 2; ++db)
+        for (int db = 0; db < D / 32; ++db)
 #pragma unroll
           for (int i = 0; i < 16; ++i) st.o[qb][db][i] *= alpha;
         st.m[qb] = mnew;
@@ -708,11 +740,11 @@ __device__ __forceinline__ void tile_step(WaveState<QB>& st, const uint16_t* kl,
     for (int mm = 0; mm < 2; ++mm) {
       const int key = kb * 32 + 16 * g + 8 * mm + (li >> 2);
 #pragma unroll
-      for (int db = 0; db < 2; ++db) {
+      for (int db = 0; db < D / 32; ++db) {
         const int col = db * 32 + dc0 + 4 * (li & 3);
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vl3 + lds_off(key, col >> 3) + (col & 4)));
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vl3 + lds_off<D>(key, col >> 3) + (col & 4)));
         const s16x4 hi =
-            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vl3 + lds_off(key + 4, col >> 3) + (col & 4)));
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vl3 + lds_off<D>(key + 4, col >> 3) + (col & 4)));
         const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
@@ -722,8 +754,8 @@ __device__ __forceinline__ void tile_step(WaveState<QB>& st, const uint16_t* kl,
   }
 }
 
-template <int QB>
-__device__ __forceinline__ void store_lse_img(const AttnArgs& a, const WaveState<QB>& st, int h, const int (&row)[QB],
+template <int QB, int D>
+__device__ __forceinline__ void store_lse_img(const AttnArgs& a, const WaveState<QB, D>& st, int h, const int (&row)[QB],
                                               const bool (&valid)[QB], int g) {
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
@@ -733,19 +765,20 @@ __device__ __forceinline__ void store_lse_img(const AttnArgs& a, const WaveState
   }
 }
 
-template <bool GATHER, int QB, bool EXACT_SUM, int KM, int KS>
+template <bool GATHER, int QB, bool EXACT_SUM, int KM, int KS, int D>
 __global__ __launch_bounds__(kThreads * KS) __attribute__((amdgpu_waves_per_eu(2))) void k_attn_mfma(AttnArgs a) {
   static_assert(KS == 1 || (KS == 2 && !EXACT_SUM && KM == 0), "key halves only on the mask-free fast path");
+  static_assert(D == 64 || D == 128, "head dim 64 or 128");
   constexpr int kRowsW = 32 * QB;
   constexpr int kBM = kWaves * kRowsW;
   // Two LDS buffers as distinct objects: every read and every DMA target below names one of them
   // statically, so the compiler can see that the prefetch into one never aliases reads of the other
   // and does not wait for the prefetch before computing.  With KS = 2 each key half of the workgroup
   // has its own pair.
-  __shared__ __attribute__((aligned(16))) uint16_t k_as[KS][kTileElems];
-  __shared__ __attribute__((aligned(16))) uint16_t v_as[KS][kTileElems];
-  __shared__ __attribute__((aligned(16))) uint16_t k_bs[KS][kTileElems];
-  __shared__ __attribute__((aligned(16))) uint16_t v_bs[KS][kTileElems];
+  __shared__ __attribute__((aligned(16))) uint16_t k_as[KS][kTileElems<D>];
+  __shared__ __attribute__((aligned(16))) uint16_t v_as[KS][kTileElems<D>];
+  __shared__ __attribute__((aligned(16))) uint16_t k_bs[KS][kTileElems<D>];
+  __shared__ __attribute__((aligned(16))) uint16_t v_bs[KS][kTileElems<D>];
   // key half of this wave (KS = 2: waves 0-3 take the first half of the key tiles, waves 4-7 the rest)
   const int half = KS == 1 ? 0 : __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 8));
   uint16_t* const k_a = k_as[half];
@@ -771,7 +804,7 @@ __global__ __launch_bounds__(kThreads * KS) __attribute__((amdgpu_waves_per_eu(2
 
   int row[QB];
   bool valid[QB];
-  WaveState<QB> st;
+  WaveState<QB, D> st;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int r = qt * kBM + w * kRowsW + qb * 32 + qi;
@@ -780,11 +813,11 @@ __global__ __launch_bounds__(kThreads * KS) __attribute__((amdgpu_waves_per_eu(2
     valid[qb] = active && rr >= 0 && rr < a.N;
     row[qb] = valid[qb] ? rr : 0;
     const bf16x8* qp =
-        reinterpret_cast<const bf16x8*>(static_cast<const uint16_t*>(a.q) + (bh * a.N + row[qb]) * kD);
+        reinterpret_cast<const bf16x8*>(static_cast<const uint16_t*>(a.q) + (bh * a.N + row[qb]) * D);
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) st.q[qb][ks] = qp[2 * ks + g];
+    for (int ks = 0; ks < D / 16; ++ks) st.q[qb][ks] = qp[2 * ks + g];
 #pragma unroll
-    for (int db = 0; db < 2; ++db)
+    for (int db = 0; db < D / 32; ++db)
 #pragma unroll
       for (int i = 0; i < 16; ++i) st.o[qb][db][i] = 0.f;
     st.m[qb] = -INFINITY;
@@ -807,11 +840,11 @@ __global__ __launch_bounds__(kThreads * KS) __attribute__((amdgpu_waves_per_eu(2
   // the warmup emission only runs on the exact-sum path (the host picks it whenever an output asks for it)
   const bool emit = EXACT_SUM && b == 0 && (a.xattn_out != nullptr || a.lse_img_out != nullptr);
   const float c2 = a.scale * kLog2e;
-  if constexpr (!EXACT_SUM) {
+  if constexpr (!EXACT_SUM && D == 64) {  // the fast path's pre-scaled Q (head dim 64 only)
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
+      for (int ks = 0; ks < D / 16; ++ks) {
         const f32x8 qf = __builtin_convertvector(st.q[qb][ks], f32x8) * c2;
         st.q[qb][ks] = __builtin_convertvector(qf, bf16x8);
       }
@@ -839,7 +872,7 @@ __global__ __launch_bounds__(kThreads * KS) __attribute__((amdgpu_waves_per_eu(2
   MaskTile<KM> mcur, mnext;
   mask_fetch(mcur, 0);
 
-  if (t_begin < t_end) stage_issue<(QB > 1)>(tile_src(a, bh, t_begin, n_img, tv), k_a, v_a);
+  if (t_begin < t_end) stage_issue<D, (QB > 1)>(tile_src<D>(a, bh, t_begin, n_img, tv), k_a, v_a);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
@@ -848,10 +881,10 @@ __global__ __launch_bounds__(kThreads * KS) __attribute__((amdgpu_waves_per_eu(2
   // prefetch and synchronise.
   auto full_tile = [&](int t, const uint16_t* ck, const uint16_t* cv, uint16_t* nk, uint16_t* nv) {
     if (t + 1 < t_end) {
-      stage_issue<(QB > 1)>(tile_src(a, bh, t + 1, n_img, tv), nk, nv);
+      stage_issue<D, (QB > 1)>(tile_src<D>(a, bh, t + 1, n_img, tv), nk, nv);
       mask_fetch(mnext, t + 1);
     }
-    tile_step<QB, false, EXACT_SUM, KM>(st, ck, cv, kperm, g, li, dc0, c2, kBN, no_store, a.scale, mcur);
+    tile_step<QB, false, EXACT_SUM, KM, D>(st, ck, cv, kperm, g, li, dc0, c2, kBN, no_store, a.scale, mcur);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if constexpr (KM != 0) mcur = mnext;
@@ -859,7 +892,7 @@ __global__ __launch_bounds__(kThreads * KS) __attribute__((amdgpu_waves_per_eu(2
   auto masked_tile = [&](int t, const uint16_t* ck, const uint16_t* cv, uint16_t* nk, uint16_t* nv) {
     if (emit && t == n_img && a.lse_img_out != nullptr) store_lse_img(a, st, h, row, valid, g);
     if (t + 1 < t_end) {
-      stage_issue<(QB > 1)>(tile_src(a, bh, t + 1, n_img, tv), nk, nv);
+      stage_issue<D, (QB > 1)>(tile_src<D>(a, bh, t + 1, n_img, tv), nk, nv);
       mask_fetch(mnext, t + 1);
     }
     const bool txt = t >= n_img;
@@ -870,7 +903,7 @@ __global__ __launch_bounds__(kThreads * KS) __attribute__((amdgpu_waves_per_eu(2
       xo[qb] = (emit && txt && a.xattn_out != nullptr && valid[qb])
                    ? a.xattn_out + (static_cast<size_t>(h) * a.N + row[qb]) * a.T + (t - n_img) * kBN
                    : nullptr;
-    tile_step<QB, true, EXACT_SUM, KM>(st, ck, cv, kperm, g, li, dc0, c2, nvalid, xo, a.scale, mcur);
+    tile_step<QB, true, EXACT_SUM, KM, D>(st, ck, cv, kperm, g, li, dc0, c2, nvalid, xo, a.scale, mcur);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if constexpr (KM != 0) mcur = mnext;
@@ -898,18 +931,21 @@ __global__ __launch_bounds__(kThreads * KS) __attribute__((amdgpu_waves_per_eu(2
     for (int i = 0; i < pad; ++i) __syncthreads();
     // merge the second key half into the first through LDS (the tile buffers are idle now): per query
     // block, the partner wave's running max, row sum and output accumulators, each lane with the
-    // lane of the same index (same rows, same register layout)
-    float* const xo0 = reinterpret_cast<float*>(&k_as[0][0]);  // [4 waves][16][64]
-    float* const xo1 = reinterpret_cast<float*>(&v_as[0][0]);
+    // lane of the same index (same rows, same register layout).  The first half of the accumulator
+    // blocks goes to k_as, the second to v_as: block db of wave w at floats [((db % nb) * 4 + w) * 16 + i][64]
+    // of its array, nb = D / 64 blocks per array (each array holds exactly that); max and sum go to k_bs.
+    constexpr int nb = D / 64;
+    static_assert(sizeof(k_as) == sizeof(float) * nb * 4 * 16 * 64 && sizeof(v_as) == sizeof(k_as), "merge area");
+    float* const xk = reinterpret_cast<float*>(&k_as[0][0]);
+    float* const xv = reinterpret_cast<float*>(&v_as[0][0]);
     float* const xml = reinterpret_cast<float*>(&k_bs[0][0]);  // [4 waves][2][64]
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       if (half == 1) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          xo0[(w * 16 + i) * 64 + L] = st.o[qb][0][i];
-          xo1[(w * 16 + i) * 64 + L] = st.o[qb][1][i];
-        }
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) (db < nb ? xk : xv)[(((db % nb) * 4 + w) * 16 + i) * 64 + L] = st.o[qb][db][i];
         xml[(w * 2 + 0) * 64 + L] = st.m[qb];
         xml[(w * 2 + 1) * 64 + L] = st.l[qb];
       }
@@ -923,10 +959,10 @@ __global__ __launch_bounds__(kThreads * KS) __attribute__((amdgpu_waves_per_eu(2
         st.m[qb] = mm;
         st.l[qb] = a0 * st.l[qb] + a1 * l1;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          st.o[qb][0][i] = a0 * st.o[qb][0][i] + a1 * xo0[(w * 16 + i) * 64 + L];
-          st.o[qb][1][i] = a0 * st.o[qb][1][i] + a1 * xo1[(w * 16 + i) * 64 + L];
-        }
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            st.o[qb][db][i] = a0 * st.o[qb][db][i] + a1 * (db < nb ? xk : xv)[(((db % nb) * 4 + w) * 16 + i) * 64 + L];
       }
       __syncthreads();
     }
@@ -939,9 +975,9 @@ __global__ __launch_bounds__(kThreads * KS) __attribute__((amdgpu_waves_per_eu(2
     const float lt = st.l[qb] + swap_halves(st.l[qb]);
     if (!valid[qb]) continue;
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    uint16_t* orow = static_cast<uint16_t*>(a.out) + (bh * a.N + row[qb]) * kD;
+    uint16_t* orow = static_cast<uint16_t*>(a.out) + (bh * a.N + row[qb]) * D;
 #pragma unroll
-    for (int db = 0; db < 2; ++db)
+    for (int db = 0; db < D / 32; ++db)
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const int dc = db * 32 + 8 * rr + 4 * g;
@@ -954,27 +990,27 @@ __global__ __launch_bounds__(kThreads * KS) __attribute__((amdgpu_waves_per_eu(2
   }
 }
 
-template <bool GATHER, int QB, bool EXACT_SUM, int KM, int KS = 1>
+template <bool GATHER, int QB, bool EXACT_SUM, int KM, int D, int KS = 1>
 static void launch(const AttnArgs& a, hipStream_t s) {
   constexpr int kBM = kWaves * 32 * QB;
   const int nqt = (a.R + kBM - 1) / kBM;
   const uint32_t grid = static_cast<uint32_t>(a.B) * a.H * nqt;
-  k_attn_mfma<GATHER, QB, EXACT_SUM, KM, KS><<<grid, kThreads * KS, 0, s>>>(a);
+  k_attn_mfma<GATHER, QB, EXACT_SUM, KM, KS, D><<<grid, kThreads * KS, 0, s>>>(a);
 }
 
-template <bool GATHER, int QB, int KM>
+template <bool GATHER, int QB, int KM, int D>
 static void launch_sum(const AttnArgs& a, hipStream_t s) {
   const bool exact = a.lse != nullptr || a.lse_img_out != nullptr || a.xattn_out != nullptr;
-  if (exact) launch<GATHER, QB, true, KM>(a, s);
-  else launch<GATHER, QB, false, KM>(a, s);
+  if (exact) launch<GATHER, QB, true, KM, D>(a, s);
+  else launch<GATHER, QB, false, KM, D>(a, s);
 }
 
 template <bool GATHER>
-static void launch_rows(const AttnArgs& a, hipStream_t s) {
+static void launch_rows64(const AttnArgs& a, hipStream_t s) {
   if (a.mask != nullptr) {
     // kept mask: one query block per wave (the per-lane mask chunks need the registers of the second)
-    if (a.mask_dtype == SAFE_DTYPE_BOOL) launch_sum<GATHER, 1, 1>(a, s);
-    else launch_sum<GATHER, 1, 2>(a, s);
+    if (a.mask_dtype == SAFE_DTYPE_BOOL) launch_sum<GATHER, 1, 1, 64>(a, s);
+    else launch_sum<GATHER, 1, 2, 64>(a, s);
     return;
   }
   // Work shape by the number of two-block waves w2 against the GPU's 2048 wave slots (thresholds from
@@ -988,16 +1024,39 @@ static void launch_rows(const AttnArgs& a, hipStream_t s) {
   // one round over the 256 CUs.)
   const double waves_qb2 = static_cast<double>(a.B) * a.H * ((a.R + 63) / 64);
   const bool exact = a.lse != nullptr || a.lse_img_out != nullptr || a.xattn_out != nullptr;
-  if (waves_qb2 >= 2048.0) launch_sum<GATHER, 2, 0>(a, s);
-  else if (exact || waves_qb2 > 1024.0) launch_sum<GATHER, 1, 0>(a, s);
-  else if (waves_qb2 >= 512.0) launch<GATHER, 2, false, 0, 2>(a, s);
-  else launch<GATHER, 1, false, 0, 2>(a, s);
+  if (waves_qb2 >= 2048.0) launch_sum<GATHER, 2, 0, 64>(a, s);
+  else if (exact || waves_qb2 > 1024.0) launch_sum<GATHER, 1, 0, 64>(a, s);
+  else if (waves_qb2 >= 512.0) launch<GATHER, 2, false, 0, 64, 2>(a, s);
+  else launch<GATHER, 1, false, 0, 64, 2>(a, s);
 }
 
-hipError_t launch_attn_mfma_bf16(const AttnArgs& a, hipStream_t s) {
+// Head dim 128: one query block per wave throughout (the Q operand and the output accumulators of one
+// block already take twice the registers of a block at head dim 64); the key range is split in two
+// while the one-block waves do not fill the GPU's 2048 wave slots.
+// A kept fp32 mask at head dim 128 is not taken here (its per-lane mask chunks do not fit beside the
+// accumulators); the caller routes it to the generic kernel.
+template <bool GATHER>
+static void launch_rows128(const AttnArgs& a, hipStream_t s) {
+  if (a.mask != nullptr) {
+    launch_sum<GATHER, 1, 1, 128>(a, s);
+    return;
+  }
+  const double waves_qb1 = static_cast<double>(a.B) * a.H * ((a.R + 31) / 32);
+  const bool exact = a.lse != nullptr || a.lse_img_out != nullptr || a.xattn_out != nullptr;
+  if (exact || waves_qb1 >= 2048.0) launch_sum<GATHER, 1, 0, 128>(a, s);
+  else launch<GATHER, 1, false, 0, 128, 2>(a, s);
+}
+
+hipError_t launch_attn_mfma_bf16(const AttnArgs& a, int d, hipStream_t s) {
   if (a.R == 0) return hipSuccess;
-  if (a.rows != nullptr) launch_rows<true>(a, s);
-  else launch_rows<false>(a, s);
+  if (d == 128 && a.mask != nullptr && a.mask_dtype != SAFE_DTYPE_BOOL) return hipErrorInvalidValue;
+  if (d == 128) {
+    if (a.rows != nullptr) launch_rows128<true>(a, s);
+    else launch_rows128<false>(a, s);
+  } else {
+    if (a.rows != nullptr) launch_rows64<true>(a, s);
+    else launch_rows64<false>(a, s);
+  }
   return hipGetLastError();
 }
 

@@ -5,8 +5,8 @@
 namespace safe {
 
 // Launchers (each returns a HIP error code; validation happens before they are called).
-hipError_t launch_attn_mfma_bf16(const AttnArgs& a, hipStream_t s);
-hipError_t launch_attn_generic(const AttnArgs& a, int dtype, hipStream_t s);
+hipError_t launch_attn_mfma_bf16(const AttnArgs& a, int d, hipStream_t s);
+hipError_t launch_attn_generic(const AttnArgs& a, int dtype, int d, hipStream_t s);
 hipError_t launch_mask_check(const void* mask, int mask_dtype, int mB, int mH, int N, int cols, int T,
                              const int32_t* tv, int B, int32_t* flag, float* c_out, hipStream_t s);
 hipError_t launch_pcsp_accumulate(const float* x, const float* lse_img, int H, int N, int T, int Tv, int c0, int c1,

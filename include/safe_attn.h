@@ -40,7 +40,7 @@ enum {
   SAFE_ERR_DTYPE = 3,       /* unknown dtype code */
   SAFE_ERR_RANGE = 4,       /* k > N, Tv > T, c0 > c1, ... */
   SAFE_ERR_WORKSPACE = 5,   /* a workspace is missing or too small */
-  SAFE_ERR_UNSUPPORTED = 6, /* valid request the library does not implement (e.g. d != 64) */
+  SAFE_ERR_UNSUPPORTED = 6, /* valid request the library does not implement (e.g. d not 64 or 128) */
   SAFE_ERR_HIP = 7,         /* a HIP runtime call failed */
   SAFE_ERR_ALIGN = 8        /* a pointer lacks the alignment stated for it */
 };
@@ -63,7 +63,8 @@ enum {
  * is -inf (possible only with a mask) gets o_i = 0 and lse_i = -inf.
  *
  * dtype           SAFE_DTYPE_BF16 or SAFE_DTYPE_F32, for q, k_*, v_*, out.
- * B, H, N, T, d   1 <= B <= SAFE_MAX_BATCH, H >= 1, N >= 1, T >= 0, d == 64.
+ * B, H, N, T, d   1 <= B <= SAFE_MAX_BATCH, H >= 1, N >= 1, T >= 0, d == 64 or d == 128 (the head
+ *                 dims of the DiT backbones the pages evaluate across; other values: SAFE_ERR_UNSUPPORTED).
  * text_valid_len  HOST array [B], 0 <= Tv[b] <= T.
  * scale           logit scale; 0 selects 1/sqrt(d).
  * mask            NULL (the mask-free fast path; use it after elision), or a kept additive mask

@@ -105,6 +105,8 @@ WORKLOADS: Dict[str, Workload] = {
     # 2560^2 latent, 160x160 tokens, |S| = 20%.
     "srsu_2560": Workload("srsu_2560", "bf16", 2, 24, 25600, 160, 256, _tv(2, 120), 64, 5120, 4, 0.125,
                           n_blobs=5),
+    # 1024^2 latent at head dim 128 (24 heads x 128, the width of the d = 128 DiT backbones), dense anchor step.
+    "dense_1024_d128": Workload("dense_1024_d128", "bf16", 2, 24, 4096, 64, 256, _tv(2, 77), 128, 1229, 6, 0.125),
     # 3072^2 latent, 192x192 tokens, 10-step trajectory after a 2-step warmup.
     "traj_3072": Workload("traj_3072", "bf16", 2, 24, 36864, 192, 256, _tv(2, 200), 64, 7373, 5, 0.125,
                           n_blobs=5, latent=(16, 384, 384), g_ctx=2.5, g_sens=7.0,

@@ -28,7 +28,7 @@ def test_library_loads_and_exports_every_symbol():
     lib = dts.load()
     for name in _declared():
         assert hasattr(lib, name), name
-    assert lib.safe_version() == 200
+    assert lib.safe_version() == 210
     for code, name in [(0, b"SAFE_OK"), (2, b"SAFE_ERR_SHAPE"), (8, b"SAFE_ERR_ALIGN"), (99, b"SAFE_ERR_UNKNOWN")]:
         assert lib.safe_status_string(code) == name
 
@@ -57,7 +57,7 @@ def _desc(**kw):
 
 @pytest.mark.parametrize("kw,code", [
     ({"dtype": 5}, DTYPE), ({"B": 0}, SHAPE), ({"N": 0}, SHAPE), ({"T": -1}, SHAPE), ({"d": 32}, UNSUP),
-    ({"d": 128}, UNSUP), ({"B": 65}, UNSUP), ({"q": None}, NULL), ({"out": None}, NULL),
+    ({"d": 96}, UNSUP), ({"d": 256}, UNSUP), ({"B": 65}, UNSUP), ({"q": None}, NULL), ({"out": None}, NULL),
     ({"tv": (77, 257)}, RANGE), ({"tv": (-1, 0)}, RANGE), ({"q": 0x10008}, ALIGN),
     ({"mask": 0x20000, "mask_dtype": 0, "mask_B": 1, "mask_H": 1, "mask_cols": 128}, DTYPE),
     ({"mask": 0x20000, "mask_dtype": 1, "mask_B": 3, "mask_H": 1, "mask_cols": 128}, SHAPE),
