@@ -40,6 +40,18 @@ def test_matches_torch_sdpa(tv):
     assert np.max(np.abs(o - ref)) < 1e-12
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_matches_torch_sdpa_at_the_library_head_dims(d):
+    """The default scale 1/sqrt(d) and the full-width dot products at both head dims the library takes."""
+    q, ki, vi, kt, vt = _inputs(B=1, H=2, N=40, T=9, d=d, seed=d, std=0.3)
+    o, lse = A.attention(q, ki, vi, kt, vt, (6,))
+    ref = _sdpa(q, ki, vi, kt, vt, (6,))
+    assert np.max(np.abs(o - ref)) < 1e-12
+    keys = np.concatenate([ki, kt[:, :, :6]], axis=2)
+    ref_lse = logsumexp(np.einsum("bhnd,bhmd->bhnm", q, keys) / math.sqrt(d), axis=-1)
+    assert np.max(np.abs(lse - ref_lse)) < 1e-12
+
+
 def test_matches_torch_sdpa_with_per_head_mask():
     q, ki, vi, kt, vt = _inputs()
     r = np.random.default_rng(5)
