@@ -121,3 +121,26 @@ def test_full_size_block_products(lib, name):
         mx, rel = err(host(g)[:, :, rows], rf[:, :, rows])
         print(f"{name} QKV: max-abs {mx:.3e}, rel-L2 {rel:.3e}")
         assert mx <= BF16_MAX_ABS and rel <= BF16_REL_L2
+
+
+def test_rows_ffn_many_tokens(lib):
+    """5632 gathered tokens (more token tiles than the GPU has CUs, in both products) with F = 2048: sampled
+    rows against the oracle, and every context row untouched."""
+    B, N, H, d, k = 2, 3000, 24, 64, 2816
+    p = _inputs(B, N, H, d, k, seed=77, ffn_mult=4)
+    F = 2048  # D -> F on 256 x 256 tiles, F -> D on 128 x 128 tiles
+    r = np.random.default_rng(78)
+    D = p["D"]
+    p["F"] = F
+    p["w1"] = syn.round_to_bf16((r.standard_normal((F, D)) / np.sqrt(D)).astype(np.float32))
+    p["w2"] = syn.round_to_bf16((r.standard_normal((D, F)) / np.sqrt(F)).astype(np.float32))
+    p["b1"] = (0.02 * r.standard_normal(F)).astype(np.float32)
+    cache0 = syn.round_to_bf16(r.standard_normal((B, N, D)).astype(np.float32))
+    got = _ffn(lib, p, cache0)
+    rows = p["rows"]
+    pick = rows[syn.sample_rows(len(rows), 48, seed=5)]
+    ref = SB.rows_ffn(p["x"], pick, p["w1"], p["b1"], p["w2"], p["b2"], cache0)
+    mx, rel = err(got[:, pick], ref[:, pick])
+    assert mx <= BF16_MAX_ABS and rel <= BF16_REL_L2, (mx, rel)
+    other = np.setdiff1d(np.arange(N), rows)
+    assert np.array_equal(got[:, other], cache0[:, other].astype(np.float64))
