@@ -136,6 +136,39 @@ __device__ __forceinline__ void stage_issue(const TileSrc& s, uint16_t* kl, uint
   }
 }
 
+// Copies of a full tile (all 64 keys valid, no clamping): the per-lane byte offset of each copy
+// instruction's chunk within the tile does not depend on the tile, so it is computed once (off[u]) and
+// added to the tile's uniform base, which lets the copy take a scalar base and a 32-bit vector offset
+// instead of a 64-bit address computed per tile.
+template <int D>
+__device__ __forceinline__ void stage_offsets(uint32_t (&off)[D / 32]) {
+  constexpr int kChunks = D / 8;
+  constexpr int kChunkShift = D == 64 ? 3 : 4;
+#pragma unroll
+  for (int u = 0; u < D / 32; ++u) {
+    const int p = u * kWaves * 64 + static_cast<int>(threadIdx.x & 255);
+    const int row = p >> kChunkShift;
+    const int c = (p & (kChunks - 1)) ^ swz<D>(row);
+    off[u] = static_cast<uint32_t>((row * D + c * 8) * 2);
+  }
+}
+
+template <int D, bool OPAQUE>
+__device__ __forceinline__ void stage_issue_full(const TileSrc& s, uint16_t* kl, uint16_t* vl, const uint32_t (&off)[D / 32]) {
+  int wslot = __builtin_amdgcn_readfirstlane(static_cast<int>((threadIdx.x >> 6) & 3)) * 64;
+  if (OPAQUE) asm volatile("" : "+s"(wslot));
+  const char* kb = reinterpret_cast<const char*>(s.k);
+  const char* vb = reinterpret_cast<const char*>(s.v);
+#pragma unroll
+  for (int u = 0; u < D / 32; ++u) {
+    const int base = u * kWaves * 64 + wslot;
+    __builtin_amdgcn_global_load_lds(static_cast<const void*>(kb + off[u]),
+                                     (__attribute__((address_space(3))) void*)(kl + base * 8), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(static_cast<const void*>(vb + off[u]),
+                                     (__attribute__((address_space(3))) void*)(vl + base * 8), 16, 0, 0);
+  }
+}
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   const bf16x2 v = __builtin_convertvector((f32x2){a, b}, bf16x2);
   return __builtin_bit_cast(uint32_t, v);
@@ -879,9 +912,12 @@ __global__ __launch_bounds__(kThreads * KS) __attribute__((amdgpu_waves_per_eu(2
   float* const no_store[QB] = {};
   // One tile: prefetch tile t+1 into the other buffer, compute on this one, then wait for the
   // prefetch and synchronise.
+  uint32_t coff[D / 32];
+  stage_offsets<D>(coff);
   auto full_tile = [&](int t, const uint16_t* ck, const uint16_t* cv, uint16_t* nk, uint16_t* nv) {
     if (t + 1 < t_end) {
-      stage_issue<D, (QB > 1)>(tile_src<D>(a, bh, t + 1, n_img, tv), nk, nv);
+      if (t + 1 < n_full) stage_issue_full<D, (QB > 1)>(tile_src<D>(a, bh, t + 1, n_img, tv), nk, nv, coff);
+      else stage_issue<D, (QB > 1)>(tile_src<D>(a, bh, t + 1, n_img, tv), nk, nv);
       mask_fetch(mnext, t + 1);
     }
     tile_step<QB, false, EXACT_SUM, KM, D>(st, ck, cv, kperm, g, li, dc0, c2, kBN, no_store, a.scale, mcur);
