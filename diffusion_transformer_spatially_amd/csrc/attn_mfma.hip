@@ -822,8 +822,20 @@ __global__ __launch_bounds__(kThreads * KS) __attribute__((amdgpu_waves_per_eu(2
   const int nqt = (a.R + kBM - 1) / kBM;
   const uint32_t G = static_cast<uint32_t>(a.B) * a.H * nqt;
   const uint32_t lid = xcd_remap(blockIdx.x, G);
-  const int bhi = static_cast<int>(lid / nqt);
-  const int qt = static_cast<int>(lid - static_cast<uint32_t>(bhi) * nqt);
+  // Workgroup order: the query tiles of one (b,h) in a row (they share K / V in L2), except with a kept fp32
+  // mask shared by the heads: there the mask stream dominates, so groups of G heads take one query tile
+  // together (each mask block read once per group), then the next tile (2560^2: 19.1 -> 17.0 ms).
+  int bhi, qt;
+  const int hgroup = (KM != 2 || a.mask_H != 1) ? 1 : a.H % 12 == 0 ? 12 : a.H % 8 == 0 ? 8 : a.H % 4 == 0 ? 4 : 1;
+  if (hgroup > 1) {
+    const uint32_t per_group = static_cast<uint32_t>(nqt) * static_cast<uint32_t>(hgroup);
+    const uint32_t grp = lid / per_group, rem = lid - grp * per_group;
+    qt = static_cast<int>(rem / static_cast<uint32_t>(hgroup));
+    bhi = static_cast<int>(grp * hgroup + (rem - static_cast<uint32_t>(qt) * hgroup));
+  } else {
+    bhi = static_cast<int>(lid / nqt);
+    qt = static_cast<int>(lid - static_cast<uint32_t>(bhi) * nqt);
+  }
   const size_t bh = static_cast<size_t>(bhi);
   const int b = bhi / a.H, h = bhi - b * a.H;
   const int tv = a.tv[b];
