@@ -14,12 +14,14 @@
 //  * wide products (D -> F, QKV): 256 features x 256 tokens per 8-wave workgroup (one per CU, two waves per
 //    SIMD), each wave 128 x 64 (4 x 2 blocks of 32 x 32): 128 flop per byte loaded, 6 KB of LDS reads per
 //    8 matrix instructions; narrow products (F -> D): 128 x 128 per 4-wave workgroup (enough workgroups to
-//    fill the GPU); K streams in stages of 64 through double-buffered LDS (two distinct objects per operand)
-//    filled by direct global -> LDS copies, which are pinned ahead of the stage's matrix work; within a
-//    stage the operands of K step ks + 1 are read while the matrix instructions of step ks run;
-//  * LDS rows of 128 bytes, 16-byte chunks XOR-swizzled per operand: weight rows are read 16 permuted rows
-//    at a time, token rows 16 consecutive rows at a time, and each pattern has its own swizzle, so neither
-//    read conflicts (SQ_LDS_BANK_CONFLICT = 0);
+//    fill the GPU); K streams through double-buffered LDS (two distinct objects per operand) filled by
+//    direct global -> LDS copies, which are pinned ahead of the stage's matrix work, in stages of 64 on the
+//    wide products and of 128 on the narrow ones (one 4-wave workgroup per CU with 128 KB of LDS: twice the
+//    matrix work per barrier, enough to cover the next stage's copy); within a stage the operands of K step
+//    ks + 1 are read while the matrix instructions of step ks run;
+//  * LDS rows of 128 bytes (stages of 64) or 256 bytes (stages of 128), 16-byte chunks XOR-swizzled per
+//    operand: weight rows are read 16 permuted rows at a time, token rows 16 consecutive rows at a time, and
+//    each pattern has its own swizzle, so neither read conflicts;
 //  * input rows: gathered through S from token-major hidden states [B, N, Din] (token t = b k + r reads
 //    row S[r] of batch b), or packed [T, Din];
 //  * output rows: packed [T, Dout], scattered to row S[r] of [B, N, Dout] (the FFN cache: context rows
@@ -50,6 +52,13 @@ __device__ __forceinline__ int gswz_w(int row) { return (((row >> 1) & 1) << 2) 
 __device__ __forceinline__ int gswz_x(int row) { return (((row >> 1) & 1) << 2) | (((row >> 2) & 1) << 1) | ((row >> 3) & 1); }
 __device__ __forceinline__ int goff_w(int row, int chunk) { return row * kKs + ((chunk ^ gswz_w(row)) << 3); }
 __device__ __forceinline__ int goff_x(int row, int chunk) { return row * kKs + ((chunk ^ gswz_x(row)) << 3); }
+
+// 256-byte rows (stages of 128 K elements, one row per bank window): weight reads (row bits 0, 1, 2, 4 vary
+// across 16 lanes) and token reads (row bits 0-3) each need an injective 4-bit XOR of the 16 chunks.
+__device__ __forceinline__ int gswz_w2(int r) { return ((r & 1) << 2) | (((r >> 1) & 1) << 3) | ((r >> 2) & 1) | (((r >> 4) & 1) << 1); }
+__device__ __forceinline__ int gswz_x2(int r) { return ((r & 1) << 2) | (((r >> 1) & 1) << 3) | ((r >> 2) & 1) | (((r >> 3) & 1) << 1); }
+__device__ __forceinline__ int goff_w2(int row, int chunk) { return row * 128 + ((chunk ^ gswz_w2(row)) << 3); }
+__device__ __forceinline__ int goff_x2(int row, int chunk) { return row * 128 + ((chunk ^ gswz_x2(row)) << 3); }
 
 __device__ __forceinline__ uint32_t pack2(float a, float b) {
   const bf16x2 v = __builtin_convertvector((f32x2){a, b}, bf16x2);
@@ -132,10 +141,11 @@ __device__ __forceinline__ void store16(const RowsGemmArgs& a, int t, int f0, co
 
 template <int IN, int OUT, bool GELU>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_rows_gemm(RowsGemmArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t w_a[kTileElems];
-  __shared__ __attribute__((aligned(16))) uint16_t w_b[kTileElems];
-  __shared__ __attribute__((aligned(16))) uint16_t x_a[kTileElems];
-  __shared__ __attribute__((aligned(16))) uint16_t x_b[kTileElems];
+  constexpr int kK2 = 128;  // K elements per stage: 256-byte rows of 16 chunks
+  __shared__ __attribute__((aligned(16))) uint16_t w_a[128 * kK2];
+  __shared__ __attribute__((aligned(16))) uint16_t w_b[128 * kK2];
+  __shared__ __attribute__((aligned(16))) uint16_t x_a[128 * kK2];
+  __shared__ __attribute__((aligned(16))) uint16_t x_b[128 * kK2];
 
   const int T = a.B * a.k;
   const int nt = (T + kTT - 1) / kTT;
@@ -153,14 +163,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 
   // Copy sources of this lane: slot p = u * 256 + threadIdx.x of a 128-row tile holds row p / 8, chunk
   // (p % 8) ^ swizzle(row).  Token rows past T are clamped to the last token (loaded, never stored).
-  const uint16_t* wsrc[4];
-  const uint16_t* xsrc[4];
+  const uint16_t* wsrc[8];
+  const uint16_t* xsrc[8];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
+  for (int u = 0; u < 8; ++u) {
     const int p = u * 256 + static_cast<int>(threadIdx.x);
-    const int row = p >> 3;
-    wsrc[u] = a.w + static_cast<size_t>(j0 + row) * a.Din + ((p & 7) ^ gswz_w(row)) * 8;
-    const int c = (p & 7) ^ gswz_x(row);
+    const int row = p >> 4;
+    wsrc[u] = a.w + static_cast<size_t>(j0 + row) * a.Din + ((p & 15) ^ gswz_w2(row)) * 8;
+    const int c = (p & 15) ^ gswz_x2(row);
     const int t = min(t0 + row, T - 1);
     size_t xr;
     if (IN == kInGather) {
@@ -173,9 +183,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     xsrc[u] = a.x + xr * a.Din + c * 8;
   }
   auto issue = [&](int s, uint16_t* wl, uint16_t* xl) {
-    const int k0 = s * kKs;
+    const int k0 = s * kK2;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < 8; ++u) {
       const int base = u * 256 + wave * 64;  // first slot of this wave instruction
       __builtin_amdgcn_global_load_lds(static_cast<const void*>(wsrc[u] + k0),
                                        (__attribute__((address_space(3))) void*)(wl + base * 8), 16, 0, 0);
@@ -197,14 +207,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     bf16x8 wa[2][2], xb[2][2];
     auto ld = [&](int ks, int slot) {
 #pragma unroll
-      for (int jb = 0; jb < 2; ++jb) wa[slot][jb] = *reinterpret_cast<const bf16x8*>(wl + goff_w(wj * 64 + jb * 32 + kperm, 2 * ks + g));
+      for (int jb = 0; jb < 2; ++jb) wa[slot][jb] = *reinterpret_cast<const bf16x8*>(wl + goff_w2(wj * 64 + jb * 32 + kperm, 2 * ks + g));
 #pragma unroll
-      for (int tb = 0; tb < 2; ++tb) xb[slot][tb] = *reinterpret_cast<const bf16x8*>(xl + goff_x(wt * 64 + tb * 32 + qi, 2 * ks + g));
+      for (int tb = 0; tb < 2; ++tb) xb[slot][tb] = *reinterpret_cast<const bf16x8*>(xl + goff_x2(wt * 64 + tb * 32 + qi, 2 * ks + g));
     };
     ld(0, 0);
 #pragma unroll
-    for (int ks = 0; ks < kKs / 16; ++ks) {
-      if (ks + 1 < kKs / 16) ld(ks + 1, (ks + 1) & 1);
+    for (int ks = 0; ks < kK2 / 16; ++ks) {
+      if (ks + 1 < kK2 / 16) ld(ks + 1, (ks + 1) & 1);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int jb = 0; jb < 2; ++jb)
@@ -215,7 +225,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     }
   };
 
-  const int ns = a.Din / kKs;
+  const int ns = a.Din / kK2;
   issue(0, w_a, x_a);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
