@@ -373,3 +373,23 @@ def test_bf16_kept_mask_full_size_sampled(lib):
                          rows=sample, mask=m)
     got = host(out)[:, :2][:, :, sample]
     assert_close(got, ro, "bf16", "1024^2 kept bool mask")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("H,k", [(3, 6), (24, 1229)])
+def test_rows_entries_outside_range_are_skipped(lib, d, H, k):
+    """Row entries outside [0, N) write nothing and every valid entry is computed (the contract of
+    safe_attn_rows), on the few-row and the many-row work shapes."""
+    w = syn.scaled(syn.WORKLOADS["srsu_1024"], B=2, H=H, N=1000 if H == 3 else 4096, T=256, tv=(77, 9), side=1,
+                   d=d)
+    inp = syn.attention_inputs(w)
+    r = np.random.default_rng(k + d)
+    valid = np.sort(r.choice(w.N, size=k - 4, replace=False)).astype(np.int32)
+    rows = np.concatenate([[-5, -1], valid, [w.N, w.N + 1000]]).astype(np.int32)
+    state = syn.initial_state(w)
+    o, _, _, _ = _run(lib, w, inp, rows=rows, state=state, want_lse=False)
+    C = np.setdiff1d(np.arange(w.N), valid)
+    assert np.array_equal(o[:, :, C], state[:, :, C].astype(np.float64))
+    pick = valid if len(valid) <= 64 else valid[syn.sample_rows(len(valid), 64, seed=d)]
+    ro, _ = _oracle(w, inp, rows=pick)
+    assert_close(o[:, :, pick], ro, "bf16", f"rows with out-of-range entries d={d} H={H}")
