@@ -926,10 +926,19 @@ __global__ __launch_bounds__(kThreads * KS) __attribute__((amdgpu_waves_per_eu(2
   // prefetch and synchronise.
   uint32_t coff[D / 32];
   stage_offsets<D>(coff);
+  // this (b,h)'s image K / V bases, opaque so that they stay in scalar registers instead of being reloaded
+  // from the kernel arguments (a scalar load and its wait) every tile
+  const uint16_t* kimg = static_cast<const uint16_t*>(a.k_img) + bh * a.N * D;
+  const uint16_t* vimg = static_cast<const uint16_t*>(a.v_img) + bh * a.N * D;
+  asm volatile("" : "+s"(kimg), "+s"(vimg));
   auto full_tile = [&](int t, const uint16_t* ck, const uint16_t* cv, uint16_t* nk, uint16_t* nv) {
     if (t + 1 < t_end) {
-      if (t + 1 < n_full) stage_issue_full<D, (QB > 1)>(tile_src<D>(a, bh, t + 1, n_img, tv), nk, nv, coff);
-      else stage_issue<D, (QB > 1)>(tile_src<D>(a, bh, t + 1, n_img, tv), nk, nv);
+      if (t + 1 < n_full) {
+        const TileSrc src{kimg + static_cast<size_t>(t + 1) * kBN * D, vimg + static_cast<size_t>(t + 1) * kBN * D, kBN};
+        stage_issue_full<D, (QB > 1)>(src, nk, nv, coff);
+      } else {
+        stage_issue<D, (QB > 1)>(tile_src<D>(a, bh, t + 1, n_img, tv), nk, nv);
+      }
       mask_fetch(mnext, t + 1);
     }
     tile_step<QB, false, EXACT_SUM, KM, D>(st, ck, cv, kperm, g, li, dc0, c2, kBN, no_store, a.scale, mcur);
