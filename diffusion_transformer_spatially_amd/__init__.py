@@ -323,20 +323,37 @@ class MaskPolicy:
     """Checks a supplied mask once (per tensor version) and drops it when it is provably redundant.
 
     Mirrors the exact fast-path rewrite: a removable mask goes to the mask-free kernels, any other mask
-    is kept and applied exactly.
+    is kept and applied exactly.  A cached verdict belongs to one live tensor: each entry holds a weak
+    reference to the mask it was computed for and is used only while that very tensor is alive and still
+    at the same version, storage address, shape and dtype (a freed mask's address is routinely handed to
+    the next allocation of the same size, whose version count starts again at zero).  Entries are dropped
+    when their tensor is garbage-collected, so the cache holds at most one entry per live mask and
+    argument set.
     """
 
     def __init__(self):
         self._cache = {}
         self._flag = None
 
+    def _evict(self, ident):
+        for key in [k for k in self._cache if k[0] == ident]:
+            del self._cache[key]
+
     def elide(self, mask, N: int, T: int, text_valid_len):
         if mask is None:
             return None
+        import weakref
         torch = _torch()
-        key = (mask.data_ptr(), mask._version, tuple(mask.shape), mask.dtype, tuple(int(t) for t in text_valid_len))
-        if key not in self._cache:
+        key = (id(mask), int(N), int(T), tuple(int(t) for t in text_valid_len))
+        stamp = (mask.data_ptr(), mask._version, tuple(mask.shape), mask.dtype)
+        hit = self._cache.get(key)
+        if hit is None or hit[0]() is not mask or hit[1] != stamp:
             if self._flag is None or self._flag.device != mask.device:
                 self._flag = torch.empty(1, dtype=torch.int32, device=mask.device)
-            self._cache[key] = safe_mask_is_row_constant(mask, N, T, text_valid_len, self._flag)
-        return None if self._cache[key] else mask
+            verdict = safe_mask_is_row_constant(mask, N, T, text_valid_len, self._flag)
+            ident = id(mask)
+            this = weakref.ref(self)
+            ref = weakref.ref(mask, lambda _r, ident=ident, this=this: this() is not None and this()._evict(ident))
+            self._cache[key] = (ref, stamp, verdict)
+            hit = self._cache[key]
+        return None if hit[2] else mask

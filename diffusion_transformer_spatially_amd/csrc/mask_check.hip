@@ -6,6 +6,7 @@
 // stop early (the verdict only ever moves from 1 to 0, so it stays deterministic).  With c_out
 // (k_mask_check) one workgroup per row also reports the row's constant.
 #include "common.hpp"
+#include "mask_span.hpp"
 
 #include <algorithm>
 
@@ -20,8 +21,25 @@ __device__ __forceinline__ float mask_value(const uint8_t* p, int dtype) {
 
 __global__ void k_flag_init(int32_t* flag) { *flag = 1; }
 
-__global__ __launch_bounds__(kMaskThreads) void k_mask_check(const uint8_t* __restrict__ mask, int dtype, int esize,
-                                                             int cols, int ncheck, int zero_required, int32_t* flag,
+// Block a of a row span [b0, hi) inside the mask buffer [buf_lo, buf_hi): one 16-byte load when the block
+// lies inside the buffer, else byte loads of the block's bytes inside the span only (the other bytes are
+// returned as 0 and are never tested).
+__device__ __forceinline__ uint4 load_block(uintptr_t a, uintptr_t buf_lo, uintptr_t buf_hi, uintptr_t b0,
+                                            uintptr_t hi) {
+  if (block_whole(a, buf_lo, buf_hi)) return *reinterpret_cast<const uint4*>(a);
+  uintptr_t r0, r1;
+  block_bytes(a, b0, hi, &r0, &r1);
+  uint32_t w[4] = {0u, 0u, 0u, 0u};
+  for (uintptr_t e = r0; e < r1; ++e) {
+    const uint32_t j = static_cast<uint32_t>(e - a);
+    w[j >> 2] |= static_cast<uint32_t>(*reinterpret_cast<const uint8_t*>(e)) << (8 * (j & 3));
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+__global__ __launch_bounds__(kMaskThreads) void k_mask_check(const uint8_t* __restrict__ mask, uintptr_t buf_lo,
+                                                             uintptr_t buf_hi, int dtype, int esize, int cols,
+                                                             int ncheck, int zero_required, int32_t* flag,
                                                              float* __restrict__ c_out, int early) {
   const uint32_t row = blockIdx.x;
   if (early && __atomic_load_n(flag, __ATOMIC_RELAXED) == 0) return;
@@ -30,12 +48,11 @@ __global__ __launch_bounds__(kMaskThreads) void k_mask_check(const uint8_t* __re
   bool ok = isfinite(first) && !(zero_required && first != 0.f);
   // Aligned 16-byte blocks covering [base, base + ncheck * esize).
   const uintptr_t b0 = reinterpret_cast<uintptr_t>(base);
-  const uintptr_t lo = b0 & ~static_cast<uintptr_t>(15);
   const uintptr_t hi = b0 + static_cast<uintptr_t>(ncheck) * esize;
-  const size_t nblk = (hi - lo + 15) / 16;
-  for (size_t blk = threadIdx.x; ok && blk < nblk; blk += kMaskThreads) {
-    const uintptr_t a = lo + blk * 16;
-    const uint4 v = *reinterpret_cast<const uint4*>(a);
+  const RowBlocks rb = row_blocks(b0, hi);
+  for (uint32_t blk = threadIdx.x; ok && blk < rb.n; blk += kMaskThreads) {
+    const uintptr_t a = rb.lo + static_cast<uintptr_t>(blk) * 16;
+    const uint4 v = load_block(a, buf_lo, buf_hi, b0, hi);
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
     if (dtype == SAFE_DTYPE_BOOL) {
 #pragma unroll
@@ -99,9 +116,9 @@ __device__ __forceinline__ bool block_ok(uint4 v, uintptr_t a, uintptr_t b0, uin
 
 constexpr int kScanRows = 4;
 
-__global__ __launch_bounds__(kMaskThreads) void k_mask_scan(const uint8_t* __restrict__ mask, int dtype, int esize,
-                                                            int cols, int nrows, int ncheck, int zero_required,
-                                                            int32_t* flag) {
+__global__ __launch_bounds__(kMaskThreads) void k_mask_scan(const uint8_t* __restrict__ mask, uintptr_t buf_lo,
+                                                            uintptr_t buf_hi, int dtype, int esize, int cols,
+                                                            int nrows, int ncheck, int zero_required, int32_t* flag) {
   bool ok = true;
   for (int r0 = blockIdx.x * kScanRows; r0 < nrows; r0 += gridDim.x * kScanRows) {
     if (__atomic_load_n(flag, __ATOMIC_RELAXED) == 0) return;
@@ -113,12 +130,11 @@ __global__ __launch_bounds__(kMaskThreads) void k_mask_scan(const uint8_t* __res
       const float first = mask_value(base, dtype);
       ok = ok && isfinite(first) && !(zero_required && first != 0.f);
       const uintptr_t b0 = reinterpret_cast<uintptr_t>(base);
-      const uintptr_t lo = b0 & ~static_cast<uintptr_t>(15);
       const uintptr_t hi = b0 + static_cast<uintptr_t>(ncheck) * esize;
-      const uint32_t nblk = static_cast<uint32_t>((hi - lo + 15) / 16);
-      for (uint32_t blk = threadIdx.x; blk < nblk; blk += kMaskThreads) {
-        const uintptr_t a = lo + static_cast<uintptr_t>(blk) * 16;
-        ok = block_ok(*reinterpret_cast<const uint4*>(a), a, b0, hi, dtype, first) && ok;
+      const RowBlocks rb = row_blocks(b0, hi);
+      for (uint32_t blk = threadIdx.x; blk < rb.n; blk += kMaskThreads) {
+        const uintptr_t a = rb.lo + static_cast<uintptr_t>(blk) * 16;
+        ok = block_ok(load_block(a, buf_lo, buf_hi, b0, hi), a, b0, hi, dtype, first) && ok;
       }
     }
   }
@@ -138,25 +154,28 @@ hipError_t launch_mask_check(const void* mask, int mask_dtype, int mB, int mH, i
   auto zero_of = [&](int tspan) { return (!full && tspan > 0) ? 1 : 0; };
   k_flag_init<<<1, 1, 0, s>>>(flag);
   const int early = c_out == nullptr ? 1 : 0;
+  // the whole mask buffer: no load leaves it
+  const uintptr_t buf_lo = reinterpret_cast<uintptr_t>(mask);
+  const uintptr_t buf_hi = buf_lo + static_cast<uintptr_t>(mB) * mH * N * static_cast<uintptr_t>(cols) * esize;
   if (c_out == nullptr) {
     const size_t slice_bytes = static_cast<size_t>(mH) * N * cols * esize;
     const int nrows = mH * N;
     const uint32_t grid = static_cast<uint32_t>(std::min<int64_t>((nrows + kScanRows - 1) / kScanRows, 2048));
     for (int b = 0; b < mB; ++b) {
       const int tspan = mB == 1 ? tmax_all : tv[b];
-      k_mask_scan<<<grid, kMaskThreads, 0, s>>>(static_cast<const uint8_t*>(mask) + b * slice_bytes, mask_dtype,
-                                                esize, cols, nrows, ncheck_of(tspan), zero_of(tspan), flag);
+      k_mask_scan<<<grid, kMaskThreads, 0, s>>>(static_cast<const uint8_t*>(mask) + b * slice_bytes, buf_lo, buf_hi,
+                                                mask_dtype, esize, cols, nrows, ncheck_of(tspan), zero_of(tspan), flag);
     }
   } else if (mB == 1) {
     const int nc = ncheck_of(tmax_all), z = zero_of(tmax_all);
     k_mask_check<<<static_cast<uint32_t>(mH) * N, kMaskThreads, 0, s>>>(
-        static_cast<const uint8_t*>(mask), mask_dtype, esize, cols, nc, z, flag, c_out, early);
+        static_cast<const uint8_t*>(mask), buf_lo, buf_hi, mask_dtype, esize, cols, nc, z, flag, c_out, early);
   } else {
     const size_t slice_bytes = static_cast<size_t>(mH) * N * cols * esize;
     for (int b = 0; b < mB; ++b) {
       const int nc = ncheck_of(tv[b]), z = zero_of(tv[b]);
       k_mask_check<<<static_cast<uint32_t>(mH) * N, kMaskThreads, 0, s>>>(
-          static_cast<const uint8_t*>(mask) + b * slice_bytes, mask_dtype, esize, cols, nc, z, flag,
+          static_cast<const uint8_t*>(mask) + b * slice_bytes, buf_lo, buf_hi, mask_dtype, esize, cols, nc, z, flag,
           c_out ? c_out + static_cast<size_t>(b) * mH * N : nullptr, early);
     }
   }

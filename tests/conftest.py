@@ -21,3 +21,23 @@ def lib():
     import diffusion_transformer_spatially_amd as dts
     dts.load()
     return dts
+
+
+def pytest_terminal_summary(terminalreporter):
+    """Worst-row errors of the parity assertions (the data behind the per-row bounds)."""
+    try:
+        from tests.gpu_util import ROW_STATS
+    except Exception:  # pragma: no cover
+        return
+    if not ROW_STATS:
+        return
+    for dt in ("bf16", "f32"):
+        st = sorted((s for s in ROW_STATS if s[1] == dt), key=lambda s: -s[2])
+        if st:
+            terminalreporter.write_line(f"worst rows ({dt}, {len(st)} assertions): " +
+                                        "; ".join(f"{w}: row {r:.2e} l2 {l:.2e}" for w, _, r, l in st[:6]))
+    path = os.environ.get("SAFE_ROW_STATS")
+    if path:
+        import json
+        with open(path, "w") as f:
+            json.dump(ROW_STATS, f)

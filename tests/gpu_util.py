@@ -10,6 +10,17 @@ F32_MAX_ABS = 1e-5
 F32_REL_L2 = 1e-5
 # fp32 CFG: |g - o| <= 1e-5 * (|eps_u| + |gamma| |eps_c - eps_u|), and relative L2 <= 1e-5.
 CFG_REL = 1e-5
+# Worst single output row (one query row of one (b, h)): ||o_row - ref_row|| / ||ref_row|| over the head
+# dimension.  The whole-tensor bounds above average over tens of thousands of rows, so on their own they
+# would let a few wholly wrong rows through (at the N(0,1)*0.125 workloads |o| stays below 1e-2, so the
+# max-abs bound cannot fail, and one zeroed row-head among 59k adds only ~4e-3 to the relative L2).
+# Bounds from the measured distribution of the worst row over every parity case (bf16: the largest
+# measured worst row, about 6e-3 on the sharply peaked stress rows and 4-5e-3 on the full-size launches,
+# times ~2.5; fp32: about 1e-6, times 20).  A row with a missing key tile, a wrong row index or a zero
+# output lands between 1e-1 and 1.
+BF16_ROW_REL = 1.5e-2
+F32_ROW_REL = 2e-5
+ROW_STATS = []  # (what, dtype, worst row, rel-L2) of every assert_close call, for the run's summary
 
 
 def torch():
@@ -41,13 +52,28 @@ def err(got: np.ndarray, ref: np.ndarray):
     return max_abs, rel
 
 
+def worst_row(got, ref) -> float:
+    """Largest relative L2 error of one row (last axis) of got against ref; a row whose reference is all
+    zero counts its absolute error (so it must come out exactly zero)."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    if got.size == 0:
+        return 0.0
+    d = np.linalg.norm((got - ref).reshape(-1, ref.shape[-1]), axis=1)
+    r = np.linalg.norm(ref.reshape(-1, ref.shape[-1]), axis=1)
+    return float(np.max(np.where(r > 0, d / np.where(r > 0, r, 1.0), d / 1e-300)))
+
+
 def assert_close(got, ref, dtype: str, what: str = ""):
+    """Both whole-tensor bounds and the worst-row bound (rows along the last axis)."""
     max_abs, rel = err(got, ref)
+    wr = worst_row(got, ref)
+    ROW_STATS.append((what, dtype, wr, rel))
     if dtype == "bf16":
-        ok = max_abs <= BF16_MAX_ABS and rel <= BF16_REL_L2
+        ok = max_abs <= BF16_MAX_ABS and rel <= BF16_REL_L2 and wr <= BF16_ROW_REL
     else:
-        ok = max_abs <= F32_MAX_ABS and rel <= F32_REL_L2
-    assert ok, f"{what}: max_abs={max_abs:.3e} rel_l2={rel:.3e} ({dtype})"
+        ok = max_abs <= F32_MAX_ABS and rel <= F32_REL_L2 and wr <= F32_ROW_REL
+    assert ok, f"{what}: max_abs={max_abs:.3e} rel_l2={rel:.3e} worst_row={wr:.3e} ({dtype})"
     return max_abs, rel
 
 

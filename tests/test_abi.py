@@ -230,3 +230,77 @@ def test_rows_block_validation():
     assert qkv(f, f, 5, 2, 64, 2, 64, f, None, None, f, f, None) == NULL
     assert qkv(f, f, 5, 2, 64, 2, 64, f, None, f, f, f + 2, None) == ALIGN
     assert qkv(None, None, 0, 2, 64, 2, 64, None, None, None, None, None, None) == OK
+
+
+# ------------------------------------------------------------------ mask-scan reads stay in the buffer
+_SPAN_CHECK = r"""
+#include "mask_span.hpp"
+#include <cstdio>
+#include <vector>
+// Walks the blocks the mask-scan kernels visit for every row of a mask placed at every byte offset of a
+// guarded arena, with the read decisions of mask_span.hpp, and checks that each byte read lies inside the
+// mask buffer and that every byte of each row's checked span is read.
+int main() {
+  using namespace safe;
+  long cases = 0;
+  const int esizes[2] = {1, 4};
+  for (int ei = 0; ei < 2; ++ei) {
+    const int es = esizes[ei];
+    for (int off = 0; off < 32; off += es)
+      for (int N = 1; N <= 23; N += 2)
+        for (int extra = 0; extra <= 5; extra += 5)
+          for (int nrows = 1; nrows <= 3; ++nrows) {
+            const int cols = N + extra;
+            for (int ncheck = N; ncheck <= cols; ++ncheck) {
+              const uintptr_t arena = 0x100000;  // 16-byte aligned stand-in address; nothing is dereferenced
+              const uintptr_t buf_lo = arena + off;
+              const uintptr_t buf_hi = buf_lo + static_cast<uintptr_t>(nrows) * cols * es;
+              for (int r = 0; r < nrows; ++r) {
+                const uintptr_t b0 = buf_lo + static_cast<uintptr_t>(r) * cols * es;
+                const uintptr_t hi = b0 + static_cast<uintptr_t>(ncheck) * es;
+                std::vector<char> seen(hi - b0, 0);
+                const RowBlocks rb = row_blocks(b0, hi);
+                for (uint32_t blk = 0; blk < rb.n; ++blk) {
+                  const uintptr_t a = rb.lo + static_cast<uintptr_t>(blk) * 16;
+                  uintptr_t r0 = a, r1 = a + 16;
+                  if (!block_whole(a, buf_lo, buf_hi)) block_bytes(a, b0, hi, &r0, &r1);
+                  if (r0 < buf_lo || r1 > buf_hi) {
+                    std::printf("OUT es=%d off=%d N=%d cols=%d rows=%d ncheck=%d r=%d blk=%u\n", es, off, N, cols,
+                                nrows, ncheck, r, blk);
+                    return 1;
+                  }
+                  for (uintptr_t e = r0; e < r1; ++e)
+                    if (e >= b0 && e < hi) seen[e - b0] = 1;
+                }
+                for (size_t i = 0; i < seen.size(); ++i)
+                  if (!seen[i]) {
+                    std::printf("MISSED es=%d off=%d N=%d r=%d byte=%zu\n", es, off, N, r, i);
+                    return 1;
+                  }
+                ++cases;
+              }
+            }
+          }
+  }
+  std::printf("ok %ld\n", cases);
+  return 0;
+}
+"""
+
+
+def test_mask_scan_reads_stay_inside_the_mask_buffer(tmp_path):
+    """Host-side bounds check of the mask-elision scan: the kernels' own block and byte decisions (the
+    header they include) never read outside [mask, mask + bytes) for any base offset or row length, and
+    cover every entry they must compare."""
+    import subprocess
+    src = tmp_path / "span_check.cpp"
+    src.write_text(_SPAN_CHECK)
+    exe = tmp_path / "span_check"
+    csrc = os.path.join(ROOT, "diffusion_transformer_spatially_amd", "csrc")
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    if not os.path.exists(hipcc):
+        pytest.skip("hipcc not available")
+    subprocess.run([hipcc, "-std=c++17", "-O1", f"-I{csrc}", str(src), "-o", str(exe)], check=True,
+                   capture_output=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert out.returncode == 0 and out.stdout.startswith("ok"), out.stdout

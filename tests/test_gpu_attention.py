@@ -59,8 +59,11 @@ def test_tiny_f32_dense_rows_and_pcsp(lib):
     rel_err = float(np.max(np.abs(a_gpu - a_ref) / a_ref))
     S = host(S_d)
     assert np.array_equal(S, OP.partition(a_gpu, w.k)[0])  # exact on the GPU's own scores
-    if margin > 10 * rel_err:
-        assert np.array_equal(S, S_ref)
+    # The end-to-end partition equals the fp64 one when the fp64 boundary margin exceeds 10x the measured fp32
+    # score error; a seed below that is ill-conditioned at the boundary and is reported as such, never passed
+    # silently (this workload's seed is screened on the CPU: margin 3.6e-5 against errors of a few 1e-7).
+    assert margin > 10 * rel_err, f"ill-conditioned boundary: margin {margin:.2e}, fp32 score error {rel_err:.2e}"
+    assert np.array_equal(S, S_ref)
     # sensitive rows into a stale state; |S| = N equals dense
     state = syn.initial_state(w)
     o2, _, _, _ = _run(lib, w, inp, rows=S, state=state)
@@ -189,8 +192,7 @@ def test_bf16_closed_forms(lib):
     for b in range(2):
         vals = np.concatenate([inp["v_img"][b], inp["v_txt"][b, :, : w.tv[b]]], axis=1).astype(np.float64)
         mean = vals.mean(axis=1)
-        m_abs, rel = err(o[b], np.broadcast_to(mean[:, None, :], o[b].shape))
-        assert m_abs <= 2e-2 and rel <= 5e-3
+        assert_close(o[b], np.broadcast_to(mean[:, None, :], o[b].shape), "bf16", "Q = 0: mean of the valid V rows")
         assert np.max(np.abs(lse[b] - np.log(w.N + w.tv[b]))) < 1e-3
 
 

@@ -194,10 +194,73 @@ def test_mask_policy_checks_once_per_tensor_version(lib):
     assert pol.elide(m, N, T, (5, 9)) is None
     assert pol.elide(m, N, T, (5, 9)) is None and len(pol._cache) == 1
     m[0, 0, 3, 7] = False  # bumps the tensor version
-    assert pol.elide(m, N, T, (5, 9)) is m and len(pol._cache) == 2
+    assert pol.elide(m, N, T, (5, 9)) is m and len(pol._cache) == 1
     f = t.zeros((1, 1, N, N + T), dtype=t.float32, device="cuda")
     assert pol.elide(f, N, T, (T, T)) is None
     f[0, 0, 1, N + T - 1] = -1.0  # a valid text column of row 1 differs
     assert pol.elide(f, N, T, (T, T)) is f
     assert pol.elide(f, N, T, (T - 1, T - 1)) is None  # that column is padding for these lengths
     assert pol.elide(None, N, T, (T, T)) is None
+
+
+def test_mask_policy_never_reuses_a_freed_masks_verdict(lib):
+    """A verdict is tied to the live tensor it was computed for: after a removable mask is freed, a
+    semantic mask of the same shape built without in-place edits (version 0 again) that the caching
+    allocator places at the freed address must be checked afresh and kept; dead entries are dropped."""
+    import gc
+    t = torch()
+    N, T = 128, 16
+    pol = lib.MaskPolicy()
+    reused = 0
+    for trial in range(4):
+        m1 = t.from_numpy(np.ones((1, 1, N, N), dtype=np.bool_)).cuda()
+        assert m1._version == 0 and pol.elide(m1, N, T, (7,)) is None
+        addr = m1.data_ptr()
+        del m1
+        gc.collect()
+        assert len(pol._cache) == 0  # the entry went with its tensor
+        sem = np.ones((1, 1, N, N), dtype=np.bool_)
+        sem[0, 0, 5 + trial, 9] = False  # a semantic (non-uniform) mask
+        m2 = t.from_numpy(sem).cuda()
+        reused += int(m2.data_ptr() == addr)
+        assert m2._version == 0
+        assert pol.elide(m2, N, T, (7,)) is m2, trial
+        del m2
+        gc.collect()
+    assert reused > 0, "the allocator never reused the address; the stale-entry case was not exercised"
+
+
+@pytest.mark.parametrize("dtype", ["bool", "f32"])
+def test_mask_check_unaligned_buffer(lib, dtype):
+    """A mask whose base is not 16-byte aligned (1 byte past an aligned address for bool, 4 for fp32) and
+    whose total length is not a multiple of 16 bytes: the verdict and per-row constants equal the oracle's,
+    with the first or the last entry of the buffer deciding (the scan reads those edge blocks byte by byte
+    and nothing outside the buffer)."""
+    t = torch()
+    N, T = 29, 4
+    es = 1 if dtype == "bool" else 4
+    for cols, tv in ((N, (0,)), (N + T, (4,)), (N + T, (1,))):
+        for trial in range(3):
+            if dtype == "bool":
+                m = np.ones((1, 2, N, cols), dtype=np.bool_)
+                bad = False
+            else:
+                m = np.full((1, 2, N, cols), -1.5, dtype=np.float32)
+                bad = np.float32(2.0)
+            if trial == 1:
+                m[0, 0, 0, 0] = bad                 # first byte(s) of the buffer
+            elif trial == 2:
+                m[0, 1, N - 1, tv[0] + N - 1 if cols > N else N - 1] = bad  # last checked entry of the buffer
+            nbytes = m.size * es
+            assert nbytes % 16 != 0
+            raw = t.zeros(16 + nbytes + 16, dtype=t.uint8, device="cuda")
+            assert raw.data_ptr() % 16 == 0
+            raw[es:es + nbytes] = t.from_numpy(m.view(np.uint8).ravel()).cuda()
+            view = raw[es:es + nbytes].view(t.bool if dtype == "bool" else t.float32).view(m.shape)
+            assert view.data_ptr() % 16 == es
+            flag = t.zeros(1, dtype=t.int32, device="cuda")
+            c = t.full((2 * N,), 123.0, dtype=t.float32, device="cuda")
+            ok = lib.safe_mask_is_row_constant(view, N, T, tv, flag, c_out=c)
+            rok, rc = OE.is_row_constant(m, N, T, tv)
+            assert ok == rok and _same(host(c).astype(np.float64), rc), (cols, tv, trial)
+            assert lib.safe_mask_is_row_constant(view, N, T, tv, flag) == rok, (cols, tv, trial)

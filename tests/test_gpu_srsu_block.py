@@ -5,7 +5,7 @@ import pytest
 
 import synthetic as syn
 from oracle import srsu_block as SB
-from tests.gpu_util import BF16_MAX_ABS, BF16_REL_L2, dev, err, host, torch
+from tests.gpu_util import assert_close, dev, host, torch
 
 pytestmark = pytest.mark.gpu
 
@@ -52,8 +52,7 @@ def test_rows_ffn_parity_and_cache_untouched(lib, B, N, H, d, k, mult):
         ref = SB.rows_ffn(p["x"], p["rows"], p["w1"], p["b1"] if with_bias else None, p["w2"],
                           p["b2"] if with_bias else None, cache0)
         rows = p["rows"]
-        mx, rel = err(got[:, rows], ref[:, rows])
-        assert mx <= BF16_MAX_ABS and rel <= BF16_REL_L2, (mx, rel)
+        assert_close(got[:, rows], ref[:, rows], "bf16", "block product")
         other = np.setdiff1d(np.arange(N), rows)
         assert np.array_equal(got[:, other], cache0[:, other].astype(np.float64))
 
@@ -77,8 +76,7 @@ def test_rows_qkv_parity_and_context_untouched(lib, B, N, H, d, k):
     rows = p["rows"]
     other = np.setdiff1d(np.arange(N), rows)
     for g, rf, orig in zip(got, ref, (q0, k0, v0)):
-        mx, rel = err(g[:, :, rows], rf[:, :, rows])
-        assert mx <= BF16_MAX_ABS and rel <= BF16_REL_L2, (mx, rel)
+        assert_close(g[:, :, rows], rf[:, :, rows], "bf16", "block product")
         assert np.array_equal(g[:, :, other], orig[:, :, other].astype(np.float64))
 
 
@@ -90,8 +88,7 @@ def test_rows_outside_range_are_skipped(lib):
     got = _ffn(lib, p, cache0)
     valid = p["rows"][(p["rows"] >= 0) & (p["rows"] < 64)]
     ref = SB.rows_ffn(p["x"], valid, p["w1"], p["b1"], p["w2"], p["b2"], cache0)
-    mx, rel = err(got, ref)
-    assert mx <= BF16_MAX_ABS and rel <= BF16_REL_L2
+    assert_close(got, ref, "bf16", "block product")
 
 
 @pytest.mark.parametrize("name", ["srsu_1024"])
@@ -112,15 +109,15 @@ def test_full_size_block_products(lib, name):
     lib.safe_rows_qkv(xd, dev(rows), _bf(bw["wqkv"]), dev(bw["bqkv"]), q, kc, vc)
     t.cuda.synchronize()
     ref = SB.rows_ffn(x, rows, bw["w1"], bw["b1"], bw["w2"], bw["b2"], cache0)
-    mx, rel = err(host(cache)[:, rows], ref[:, rows])
+    mx, rel = assert_close(host(cache)[:, rows], ref[:, rows], "bf16", f"{name} FFN")
+
     print(f"{name} FFN: max-abs {mx:.3e}, rel-L2 {rel:.3e}")
-    assert mx <= BF16_MAX_ABS and rel <= BF16_REL_L2
     z = np.zeros((w.B, w.H, w.N, w.d), dtype=np.float32)
     rq = SB.rows_qkv(x, rows, bw["wqkv"], bw["bqkv"], z, z, z, w.H, w.d)
     for g, rf in zip((q, kc, vc), rq):
-        mx, rel = err(host(g)[:, :, rows], rf[:, :, rows])
+        mx, rel = assert_close(host(g)[:, :, rows], rf[:, :, rows], "bf16", f"{name} QKV")
+
         print(f"{name} QKV: max-abs {mx:.3e}, rel-L2 {rel:.3e}")
-        assert mx <= BF16_MAX_ABS and rel <= BF16_REL_L2
 
 
 def test_rows_ffn_many_tokens(lib):
@@ -140,7 +137,6 @@ def test_rows_ffn_many_tokens(lib):
     rows = p["rows"]
     pick = rows[syn.sample_rows(len(rows), 48, seed=5)]
     ref = SB.rows_ffn(p["x"], pick, p["w1"], p["b1"], p["w2"], p["b2"], cache0)
-    mx, rel = err(got[:, pick], ref[:, pick])
-    assert mx <= BF16_MAX_ABS and rel <= BF16_REL_L2, (mx, rel)
+    assert_close(got[:, pick], ref[:, pick], "bf16", "block product")
     other = np.setdiff1d(np.arange(N), rows)
     assert np.array_equal(got[:, other], cache0[:, other].astype(np.float64))
