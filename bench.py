@@ -29,6 +29,7 @@ sys.path.insert(0, ROOT)
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+BREAKDOWN_STEPS = 100            # minimum length of each half of the eager per-kernel pass
 
 
 def parse():
@@ -38,7 +39,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=200,
                     help="untimed graph steps before the timed ones (the step time settles over the first ~100-300)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="time budget of the oracle sample")
+    ap.add_argument("--cpu-seconds", type=float, default=9.0, help="time budget of the dense oracle sample")
     ap.add_argument("--no-large", action="store_true", help="skip the 2560^2 attention lines")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 256 MiB device copy (for scaling HBM byte counters)")
@@ -190,11 +191,13 @@ def main():
     # same steps (events cannot sit inside the graph), with each step's check started only once the
     # previous step's kernels have finished, so that no kernel shares the GPU with another.  This pass
     # also brings the GPU to its working clock before the timed graph steps (the first few dozen steps
-    # after an idle GPU run slower).
-    for _ in range(args.warmup):
+    # after an idle GPU run slower).  Its length is fixed (at least 100 untimed and 100 recorded steps,
+    # whatever W and K are), so that the medians are stable and the timed graph steps start on a GPU at its
+    # working clock.
+    for _ in range(max(args.warmup, BREAKDOWN_STEPS)):
         eager_step(False)
     torch.cuda.synchronize()
-    for _ in range(args.steps):
+    for _ in range(max(args.steps, BREAKDOWN_STEPS)):
         eager_step(True)
     torch.cuda.synchronize()
     avg_ms = {s: float(np.median([a.elapsed_time(b) for a, b in ev[s]])) for s in stages}  # median per launch
@@ -236,37 +239,23 @@ def main():
     mask_bytes = 1.0 * N * N
     gbs = lambda b, ms: b / (ms * 1e-3) / 1e9
     hbm = lambda b, ms: {"ms": ms, "gbs": gbs(b, ms), "frac_hbm": gbs(b, ms) / HBM_PEAK_GBS, "bytes": b}
+    # the step's HBM stages: their working sets (tens of MB) stay in the 256 MB MALL from step to step and
+    # each launch lasts a few microseconds, so these are cache-resident, launch-granularity figures; the
+    # HBM fractions of these kernels come from the batched and cold launches of the `hbm` section
+    step_line = lambda b, ms: {"ms": ms, "gbs_cache": gbs(b, ms), "bytes": b}
     breakdown = {
         "attn_dense": {"ms": avg_ms["attn_dense"], "tflops": dense_tf, "frac_mfma": dense_tf / MFMA_BF16_PEAK_TFLOPS},
         "attn_rows": {"ms": avg_ms["attn_rows"], "tflops": rows_tf, "frac_mfma": rows_tf / MFMA_BF16_PEAK_TFLOPS},
-        "pcsp_accumulate": hbm(pcsp_bytes, avg_ms["pcsp_accumulate"]),
+        "pcsp_accumulate": step_line(pcsp_bytes, avg_ms["pcsp_accumulate"]),
         "pcsp_partition": {"ms": avg_ms["pcsp_partition"], "note": "one workgroup: latency-bound, no roofline"},
-        "swcfg_combine": hbm(cfg_bytes, avg_ms["swcfg_combine"]),
-        "gather_rows": hbm(gs_bytes, avg_ms["gather_rows"]),
-        "scatter_rows": hbm(gs_bytes, avg_ms["scatter_rows"]),
-        "mask_check": dict(hbm(mask_bytes, avg_ms["mask_check"]),
+        "swcfg_combine": step_line(cfg_bytes, avg_ms["swcfg_combine"]),
+        "gather_rows": step_line(gs_bytes, avg_ms["gather_rows"]),
+        "scatter_rows": step_line(gs_bytes, avg_ms["scatter_rows"]),
+        "mask_check": dict(step_line(mask_bytes, avg_ms["mask_check"]),
                            note="synchronous (host verdict), includes the device-to-host copy"),
-        "stat": "median over the timed launches",
+        "stat": "median over the timed launches, each with its own event pair (about 2 us of event packets "
+                "included); HBM stages cache-resident",
     }
-
-    # Cold mode: each HBM-bound stage of the step with L2 and MALL swept by a 1 GiB write before the launch
-    # (the step's own working set, tens of MB, otherwise stays in the 256 MB MALL from step to step).
-    flush = torch.empty(256 << 20, dtype=torch.float32, device=dev)
-    cold = {
-        "pcsp_accumulate": cold_line(hbm, pcsp_bytes, cold_launch_ms(
-            torch, lambda: dts.safe_pcsp_accumulate(xd, lid, Tv, 0, Tv, scores, False), flush)),
-        "gather_rows": cold_line(hbm, gs_bytes, cold_launch_ms(
-            torch, lambda: dts.safe_gather_rows(state, S, packed), flush)),
-        "scatter_rows": cold_line(hbm, gs_bytes, cold_launch_ms(
-            torch, lambda: dts.safe_scatter_rows(packed, S, state), flush)),
-        "swcfg_combine": cold_line(hbm, cfg_bytes, cold_launch_ms(
-            torch, lambda: dts.safe_swcfg_combine(eps, s01, w.side, w.g_ctx, w.g_sens, cfg_out), flush)),
-        "mask_scan": cold_line(hbm, mask_bytes, cold_launch_ms(
-            torch, lambda: dts.safe_mask_check_launch(mask, N, T, w.tv, flags[0]), flush)),
-        "note": "1024^2 step shapes; a 1 GiB write and a 1 GiB read sweep L2 and MALL before each launch; one event "
-                "pair per launch, the median of an empty pair after the same sweep subtracted (ms_raw, event_pair_ms)",
-    }
-    del flush
 
     sclk = profiled_traffic("sclk_mhz")
     peak_sclk = 256 * 4 * 1024 * sclk / 1e6 if sclk else None  # TFLOP/s
@@ -279,11 +268,12 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": ms_per_step,
         "kernel_ms_sum": kernel_ms_sum,
-        "timing": "wall clock of K whole steps (each step: its elision check, launched two steps ahead on a "
-                  "side stream, and a graph replay of the rest, every stage in order on one stream); kernel "
-                  "durations and the roofline from HIP events in an eager pass of the same steps, run "
-                  "without overlap between steps, each step's launches queued behind a spin so that the "
-                  "events time the kernels; kernel_ms_sum adds the main-stream kernels' medians",
+        "timing": "wall clock of K whole steps after W untimed ones (each step: its elision check, launched two "
+                  "steps ahead on a side stream, and a graph replay of the rest, every stage in order on one "
+                  "stream); kernel durations and the roofline from HIP events in an eager pass of the same steps "
+                  "that runs first (max(W,100) untimed + max(K,100) recorded steps), without overlap between "
+                  "steps, each step's launches queued behind a spin so that the events time the kernels; "
+                  "kernel_ms_sum adds the main-stream kernels' medians",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -301,7 +291,6 @@ def main():
                      "sclk_note": "shader clock during this kernel from the profile's GRBM_COUNT pass; "
                                   "peak_at_sclk = 256 CU x 4 SIMD x 1024 flop/clk x sclk"},
         "breakdown": breakdown,
-        "hbm_cold": cold,
         "step_branched": {"ms_per_step": ms_per_step_branched,
                           "value": attn_flops / (ms_per_step_branched * 1e-3) / 1e12,
                           "note": "the same steps from a graph that runs PCSP, partition and SW-CFG on a branch beside "
@@ -327,34 +316,23 @@ def main():
         wl = syn.WORKLOADS["srsu_2560"]
         lq, lki, lvi, lkt, lvt, lrows, lout, line = attention_large(dts, torch, syn, dev, wl, stream)
         result["attention_2560"] = line
-        result["hbm_large"] = hbm_large(dts, torch, np, syn, dev, lout, lrows, hbm)
         lmask = torch.ones((1, 1, wl.N, wl.N), dtype=torch.bool, device=dev)  # 655 MB
         kept = time_launches(torch, lambda: dts.safe_attn_dense(lq, lki, lvi, lkt, lvt, wl.tv, lout, mask=lmask), reps=3)
         tax["dense_2560_elided_ms"] = line["dense_ms"]
         tax["dense_2560_kept_bool_ms"] = kept
         tax["tax_2560_bool"] = kept / line["dense_ms"]
-        # the elision check itself on the 655 MB bool mask (verdict only, launch form, device flag)
-        lflag = torch.zeros(1, dtype=torch.int32, device=dev)
-        chk = {"bool_ms": time_launches(torch, lambda: dts.safe_mask_check_launch(lmask, wl.N, wl.T, wl.tv, lflag),
-                                        reps=5)}
         del lmask
         lfmask = torch.zeros((1, 1, wl.N, wl.N), dtype=torch.float32, device=dev)  # 2.6 GB
-        chk["f32_ms"] = time_launches(torch, lambda: dts.safe_mask_check_launch(lfmask, wl.N, wl.T, wl.tv, lflag),
-                                      reps=5)
         kept32 = time_launches(torch, lambda: dts.safe_attn_dense(lq, lki, lvi, lkt, lvt, wl.tv, lout, mask=lfmask),
                                reps=2)
         tax["dense_2560_kept_f32_ms"] = kept32
         tax["tax_2560_f32"] = kept32 / line["dense_ms"]
         del lfmask
-        nb = float(wl.N) * wl.N
-        chk.update({"bool_frac_hbm": nb / (chk["bool_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                    "f32_frac_hbm": 4 * nb / (chk["f32_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                    "workload": "srsu_2560 all-valid image mask [1,1,25600,25600]: 655 MB bool / 2.62 GB fp32 zeros; "
-                                "verdict-only scan, 5 back-to-back launches"})
-        result["mask_check_2560"] = chk
         del lq, lki, lvi, lkt, lvt, lout, lrows
         result["attention_3072"] = attention_large(dts, torch, syn, dev, syn.WORKLOADS["traj_3072"], stream,
                                                    reps=3)[-1]
+        result["trajectory_3072"] = trajectory_3072(dts, torch, np, syn, dev)
+        result["hbm"] = hbm_stages(dts, torch, np, syn, dev, hbm)
 
     result["mask_tax"] = tax
     # head dim 128 at the 1024^2 grid (24 heads x 128): the same path at the other head dim the library takes
@@ -373,7 +351,7 @@ def main():
 
     # ---------------------------------------------------------------- oracle on the host cores
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(w, inp, S.cpu().numpy(), args.cpu_seconds, not args.no_large)
         result["cpu_oracle_other_stages"] = cpu_other_stages(w, x, syn)
     print(json.dumps(result), flush=True)
 
@@ -473,58 +451,182 @@ def time_launches(torch, fn, reps=20):
     return e0.elapsed_time(e1) / reps
 
 
-def hbm_large(dts, torch, np, syn, dev, state, rows, hbm):
-    """The HBM-bound stages on the 2560^2 / 3072^2 shapes (working sets of tens to hundreds of MB, far
-    beyond the launch-overhead regime of the 1024^2 step), and torch's device copy as a reference point."""
-    wl, w5 = syn.WORKLOADS["srsu_2560"], syn.WORKLOADS["traj_3072"]
+def hbm_stages(dts, torch, np, syn, dev, hbm):
+    """The HBM-bound stages at the 2560^2 / 3072^2 shapes, in three modes:
+      batched: one launch whose working set exceeds the 256 MB MALL (several independent instances of the
+               3072^2 shape in one launch where one instance is smaller), L2 and MALL swept before it;
+      cold:    one launch of the single-instance 2560^2 / 3072^2 shape after the same sweep;
+      cache_resident: 20 back-to-back launches of the single-instance shape between one event pair, whose
+               working set stays in the MALL from launch to launch -- a cache figure, not an HBM one.
+    The batched and cold launches each have their own event pair (queued behind the sweep, so the pair
+    brackets the kernel, not the host's launch), minus the median of an empty pair after the same sweep;
+    frac_hbm is reported for these two modes only."""
+    w4, w5 = syn.WORKLOADS["srsu_2560"], syn.WORKLOADS["traj_3072"]
     g = torch.Generator(device=dev)
-    g.manual_seed(wl.seed + 100)
-    out = {}
-    H, N, T, Tv = wl.H, wl.N, wl.T, wl.tv[0]
-    x = torch.randn((H, N, T), generator=g, device=dev)
-    li = torch.randn((H, N), generator=g, device=dev) + float(np.log(N))
-    sc = torch.empty(N, dtype=torch.float32, device=dev)
-    out["pcsp_accumulate_2560"] = hbm(4.0 * H * N * Tv + 4.0 * H * N + 4.0 * N,
-                                      time_launches(torch, lambda: dts.safe_pcsp_accumulate(x, li, Tv, 0, Tv, sc, False)))
+    g.manual_seed(w4.seed + 100)
     sweep = torch.empty(256 << 20, dtype=torch.float32, device=dev)  # 1 GiB
-    pcsp_cold = cold_line(hbm, 4.0 * H * N * Tv + 4.0 * H * N + 4.0 * N, cold_launch_ms(
-        torch, lambda: dts.safe_pcsp_accumulate(x, li, Tv, 0, Tv, sc, False), sweep))
-    del x, li, sweep
-    S = torch.empty(wl.k, dtype=torch.int32, device=dev)
-    C = torch.empty(N - wl.k, dtype=torch.int32, device=dev)
-    isn = torch.empty(N, dtype=torch.uint8, device=dev)
-    s01 = torch.empty(N, dtype=torch.float32, device=dev)
-    out["pcsp_partition_2560"] = {"ms": time_launches(torch, lambda: dts.safe_pcsp_partition(sc, wl.k, S, C, isn, s01)),
-                                  "note": "one workgroup over N=25600: latency-bound, no roofline"}
-    packed = torch.empty((wl.B, wl.H, wl.k, wl.d), dtype=torch.bfloat16, device=dev)
-    gs = 2 * 2.0 * wl.B * wl.H * wl.k * wl.d
-    out["gather_rows_2560"] = hbm(gs, time_launches(torch, lambda: dts.safe_gather_rows(state, rows, packed)))
-    out["scatter_rows_2560"] = hbm(gs, time_launches(torch, lambda: dts.safe_scatter_rows(packed, rows, state)))
+    batched, cold, resident = {}, {}, {}
+
+    def cache_line(bytes_, ms):
+        return {"ms": ms, "gbs_cache": bytes_ / (ms * 1e-3) / 1e9, "bytes": bytes_,
+                "note": "MALL-resident working set: a cache bandwidth, not an HBM fraction"}
+
+    # PCSP aggregation: 3072^2 (708 MB of valid logits: batched by size alone) and 2560^2 (297 MB)
+    for wl, tag, modes in ((w5, "3072", (batched,)), (w4, "2560", (cold, resident))):
+        H, N, T, Tv = wl.H, wl.N, wl.T, wl.tv[0]
+        x = torch.randn((H, N, T), generator=g, device=dev)
+        li = torch.randn((H, N), generator=g, device=dev) + float(np.log(N))
+        sc = torch.empty(N, dtype=torch.float32, device=dev)
+        nb = 4.0 * H * N * Tv + 4.0 * H * N + 4.0 * N
+        fn = lambda: dts.safe_pcsp_accumulate(x, li, Tv, 0, Tv, sc, False)
+        for m in modes:
+            if m is resident:
+                m["pcsp_accumulate_" + tag] = cache_line(nb, time_launches(torch, fn))
+            else:
+                m["pcsp_accumulate_" + tag] = cold_line(hbm, nb, cold_launch_ms(torch, fn, sweep))
+        if tag == "2560":
+            S = torch.empty(wl.k, dtype=torch.int32, device=dev)
+            C = torch.empty(N - wl.k, dtype=torch.int32, device=dev)
+            isn = torch.empty(N, dtype=torch.uint8, device=dev)
+            s01 = torch.empty(N, dtype=torch.float32, device=dev)
+            resident["pcsp_partition_2560"] = {
+                "ms": time_launches(torch, lambda: dts.safe_pcsp_partition(sc, wl.k, S, C, isn, s01)),
+                "note": "one workgroup over N=25600: latency-bound, no roofline"}
+        del x, li
+    # row gather / scatter: 3072^2 state with 6 instances (B = 12) in one launch, and the 2560^2 state
+    for wl, tag, Bx, modes in ((w5, "3072x6", 6 * w5.B, (batched,)), (w4, "2560", w4.B, (cold, resident))):
+        st = torch.randn((Bx, wl.H, wl.N, wl.d), generator=g, device=dev).to(torch.bfloat16)
+        rows = torch.from_numpy(syn.random_rows(wl)).to(dev)
+        packed = torch.empty((Bx, wl.H, wl.k, wl.d), dtype=torch.bfloat16, device=dev)
+        gs = 2 * 2.0 * Bx * wl.H * wl.k * wl.d
+        for name, fn in (("gather_rows_", lambda: dts.safe_gather_rows(st, rows, packed)),
+                         ("scatter_rows_", lambda: dts.safe_scatter_rows(packed, rows, st))):
+            for m in modes:
+                m[name + tag] = (cache_line(gs, time_launches(torch, fn)) if m is resident
+                                 else cold_line(hbm, gs, cold_launch_ms(torch, fn, sweep)))
+        del st, packed
+    # SW-CFG and StepCache on the 3072^2 latent [16,384,384]; batched: 10 latents' channels in one launch
     C5, Hl, Wl = w5.latent
-    eps = torch.randn((2, C5, Hl, Wl), generator=g, device=dev)
-    s5 = torch.rand(w5.N, generator=g, device=dev)
-    cout = torch.empty((C5, Hl, Wl), dtype=torch.float32, device=dev)
-    out["swcfg_combine_3072"] = hbm(3 * 4.0 * C5 * Hl * Wl + 4.0 * w5.N,
-                                    time_launches(torch, lambda: dts.safe_swcfg_combine(eps, s5, w5.side, w5.g_ctx,
-                                                                                         w5.g_sens, cout)))
+    for reps, tag, modes in ((10, "3072x10", (batched,)), (1, "3072", (cold, resident))):
+        Cx = C5 * reps
+        eps = torch.randn((2, Cx, Hl, Wl), generator=g, device=dev)
+        s5 = torch.rand(w5.N, generator=g, device=dev)
+        cout = torch.empty((Cx, Hl, Wl), dtype=torch.float32, device=dev)
+        cb = 3 * 4.0 * Cx * Hl * Wl + 4.0 * w5.N
+        fn = lambda: dts.safe_swcfg_combine(eps, s5, w5.side, w5.g_ctx, w5.g_sens, cout)
+        for m in modes:
+            m["swcfg_combine_" + tag] = (cache_line(cb, time_launches(torch, fn)) if m is resident
+                                         else cold_line(hbm, cb, cold_launch_ms(torch, fn, sweep)))
+        # StepCache reuses eps[0] / eps[1] as the two full predictions
+        sb = 12.0 * Cx * Hl * Wl
+        fn = lambda: dts.safe_stepcache_extrapolate(eps[0], eps[1], 1.0 / 3.0, cout)
+        for m in modes:
+            m["stepcache_" + tag] = (cache_line(sb, time_launches(torch, fn)) if m is resident
+                                     else cold_line(hbm, sb, cold_launch_ms(torch, fn, sweep)))
+        del eps, cout
+    # the elision scan on the 2560^2 all-valid image mask (655 MB bool, 2.62 GB fp32): batched by size
+    lflag = torch.zeros(1, dtype=torch.int32, device=dev)
+    for dt, esz in ((torch.bool, 1.0), (torch.float32, 4.0)):
+        m = (torch.ones if dt == torch.bool else torch.zeros)((1, 1, w4.N, w4.N), dtype=dt, device=dev)
+        batched["mask_scan_2560_" + ("bool" if dt == torch.bool else "f32")] = cold_line(
+            hbm, esz * w4.N * w4.N, cold_launch_ms(torch, lambda: dts.safe_mask_check_launch(m, w4.N, w4.T, w4.tv, lflag),
+                                                   sweep, reps=5))
+        del m
     src = torch.empty(256 << 20, dtype=torch.float32, device=dev).fill_(1.0)  # 1 GiB
+    del sweep
     dst = torch.empty_like(src)
-    out["torch_copy_1GiB"] = hbm(2.0 * src.numel() * 4, time_launches(torch, lambda: dst.copy_(src), reps=10))
-    # the same stages once more with L2 and MALL swept before each launch (dst is the sweep buffer)
-    out["cold"] = {
-        "pcsp_accumulate_2560": pcsp_cold,
-        "gather_rows_2560": cold_line(hbm, gs, cold_launch_ms(
-            torch, lambda: dts.safe_gather_rows(state, rows, packed), dst)),
-        "scatter_rows_2560": cold_line(hbm, gs, cold_launch_ms(
-            torch, lambda: dts.safe_scatter_rows(packed, rows, state), dst)),
-        "swcfg_combine_3072": cold_line(hbm, 3 * 4.0 * C5 * Hl * Wl + 4.0 * w5.N, cold_launch_ms(
-            torch, lambda: dts.safe_swcfg_combine(eps, s5, w5.side, w5.g_ctx, w5.g_sens, cout), dst)),
-    }
-    out["note"] = ("shapes: PCSP x [24,25600,256] fp32 (Tv=120 valid), partition N=25600 k=5120, gather/scatter "
-                   "[2,24,25600,64] bf16 k=5120, SW-CFG [2,16,384,384] fp32; torch_copy_1GiB is torch's device copy, a "
-                   "reference point rather than the ceiling (a streaming copy with nontemporal loads and stores "
-                   "moves about 6.4 TB/s on this part)")
-    return out
+    ref = {"torch_copy_1GiB": hbm(2.0 * src.numel() * 4, time_launches(torch, lambda: dst.copy_(src), reps=10)),
+           "note": "torch's device copy: a reference point rather than the ceiling (a streaming copy with "
+                   "nontemporal loads and stores moves about 6.4 TB/s on this part)"}
+    del src, dst
+    return {"batched": batched, "cold": cold, "cache_resident": resident, "reference": ref,
+            "shapes": "PCSP x [24,N,256] fp32 (3072^2: N=36864, Tv=200; 2560^2: N=25600, Tv=120); gather/scatter "
+                      "state [B,24,N,64] bf16 (3072^2 x6: B=12, k=7373; 2560^2: B=2, k=5120); SW-CFG / StepCache "
+                      "[2,C,384,384] / [C,384,384] fp32 (x10: C=160; single: C=16); mask [1,1,25600,25600]",
+            "note": "batched and cold: one launch, its own HIP event pair after a 1 GiB write + 1 GiB read sweep, "
+                    "minus the empty pair (ms_raw, event_pair_ms); the kernel trace of the same launches is "
+                    "in profiles/hbm_stages_large.md"}
+
+
+def trajectory_3072(dts, torch, np, syn, dev, reps=2):
+    """The 3072^2 trajectory end to end (SAFE-DiT summary, Methodology 2-3): two warmup steps, each a dense
+    anchor attention of every row plus the PCSP aggregation of that step's image->text logits; the
+    partition once; then 10 steps following the library's plan (anchor refresh at steps 0, 4, 8, sensitive
+    rows of S otherwise), each followed by the SW-CFG combine of the [2,16,384,384] prediction with the
+    partition's sensitivities.  Seeded device tensors of the workload's shapes and laws (Q/K/V N(0,1)*0.125;
+    logits N(0,1) plus the workload's blob bias, drawn beforehand as a warmup step's emission would have
+    written them; lse_img = ln N + 1/2).  The same 12 attention steps with every step an anchor (no
+    partition, global guidance) are timed beside it.  One event pair around each whole trajectory."""
+    w = syn.WORKLOADS["traj_3072"]
+    g = torch.Generator(device=dev)
+    g.manual_seed(w.seed)
+    mk = lambda n: (torch.randn((w.B, w.H, n, w.d), generator=g, device=dev) * w.std).to(torch.bfloat16)
+    q, ki, vi, kt, vt = mk(w.N), mk(w.N), mk(w.N), mk(w.T), mk(w.T)
+    state = torch.zeros_like(q)
+    Tv = w.tv[0]
+    bias = torch.from_numpy(syn.blob_bias(w)).to(dev)
+    xs = []
+    for _ in range(w.warmup_steps):
+        x = torch.randn((w.H, w.N, w.T), generator=g, device=dev)
+        x[:, :, :Tv] += bias[None, :, None]
+        xs.append(x)
+    lse_img = torch.full((w.H, w.N), float(np.log(w.N) + 0.5), dtype=torch.float32, device=dev)
+    scores = torch.zeros(w.N, dtype=torch.float32, device=dev)
+    S = torch.empty(w.k, dtype=torch.int32, device=dev)
+    C = torch.empty(w.N - w.k, dtype=torch.int32, device=dev)
+    isn = torch.empty(w.N, dtype=torch.uint8, device=dev)
+    s01 = torch.empty(w.N, dtype=torch.float32, device=dev)
+    C5, Hl, Wl = w.latent
+    eps = torch.randn((2, C5, Hl, Wl), generator=g, device=dev)
+    cfg_out = torch.empty((C5, Hl, Wl), dtype=torch.float32, device=dev)
+    plan = dts.safe_trajectory_plan(w.steps, w.anchor_every)
+    dense = lambda: dts.safe_attn_dense(q, ki, vi, kt, vt, w.tv, state)
+
+    def safe_traj():
+        for st in range(w.warmup_steps):
+            dense()
+            dts.safe_pcsp_accumulate(xs[st], lse_img, Tv, 0, Tv, scores, st > 0)
+        dts.safe_pcsp_partition(scores, w.k, S, C, isn, s01)
+        for kind in plan:
+            if kind == dts.SAFE_STEP_DENSE:
+                dense()
+            else:
+                dts.safe_attn_rows(q, ki, vi, kt, vt, w.tv, S, state)
+            dts.safe_swcfg_combine(eps, s01, w.side, w.g_ctx, w.g_sens, cfg_out)
+
+    def dense_traj():
+        for _ in range(w.warmup_steps + w.steps):
+            dense()
+            dts.safe_swcfg_combine(eps, s01, w.side, w.g_ctx, w.g_ctx, cfg_out)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        out = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            out.append(e0.elapsed_time(e1))
+        return float(np.median(out))
+
+    t_safe = timed(safe_traj)
+    t_dense = timed(dense_traj)
+    n_dense = w.warmup_steps + sum(1 for k in plan if k == dts.SAFE_STEP_DENSE)
+    n_rows = len(plan) - sum(1 for k in plan if k == dts.SAFE_STEP_DENSE)
+    fl = n_dense * w.flops_dense + n_rows * w.flops_rows
+    fl_dense = (w.warmup_steps + w.steps) * w.flops_dense
+    return {"workload": f"traj_3072: B={w.B}, H={w.H}, d={w.d}, N={w.N}, Tv={Tv}, |S|={w.k}; {w.warmup_steps} warmup "
+                        f"steps (dense + PCSP), partition, {w.steps} steps (plan {plan}: 0 = anchor, 1 = rows), "
+                        f"SW-CFG [2,{C5},{Hl},{Wl}] after each step",
+            "ms": t_safe, "attention_flops": fl, "tflops": fl / (t_safe * 1e-3) / 1e12,
+            "frac_mfma": fl / (t_safe * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+            "dense_only_ms": t_dense, "speedup_vs_dense_only": t_dense / t_safe,
+            "dense_only_equivalent_tflops": fl_dense / (t_safe * 1e-3) / 1e12,
+            "reps": reps, "note": "one event pair around each whole trajectory; attention flops count the "
+                                  "dense anchors (all rows) and the sensitive-row steps (|S| rows)"}
 
 
 def next_rows(dts, torch, np, syn, dev, hbm, large: bool):
@@ -546,7 +648,8 @@ def next_rows(dts, torch, np, syn, dev, hbm, large: bool):
         isn = torch.empty(N, dtype=torch.uint8, device=dev)
         nbytes = 4.0 * H * N * Tv + 4.0 * H * N + 4.0 * N
         aff = lambda: dts.safe_affinity_accumulate(x, li, Tv, sel, sc, False)
-        line = {"affinity_warm": hbm(nbytes, time_launches(torch, aff)),
+        line = {"affinity_cache_resident": {"ms": time_launches(torch, aff), "bytes": nbytes,
+                                            "note": "MALL-resident working set: not an HBM fraction"},
                 "affinity_cold": cold_line(hbm, nbytes, cold_launch_ms(torch, aff, sweep)),
                 "mask_ms": time_launches(torch, lambda: (aff(), dts.safe_pcsp_partition(sc, k, S, C, isn))),
                 "k": k,
@@ -561,10 +664,11 @@ def next_rows(dts, torch, np, syn, dev, hbm, large: bool):
         ex = lambda: dts.safe_stepcache_extrapolate(preds[0], preds[1], 1.0 / 3.0, o)
         C_, Hl, Wl = w.latent
         out["stepcache_" + name.split("_")[1]] = {
-            "warm": hbm(12.0 * n, time_launches(torch, ex)),
+            "cache_resident": {"ms": time_launches(torch, ex), "bytes": 12.0 * n,
+                               "note": "MALL-resident working set: not an HBM fraction"},
             "cold": cold_line(hbm, 12.0 * n, cold_launch_ms(torch, ex, sweep)),
             "workload": f"{name}: prediction [{C_},{Hl},{Wl}] fp32, w = 1/3"}
-    out["note"] = ("warm: 20 back-to-back launches between one event pair; cold: each launch after a 1 GiB write "
+    out["note"] = ("cache_resident: 20 back-to-back launches between one event pair; cold: each launch after a 1 GiB write "
                    "and a 1 GiB read, its own event pair minus an empty pair; mask_ms: affinity + partition")
     del sweep
     return out
@@ -636,10 +740,32 @@ def profiled_traffic(field: str = "traffic_bytes_per_launch"):
     return float(fields[field])
 
 
-def cpu_baseline(w, inp, budget_s: float):
-    """The fp64 oracle as it stands, on a bounded sample of the same step's attention work."""
-    import numpy as np
+def _oracle_heads(w, inp, rows, budget_s: float):
+    """Runs the fp64 oracle over (b, h) heads in order, on query rows `rows` (None: all), until the budget is
+    spent; returns (flops done, seconds, heads done)."""
     from oracle import attention as OA
+    R = w.N if rows is None else len(rows)
+    flops, done = 0.0, 0
+    t0 = time.perf_counter()
+    for b in range(w.B):
+        for h in range(w.H):
+            sl = lambda a: a[b:b + 1, h:h + 1]
+            OA.attention(sl(inp["q"]), sl(inp["k_img"]), sl(inp["v_img"]), sl(inp["k_txt"]), sl(inp["v_txt"]),
+                         (w.tv[b],), rows=rows)
+            flops += 4.0 * R * (w.N + w.tv[b]) * w.d
+            done += 1
+            if time.perf_counter() - t0 > budget_s:
+                return flops, time.perf_counter() - t0, done
+    return flops, time.perf_counter() - t0, done
+
+
+def cpu_baseline(w, inp, rows_S, budget_s: float, large: bool):
+    """The fp64 oracle as it stands, on bounded samples of the benchmark's attention work, on this host's
+    cores: dense and sensitive-row attention of the 1024^2 step (heads in order until a time budget is
+    spent), and the 2560^2 / 3072^2 attention on a 1/64 sample of query rows across every (b, h), scaled
+    linearly to the full launch (the cost is linear in the rows at fixed keys)."""
+    import numpy as np
+    import synthetic as syn
 
     try:
         from threadpoolctl import threadpool_info
@@ -647,27 +773,30 @@ def cpu_baseline(w, inp, budget_s: float):
     except Exception:  # pragma: no cover
         blas = 1
     cores = len(os.sched_getaffinity(0))
-    rows = None  # every query row of each (b, h) visited
-    flops = 0.0
-    done = 0
-    t0 = time.perf_counter()
-    for b in range(w.B):
-        for h in range(w.H):
-            sl = lambda a: a[b:b + 1, h:h + 1]
-            OA.attention(sl(inp["q"]), sl(inp["k_img"]), sl(inp["v_img"]), sl(inp["k_txt"]), sl(inp["v_txt"]),
-                         (w.tv[b],), rows=rows)
-            flops += 4.0 * w.N * (w.N + w.tv[b]) * w.d
-            done += 1
-            if time.perf_counter() - t0 > budget_s:
-                break
-        if time.perf_counter() - t0 > budget_s:
-            break
-    el = time.perf_counter() - t0
-    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": min(cores, blas) if blas else cores,
+    fl, el, done = _oracle_heads(w, inp, None, budget_s)
+    legs = {}
+    fr, er, dr = _oracle_heads(w, inp, np.asarray(rows_S, dtype=np.int64), budget_s / 3)
+    legs["rows_1024"] = {"value": fr / er / 1e12, "unit": "TFLOP/s", "s": er,
+                         "sample": f"sensitive rows (|S| = {len(rows_S)}) of {dr} of the {w.B * w.H} heads"}
+    if large:
+        for name in ("srsu_2560", "traj_3072"):
+            wl = syn.WORKLOADS[name]
+            li = syn.attention_inputs(wl)
+            sample = np.arange(0, wl.N, 64)
+            fs, es, ds = _oracle_heads(wl, li, sample, 1e9)
+            full = wl.flops_dense
+            legs["dense_" + name.split("_")[1] + "_rows_1_in_64"] = {
+                "value": fs / es / 1e12, "unit": "TFLOP/s", "sample_s": es,
+                "scaled_full_launch_s": es * full / fs,
+                "sample": f"{name}: every 64th query row ({len(sample)} of {wl.N}) of all {ds} heads; the scaled "
+                          f"figure is the time the whole dense launch ({full / 1e12:.2f} TFLOP) would take"}
+            del li
+    return {"value": fl / el / 1e12, "unit": "TFLOP/s", "cores": min(cores, blas) if blas else cores,
             "kind": "oracle",
             "sample": f"fp64 numpy oracle dense attention (all {w.N} query rows) of {done} of the "
                       f"{w.B * w.H} (b,h) heads of srsu_1024, stopped after a {budget_s:.0f} s budget ({el:.1f} s); "
-                      f"host affinity {cores} cores, BLAS threads {blas}"}
+                      f"host affinity {cores} cores, BLAS threads {blas}",
+            "legs": legs}
 
 
 if __name__ == "__main__":
