@@ -22,7 +22,7 @@ EXPORTS = ("safe_attn_dense", "safe_attn_rows", "safe_mask_is_row_constant", "sa
            "safe_pcsp_partition", "safe_swcfg_combine", "safe_gather_rows", "safe_scatter_rows",
            "safe_affinity_accumulate", "safe_percentile_count", "safe_stepcache_extrapolate",
            "safe_stepcache_plan", "safe_trajectory_plan", "safe_rows_ffn", "safe_rows_ffn_workspace_bytes",
-           "safe_rows_qkv",
+           "safe_rows_qkv", "safe_rows_ffn_noalloc", "safe_rows_ffn_noalloc_max_bytes",
            "safe_status_string", "safe_version")
 
 
@@ -79,9 +79,12 @@ def load(path: Optional[str] = None):
     lib.safe_rows_ffn.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.safe_rows_ffn_workspace_bytes.argtypes = [i32, i32, i32]
     lib.safe_rows_qkv.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp]
+    lib.safe_rows_ffn_noalloc.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp]
+    lib.safe_rows_ffn_noalloc_max_bytes.argtypes = []
     for name in EXPORTS[:-2]:
         getattr(lib, name).restype = i32
     lib.safe_rows_ffn_workspace_bytes.restype = ctypes.c_size_t
+    lib.safe_rows_ffn_noalloc_max_bytes.restype = ctypes.c_size_t
     lib.safe_status_string.argtypes = [i32]
     lib.safe_status_string.restype = ctypes.c_char_p
     lib.safe_version.argtypes = []
@@ -303,6 +306,20 @@ def safe_rows_ffn(x, rows, w1, b1, w2, b2, cache, ws, stream=None):
                                 _ptr(b2), _ptr(cache), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
            "safe_rows_ffn")
     return cache
+
+
+def safe_rows_ffn_noalloc(x, rows, w1, b1, w2, b2, cache, stream=None):
+    """safe_rows_ffn without a workspace: the hidden activation lives in the library's fixed per-GPU array
+    (safe_rows_ffn_noalloc; at most safe_rows_ffn_noalloc_max_bytes() bytes)."""
+    B, N, D = x.shape
+    F = w1.shape[0]
+    _check(load().safe_rows_ffn_noalloc(_ptr(x), _ptr(rows), rows.numel(), B, N, D, F, _ptr(w1), _ptr(b1), _ptr(w2),
+                                        _ptr(b2), _ptr(cache), _stream(stream)), "safe_rows_ffn_noalloc")
+    return cache
+
+
+def safe_rows_ffn_noalloc_max_bytes() -> int:
+    return int(load().safe_rows_ffn_noalloc_max_bytes())
 
 
 def safe_rows_qkv(x, rows, wqkv, bqkv, q, k_cache, v_cache, stream=None):

@@ -9,7 +9,8 @@
  * Conventions shared by every call
  * - Every tensor pointer is caller-owned DEVICE memory unless the argument says "host".  Tensors are
  *   dense, row-major, with the last dimension contiguous.  The library allocates nothing, keeps no
- *   pointer after a call returns and holds no state besides its loaded code objects.
+ *   pointer after a call returns and holds no state besides its loaded code objects (which include the
+ *   fixed scratch array of safe_rows_ffn_noalloc) and the per-device address of that array.
  * - Work is enqueued on `stream` (NULL = the default stream) and is asynchronous unless stated.
  * - Arguments are validated before anything is launched.  On a validation failure a non-zero
  *   status is returned, nothing is launched and no output is written.  A launch failure returns
@@ -271,6 +272,22 @@ size_t safe_rows_ffn_workspace_bytes(int32_t B, int32_t k, int32_t F);
 safe_status safe_rows_qkv(const void* x, const int32_t* rows, int32_t k, int32_t B, int32_t N, int32_t H, int32_t d,
                           const void* wqkv, const float* bqkv, void* q, void* k_cache, void* v_cache,
                           hipStream_t stream);
+
+/*
+ * Allocation-free form of safe_rows_ffn, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc).  Same operation, arguments, layouts
+ * and kernels as safe_rows_ffn, without the workspace: the bf16 hidden activation (B * k * F * 2 bytes) lives
+ * in a fixed device array of the library, one per GPU, of safe_rows_ffn_noalloc_max_bytes() bytes (32 MiB;
+ * the 1024^2 block, B = 2, k = 1229, F = 6144, needs 30.2 MB).  A larger request returns SAFE_ERR_WORKSPACE
+ * and launches nothing.  The array is looked up on the current device, which must be the stream's.  Calls
+ * that overlap on one GPU (other streams or threads) share the array and race; calls on different GPUs do
+ * not.  The call allocates nothing (no hipMalloc, no allocating library routine); the array is reserved
+ * when the library's code object is loaded on the GPU and is held until the process ends.
+ */
+safe_status safe_rows_ffn_noalloc(const void* x, const int32_t* rows, int32_t k, int32_t B, int32_t N, int32_t D,
+                                  int32_t F, const void* w1, const float* b1, const void* w2, const float* b2,
+                                  void* cache, hipStream_t stream);
+size_t safe_rows_ffn_noalloc_max_bytes(void);
 
 /* Human-readable name of a status code (static storage). */
 const char* safe_status_string(safe_status s);
