@@ -14,12 +14,12 @@ CFG_REL = 1e-5
 # dimension.  The whole-tensor bounds above average over tens of thousands of rows, so on their own they
 # would let a few wholly wrong rows through (at the N(0,1)*0.125 workloads |o| stays below 1e-2, so the
 # max-abs bound cannot fail, and one zeroed row-head among 59k adds only ~4e-3 to the relative L2).
-# Bounds from the measured distribution of the worst row over every parity case (bf16: the largest
-# measured worst row, about 6e-3 on the sharply peaked stress rows and 4-5e-3 on the full-size launches,
-# times ~2.5; fp32: about 1e-6, times 20).  A row with a missing key tile, a wrong row index or a zero
-# output lands between 1e-1 and 1.
-BF16_ROW_REL = 1.5e-2
-F32_ROW_REL = 2e-5
+# Bounds from the measured distribution of the worst row over every parity case on MI355X (bf16: 121
+# assertions, worst 5.2e-3 on the logit-std-3 stress rows, 2.8-3.3e-3 on the full-size 1024^2 / 2560^2 /
+# 3072^2 launches, 2.5-2.6e-3 on the block products; fp32: worst 8.9e-7), about twice the worst case.
+# A row with a missing key tile, a wrong row index or a zero output lands between 1e-1 and 1.
+BF16_ROW_REL = 1e-2
+F32_ROW_REL = 2e-6
 ROW_STATS = []  # (what, dtype, worst row, rel-L2) of every assert_close call, for the run's summary
 
 
