@@ -43,6 +43,9 @@ def parse():
     ap.add_argument("--no-large", action="store_true", help="skip the 2560^2 attention lines")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 256 MiB device copy (for scaling HBM byte counters)")
+    ap.add_argument("--hbm-only", action="store_true",
+                    help="run only the HBM-bound stages (batched / cold / cache-resident) and print them; for "
+                         "profiling those launches")
     return ap.parse_args()
 
 
@@ -62,6 +65,14 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dts.load()
     dev = torch.device("cuda:0")
+    if args.hbm_only:
+        gbs_ = lambda b, ms: b / (ms * 1e-3) / 1e9
+        hbm_ = lambda b, ms: {"ms": ms, "gbs": gbs_(b, ms), "frac_hbm": gbs_(b, ms) / HBM_PEAK_GBS, "bytes": b}
+        out = {"hbm": hbm_stages(dts, torch, np, syn, dev, hbm_)}
+        if args.copy_calibration:
+            out["copy_calibration_bytes"] = copy_calibration(torch, dev)
+        print(json.dumps(out), flush=True)
+        return
     w = syn.WORKLOADS["srsu_1024"]
     B, H, N, T, d, k = w.B, w.H, w.N, w.T, w.d, w.k
     Tv = w.tv[0]
@@ -338,16 +349,14 @@ def main():
     # head dim 128 at the 1024^2 grid (24 heads x 128): the same path at the other head dim the library takes
     result["attention_d128_1024"] = attention_large(dts, torch, syn, dev, syn.WORKLOADS["dense_1024_d128"], stream,
                                                     reps=10)[-1]
+    result["attention_fp8_1024"] = attention_fp8(dts, torch, syn, dev, syn.WORKLOADS["srsu_1024"])
+    if not args.no_large:
+        result["attention_fp8_2560"] = attention_fp8(dts, torch, syn, dev, syn.WORKLOADS["srsu_2560"], reps=3)
     result["aesmask_stepcache"] = next_rows(dts, torch, np, syn, dev, hbm, not args.no_large)
     result["srsu_block"] = srsu_block(dts, torch, np, syn, dev)
 
     if args.copy_calibration:
-        src = torch.empty(64 << 20, dtype=torch.float32, device=dev).fill_(1.0)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        result["copy_calibration_bytes"] = {"read": src.numel() * 4, "write": dst.numel() * 4}
+        result["copy_calibration_bytes"] = copy_calibration(torch, dev)
 
     # ---------------------------------------------------------------- oracle on the host cores
     if not args.no_cpu_baseline:
@@ -357,6 +366,16 @@ def main():
 
 
 _SLEEP_CYCLES_PER_MS = []
+
+
+def copy_calibration(torch, dev):
+    """One plain 256 MiB device copy, whose FETCH_SIZE / WRITE_SIZE counts scale the byte counters."""
+    src = torch.empty(64 << 20, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    return {"read": src.numel() * 4, "write": dst.numel() * 4}
 
 
 def gpu_busy(torch, ms=1.0):
@@ -433,6 +452,39 @@ def attention_large(dts, torch, syn, dev, wl, stream, reps=5):
             "rows_ms": timing["rows"], "rows_tflops": tfr, "rows_frac_mfma": tfr / MFMA_BF16_PEAK_TFLOPS,
             "reps": reps}
     return q, ki, vi, kt, vt, rows, out, line
+
+
+def attention_fp8(dts, torch, syn, dev, wl, reps=10):
+    """The fp8 path (E4M3 Q and K with per-(b,h) factors, bf16 V and output) on a workload's shapes: seeded
+    N(0,1)*std draws quantised per head on the device, `reps` back-to-back launches between one event pair.
+    Besides the bf16 peak, the fraction is given against the peak of this mix: the Q K^T half of the flops
+    at the fp8 rate (5.0 PFLOP/s), the P V half at the bf16 rate (2.5 PFLOP/s), i.e. 3.33 PFLOP/s."""
+    g = torch.Generator(device=dev)
+    g.manual_seed(wl.seed + 7)
+    mk = lambda n: torch.randn((wl.B, wl.H, n, wl.d), generator=g, device=dev) * wl.std
+
+    def quant(*xs):
+        amax = torch.stack([x.abs().amax(dim=(2, 3)) for x in xs]).amax(dim=0)
+        sc = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax)).float()
+        return [(x / sc[:, :, None, None]).to(torch.float8_e4m3fn) for x in xs], sc.reshape(-1).contiguous()
+
+    (q,), qd = quant(mk(wl.N))
+    (ki, kt), kd = quant(mk(wl.N), mk(wl.T))
+    vi, vt = mk(wl.N).to(torch.bfloat16), mk(wl.T).to(torch.bfloat16)
+    rows = torch.from_numpy(syn.random_rows(wl)).to(dev)
+    out = torch.zeros(q.shape, dtype=torch.bfloat16, device=dev)
+    mixed_peak = 2.0 / (1.0 / 5000.0 + 1.0 / 2500.0)
+    line = {"workload": f"{wl.name} fp8 Q/K: B={wl.B}, H={wl.H}, d={wl.d}, N={wl.N}, Tv={wl.tv[0]}, |S|={wl.k}",
+            "reps": reps, "mixed_peak_tflops": mixed_peak}
+    for name, fn, fl in (("dense", lambda: dts.safe_attn_dense(q, ki, vi, kt, vt, wl.tv, out, q_descale=qd, k_descale=kd),
+                          wl.flops_dense),
+                         ("rows", lambda: dts.safe_attn_rows(q, ki, vi, kt, vt, wl.tv, rows, out, q_descale=qd,
+                                                             k_descale=kd), wl.flops_rows)):
+        ms = time_launches(torch, fn, reps=reps)
+        tf = fl / (ms * 1e-3) / 1e12
+        line.update({f"{name}_ms": ms, f"{name}_tflops": tf, f"{name}_frac_bf16_peak": tf / MFMA_BF16_PEAK_TFLOPS,
+                     f"{name}_frac_mixed_peak": tf / mixed_peak})
+    return line
 
 
 def time_launches(torch, fn, reps=20):

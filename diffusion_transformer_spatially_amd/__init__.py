@@ -14,7 +14,7 @@ from typing import Optional, Sequence
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libsafe_attn.so")
 
-SAFE_DTYPE_BF16, SAFE_DTYPE_F32, SAFE_DTYPE_BOOL = 0, 1, 2
+SAFE_DTYPE_BF16, SAFE_DTYPE_F32, SAFE_DTYPE_BOOL, SAFE_DTYPE_FP8_E4M3 = 0, 1, 2, 3
 SAFE_MAX_BATCH = 64
 SAFE_STEP_DENSE, SAFE_STEP_ROWS = 0, 1
 EXPORTS = ("safe_attn_dense", "safe_attn_rows", "safe_mask_is_row_constant", "safe_mask_check_launch",
@@ -44,7 +44,7 @@ class safe_attn_desc(ctypes.Structure):
         ("mask", ctypes.c_void_p), ("mask_dtype", ctypes.c_int32), ("mask_B", ctypes.c_int32),
         ("mask_H", ctypes.c_int32), ("mask_cols", ctypes.c_int32),
         ("out", ctypes.c_void_p), ("lse", ctypes.c_void_p), ("xattn_out", ctypes.c_void_p),
-        ("lse_img_out", ctypes.c_void_p),
+        ("lse_img_out", ctypes.c_void_p), ("q_descale", ctypes.c_void_p), ("k_descale", ctypes.c_void_p),
     ]
 
 
@@ -131,19 +131,30 @@ def _dtype_code(t) -> int:
         return SAFE_DTYPE_F32
     if t.dtype == torch.bool:
         return SAFE_DTYPE_BOOL
+    if t.dtype == torch.float8_e4m3fn:
+        return SAFE_DTYPE_FP8_E4M3
     raise ValueError(f"unsupported dtype {t.dtype}")
 
 
 def _desc(q, k_img, v_img, k_txt, v_txt, text_valid_len: Sequence[int], out, scale, mask, lse, xattn_out,
-          lse_img_out):
+          lse_img_out, q_descale=None, k_descale=None):
+    torch = _torch()
     B, H, N, d = q.shape
     T = k_txt.shape[2] if k_txt is not None else 0
     tv = (ctypes.c_int32 * max(1, len(text_valid_len)))(*[int(x) for x in text_valid_len])
     if len(text_valid_len) != B:
         raise ValueError("text_valid_len needs one entry per batch element")
-    for t in (k_img, v_img, out):
-        if tuple(t.shape) != (B, H, N, d) or t.dtype != q.dtype:
-            raise ValueError("q, k_img, v_img and out must share shape [B,H,N,d] and dtype")
+    fp8 = q.dtype == torch.float8_e4m3fn
+    vdt = torch.bfloat16 if fp8 else q.dtype  # fp8 Q / K come with bf16 V and output
+    for t, dt in ((k_img, q.dtype), (v_img, vdt), (out, vdt)):
+        if tuple(t.shape) != (B, H, N, d) or t.dtype != dt:
+            raise ValueError("q, k_img, v_img and out must share shape [B,H,N,d]; k_img the dtype of q; v_img and "
+                             "out the dtype of q, or bf16 when q is fp8")
+    if k_txt is not None and (k_txt.dtype != q.dtype or v_txt.dtype != vdt):
+        raise ValueError("k_txt / v_txt must have the dtypes of k_img / v_img")
+    for f in (q_descale, k_descale):
+        if f is not None and (f.dtype != torch.float32 or f.numel() != B * H):
+            raise ValueError("q_descale / k_descale must be fp32 with B*H entries")
     if k_txt is not None and (tuple(k_txt.shape) != (B, H, T, d) or tuple(v_txt.shape) != (B, H, T, d)):
         raise ValueError("k_txt and v_txt must be [B,H,T,d]")
     D = safe_attn_desc()
@@ -163,25 +174,30 @@ def _desc(q, k_img, v_img, k_txt, v_txt, text_valid_len: Sequence[int], out, sca
     D.lse = _ptr(lse)
     D.xattn_out = _ptr(xattn_out)
     D.lse_img_out = _ptr(lse_img_out)
+    D.q_descale = _ptr(q_descale)
+    D.k_descale = _ptr(k_descale)
     return D, tv
 
 
 # ----------------------------------------------------------------------------- entry points
 def safe_attn_dense(q, k_img, v_img, k_txt, v_txt, text_valid_len, out, scale=0.0, mask=None, lse=None,
-                    xattn_out=None, lse_img_out=None, stream=None):
-    """Dense anchor step: all N image rows of `out` (safe_attn_dense)."""
-    D, _keep = _desc(q, k_img, v_img, k_txt, v_txt, text_valid_len, out, scale, mask, lse, xattn_out, lse_img_out)
+                    xattn_out=None, lse_img_out=None, stream=None, q_descale=None, k_descale=None):
+    """Dense anchor step: all N image rows of `out` (safe_attn_dense).  fp8 (float8_e4m3fn) q / k take
+    bf16 v / out and optional fp32 [B, H] dequantisation factors q_descale / k_descale."""
+    D, _keep = _desc(q, k_img, v_img, k_txt, v_txt, text_valid_len, out, scale, mask, lse, xattn_out, lse_img_out,
+                     q_descale, k_descale)
     _check(load().safe_attn_dense(ctypes.byref(D), _stream(stream)), "safe_attn_dense")
     return out
 
 
 def safe_attn_rows(q, k_img, v_img, k_txt, v_txt, text_valid_len, rows, out, scale=0.0, mask=None, lse=None,
-                   xattn_out=None, lse_img_out=None, stream=None):
+                   xattn_out=None, lse_img_out=None, stream=None, q_descale=None, k_descale=None):
     """Sensitive-row step: rows[] of `out` only, against the global keys (safe_attn_rows)."""
     torch = _torch()
     if rows.dtype != torch.int32 or rows.dim() != 1:
         raise ValueError("rows must be a 1-D int32 tensor")
-    D, _keep = _desc(q, k_img, v_img, k_txt, v_txt, text_valid_len, out, scale, mask, lse, xattn_out, lse_img_out)
+    D, _keep = _desc(q, k_img, v_img, k_txt, v_txt, text_valid_len, out, scale, mask, lse, xattn_out, lse_img_out,
+                     q_descale, k_descale)
     _check(load().safe_attn_rows(ctypes.byref(D), _ptr(rows), rows.numel(), _stream(stream)), "safe_attn_rows")
     return out
 

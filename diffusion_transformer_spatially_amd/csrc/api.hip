@@ -16,7 +16,8 @@ safe_status from_hip(hipError_t e) { return e == hipSuccess ? SAFE_OK : SAFE_ERR
 
 safe_status check_attn(const safe_attn_desc* d) {
   if (d == nullptr) return SAFE_ERR_NULL;
-  if (d->dtype != SAFE_DTYPE_BF16 && d->dtype != SAFE_DTYPE_F32) return SAFE_ERR_DTYPE;
+  if (d->dtype != SAFE_DTYPE_BF16 && d->dtype != SAFE_DTYPE_F32 && d->dtype != SAFE_DTYPE_FP8_E4M3)
+    return SAFE_ERR_DTYPE;
   if (d->B < 1 || d->H < 1 || d->N < 1 || d->T < 0 || d->d < 1) return SAFE_ERR_SHAPE;
   if (d->B > SAFE_MAX_BATCH) return SAFE_ERR_UNSUPPORTED;
   if (d->d != 64 && d->d != 128) return SAFE_ERR_UNSUPPORTED;
@@ -42,6 +43,13 @@ safe_status check_attn(const safe_attn_desc* d) {
     if (!(d->mask_cols == d->N || d->mask_cols == d->N + d->T)) return SAFE_ERR_SHAPE;
     if (d->mask_dtype == SAFE_DTYPE_F32 && (reinterpret_cast<uintptr_t>(d->mask) & 3u) != 0) return SAFE_ERR_ALIGN;
   }
+  if (d->dtype == SAFE_DTYPE_FP8_E4M3) {
+    // fp8 Q / K: the mask-free fast path at head dim 64 only
+    if (d->d != 64 || d->mask != nullptr || d->lse != nullptr || d->xattn_out != nullptr || d->lse_img_out != nullptr)
+      return SAFE_ERR_UNSUPPORTED;
+    if ((reinterpret_cast<uintptr_t>(d->q_descale) & 3u) != 0 || (reinterpret_cast<uintptr_t>(d->k_descale) & 3u) != 0)
+      return SAFE_ERR_ALIGN;
+  }
   return SAFE_OK;
 }
 
@@ -63,6 +71,8 @@ AttnArgs make_args(const safe_attn_desc* d, const int32_t* rows, int R) {
   a.mask_B = d->mask_B;
   a.mask_H = d->mask_H;
   a.mask_cols = d->mask_cols;
+  a.q_descale = d->dtype == SAFE_DTYPE_FP8_E4M3 ? d->q_descale : nullptr;
+  a.k_descale = d->dtype == SAFE_DTYPE_FP8_E4M3 ? d->k_descale : nullptr;
   a.B = d->B;
   a.H = d->H;
   a.N = d->N;
@@ -86,6 +96,7 @@ bool mfma_takes_mask(const safe_attn_desc* d) {
 safe_status run_attn(const safe_attn_desc* d, const int32_t* rows, int R, hipStream_t s) {
   const AttnArgs a = make_args(d, rows, R);
   if (R == 0) return SAFE_OK;
+  if (d->dtype == SAFE_DTYPE_FP8_E4M3) return from_hip(launch_attn_mfma_fp8(a, s));
   if (d->dtype == SAFE_DTYPE_BF16 && (d->mask == nullptr || mfma_takes_mask(d)))
     return from_hip(launch_attn_mfma_bf16(a, d->d, s));
   return from_hip(launch_attn_generic(a, d->dtype, d->d, s));

@@ -48,6 +48,8 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) uint16_t lds_u16;
 
@@ -83,22 +85,25 @@ template <int D>
 __device__ __forceinline__ int lds_off(int key, int chunk) { return key * D + ((chunk ^ swz<D>(key)) << 3); }
 
 struct TileSrc {
-  const uint16_t* k;
+  const uint16_t* k;  // bf16 K rows (D elements), or fp8 K rows (D bytes) read through k8
   const uint16_t* v;
   int nvalid;
+  __device__ const uint8_t* k8() const { return reinterpret_cast<const uint8_t*>(k); }
 };
 
-template <int D>
+// FP8: K rows are D bytes (fp8 E4M3) instead of 2D; V stays bf16.
+template <int D, bool FP8 = false>
 __device__ __forceinline__ TileSrc tile_src(const AttnArgs& a, size_t bh, int t, int n_img, int tv) {
+  constexpr size_t kRowK = FP8 ? D : 2 * D;  // bytes per K row
   TileSrc s;
   if (t < n_img) {
     const int j0 = t * kBN;
-    s.k = static_cast<const uint16_t*>(a.k_img) + (bh * a.N + j0) * D;
+    s.k = reinterpret_cast<const uint16_t*>(static_cast<const uint8_t*>(a.k_img) + (bh * a.N + j0) * kRowK);
     s.v = static_cast<const uint16_t*>(a.v_img) + (bh * a.N + j0) * D;
     s.nvalid = min(kBN, a.N - j0);
   } else {
     const int j0 = (t - n_img) * kBN;
-    s.k = static_cast<const uint16_t*>(a.k_txt) + (bh * a.T + j0) * D;
+    s.k = reinterpret_cast<const uint16_t*>(static_cast<const uint8_t*>(a.k_txt) + (bh * a.T + j0) * kRowK);
     s.v = static_cast<const uint16_t*>(a.v_txt) + (bh * a.T + j0) * D;
     s.nvalid = min(kBN, tv - j0);
   }
@@ -115,13 +120,29 @@ __device__ __forceinline__ TileSrc tile_src(const AttnArgs& a, size_t bh, int t,
 // through an empty asm, so the compiler cannot treat the LDS destinations derived from it as loop
 // invariants; it recomputes them per tile (two scalar adds) instead of hoisting all of them out of the
 // tile loop, where they were spilled and each reload waited for the tile copies already in flight.
-template <int D, bool OPAQUE>
+// FP8 K tiles (head dim 64): 64-byte key rows, four 16-byte chunks; chunk c of key row r sits in LDS slot
+// 4r + (c ^ swz8(r)).  The K operand read of a lane half takes chunks (2g, 2g + 1) of 16 key rows that
+// differ in row bits {0, 1, 2, 4}: rows with equal bits 0-1 share a 16-byte bank quad of the 256-byte
+// window unless their chunks differ, which row bits 2 and 4 ensure, so each read is conflict-free.
+__device__ __forceinline__ int swz8(int key) { return ((key >> 2) & 1) | (((key >> 4) & 1) << 1); }
+__device__ __forceinline__ int lds8_off(int key, int chunk) { return key * 64 + ((chunk ^ swz8(key)) << 4); }  // bytes
+
+template <int D, bool OPAQUE, bool FP8 = false>
 __device__ __forceinline__ void stage_issue(const TileSrc& s, uint16_t* kl, uint16_t* vl) {
   constexpr int kChunks = D / 8;                // 16-byte chunks per key row
   constexpr int kChunkShift = D == 64 ? 3 : 4;  // log2(kChunks)
   const int lane = threadIdx.x & 63;
   int wslot = __builtin_amdgcn_readfirstlane(static_cast<int>((threadIdx.x >> 6) & 3)) * 64;
   if (OPAQUE) asm volatile("" : "+s"(wslot));
+  if constexpr (FP8) {
+    static_assert(D == 64, "fp8 K tiles at head dim 64");
+    const int p = wslot + lane;  // one 16-byte slot per thread: 64 rows x 4 chunks
+    const int row = p >> 2;
+    const int c = (p & 3) ^ swz8(row);
+    const int srow = row < s.nvalid ? row : s.nvalid - 1;
+    __builtin_amdgcn_global_load_lds(static_cast<const void*>(s.k8() + srow * 64 + c * 16),
+                                     (__attribute__((address_space(3))) void*)(kl + wslot * 8), 16, 0, 0);
+  }
 #pragma unroll
   for (int u = 0; u < kBN * kChunks / (kWaves * 64); ++u) {
     const int base = u * kWaves * 64 + wslot;  // first slot of this wave instruction
@@ -129,8 +150,9 @@ __device__ __forceinline__ void stage_issue(const TileSrc& s, uint16_t* kl, uint
     const int row = p >> kChunkShift;
     const int c = (p & (kChunks - 1)) ^ swz<D>(row);
     const int srow = row < s.nvalid ? row : s.nvalid - 1;
-    __builtin_amdgcn_global_load_lds(static_cast<const void*>(s.k + srow * D + c * 8),
-                                     (__attribute__((address_space(3))) void*)(kl + base * 8), 16, 0, 0);
+    if constexpr (!FP8)
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(s.k + srow * D + c * 8),
+                                       (__attribute__((address_space(3))) void*)(kl + base * 8), 16, 0, 0);
     __builtin_amdgcn_global_load_lds(static_cast<const void*>(s.v + srow * D + c * 8),
                                      (__attribute__((address_space(3))) void*)(vl + base * 8), 16, 0, 0);
   }
@@ -153,20 +175,51 @@ __device__ __forceinline__ void stage_offsets(uint32_t (&off)[D / 32]) {
   }
 }
 
-template <int D, bool OPAQUE>
-__device__ __forceinline__ void stage_issue_full(const TileSrc& s, uint16_t* kl, uint16_t* vl, const uint32_t (&off)[D / 32]) {
+// koff8: the fp8 K copy's per-lane byte offset within a full tile (FP8 only).
+__device__ __forceinline__ uint32_t stage8_offset() {
+  const int p = static_cast<int>(threadIdx.x & 255);
+  const int row = p >> 2;
+  return static_cast<uint32_t>(row * 64 + (((p & 3) ^ swz8(row)) << 4));
+}
+
+template <int D, bool OPAQUE, bool FP8 = false>
+__device__ __forceinline__ void stage_issue_full(const TileSrc& s, uint16_t* kl, uint16_t* vl, const uint32_t (&off)[D / 32],
+                                                 uint32_t koff8 = 0) {
   int wslot = __builtin_amdgcn_readfirstlane(static_cast<int>((threadIdx.x >> 6) & 3)) * 64;
   if (OPAQUE) asm volatile("" : "+s"(wslot));
   const char* kb = reinterpret_cast<const char*>(s.k);
   const char* vb = reinterpret_cast<const char*>(s.v);
+  if constexpr (FP8)
+    __builtin_amdgcn_global_load_lds(static_cast<const void*>(kb + koff8),
+                                     (__attribute__((address_space(3))) void*)(kl + wslot * 8), 16, 0, 0);
 #pragma unroll
   for (int u = 0; u < D / 32; ++u) {
     const int base = u * kWaves * 64 + wslot;
-    __builtin_amdgcn_global_load_lds(static_cast<const void*>(kb + off[u]),
-                                     (__attribute__((address_space(3))) void*)(kl + base * 8), 16, 0, 0);
+    if constexpr (!FP8)
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(kb + off[u]),
+                                       (__attribute__((address_space(3))) void*)(kl + base * 8), 16, 0, 0);
     __builtin_amdgcn_global_load_lds(static_cast<const void*>(vb + off[u]),
                                      (__attribute__((address_space(3))) void*)(vl + base * 8), 16, 0, 0);
   }
+}
+
+// S^T block of 32 keys x 32 queries over the whole head dim (64) from fp8 K and Q on the gfx950 fp8 matrix
+// instruction (format 0 = E4M3 for both operands; block scales 2^0).  Each lane half g holds bytes
+// 32g .. 32g + 31 of its row of K (A) and of Q (B): whatever order the instruction gives the 64 products,
+// both operands follow the same one, so the sum is the full dot product.
+__device__ __forceinline__ f32x16 mfma_fp8(bf16x8 a0, bf16x8 a1, bf16x8 b0, bf16x8 b1, const f32x16& c) {
+  const i32x8 av = __builtin_shufflevector(__builtin_bit_cast(i32x4, a0), __builtin_bit_cast(i32x4, a1), 0, 1, 2, 3, 4, 5,
+                                           6, 7);
+  const i32x8 bv = __builtin_shufflevector(__builtin_bit_cast(i32x4, b0), __builtin_bit_cast(i32x4, b1), 0, 1, 2, 3, 4, 5,
+                                           6, 7);
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c, 0, 0, 0, 127, 0, 127);
+}
+
+// A lane's fp8 K operand of key row `key` (chunks 2g and 2g + 1).
+__device__ __forceinline__ void read_k8(bf16x8 (&ka)[2], const uint16_t* kl, int key, int g) {
+  const uint8_t* kb = reinterpret_cast<const uint8_t*>(kl);
+  ka[0] = *reinterpret_cast<const bf16x8*>(kb + lds8_off(key, 2 * g));
+  ka[1] = *reinterpret_cast<const bf16x8*>(kb + lds8_off(key, 2 * g + 1));
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
@@ -436,14 +489,180 @@ __device__ __forceinline__ void tile_step_fast2(WaveState<2, 64>& st, const uint
         st.o[1][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[kb][mm][db], p1[kb][mm], st.o[1][db], 0, 0, 0);
 }
 
-template <int QB, bool MASKED, int KM, int D>
+// soft_chunk on raw fp8 dot products: each probability is exp2(s * c2 - m), c2 = scale * log2(e) times the
+// (b,h) dequantisation factors of Q and K (the fp8 operands cannot carry the scale, so the fma that the
+// bf16 path folds into a pre-scaled Q is paid per logit here; the logit chains start at zero instead).
+__device__ __forceinline__ void soft_chunk_sc(uint32_t (&pk)[2][2][4], const f32x16 (&s)[2], float& tsum, int c, float c2,
+                                              float nm) {
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  const int kb = c >> 2, mm = (c >> 1) & 1, h = c & 1;
+  const int i0 = 8 * mm + 4 * h;
+  const uint32_t w0 = pack_bf16x2(__builtin_amdgcn_exp2f(fmaf(s[kb][i0 + 0], c2, nm)),
+                                  __builtin_amdgcn_exp2f(fmaf(s[kb][i0 + 1], c2, nm)));
+  const uint32_t w1 = pack_bf16x2(__builtin_amdgcn_exp2f(fmaf(s[kb][i0 + 2], c2, nm)),
+                                  __builtin_amdgcn_exp2f(fmaf(s[kb][i0 + 3], c2, nm)));
+  pk[kb][mm][2 * h] = w0;
+  pk[kb][mm][2 * h + 1] = w1;
+  tsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w0), ones, tsum, false);
+  tsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w1), ones, tsum, false);
+}
+
+// Logits of a tile in log2 units minus m (s * c2 - m), keys past nvalid at -inf (partial fp8 tiles).
+template <bool MASKED>
+__device__ __forceinline__ void scale_logits(f32x16 (&s)[2], float c2, float nm, int g, int nvalid) {
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float v = fmaf(s[kb][i], c2, nm);
+      s[kb][i] = (!MASKED || (kb * 32 + 16 * g + i) < nvalid) ? v : -INFINITY;
+    }
+}
+
+// Exact path of one fp8 query block (rare): logits again from K in LDS, tile max in log2 units, rescale,
+// probabilities again.
+template <bool MASKED>
+__device__ __forceinline__ float fast_exact_fp8(bf16x8 (&p)[2][2], bf16x8 q0, bf16x8 q1, float& m, float& l,
+                                                f32x16 (&o)[2], const uint16_t* kl, int kperm, int g, int nvalid,
+                                                float c2) {
+  f32x16 sx[2];
+  const f32x16 zero = {};
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    bf16x8 ka[2];
+    read_k8(ka, kl, kb * 32 + kperm, g);
+    sx[kb] = mfma_fp8(ka[0], ka[1], q0, q1, zero);
+  }
+  scale_logits<MASKED>(sx, c2, 0.f, g, nvalid);
+  float mx = -INFINITY;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sx[kb][i]);
+  mx = fmaxf(mx, swap_halves(mx));
+  const float mnew = fmaxf(m, mx);
+  if (mnew > m) {
+    const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+    l *= alpha;
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+    m = mnew;
+  }
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sx[kb][i] -= m;
+  return fast_probs<false>(p, sx, g, kBN);
+}
+
+// Two fp8 query blocks, staggered as in tile_step_fast2: logits of block 0 (one fp8 instruction per 32-key
+// half); logits of block 1 beside the softmax of block 0; output update of block 0 (bf16 P V) beside the
+// softmax of block 1; output update of block 1.
+template <bool MASKED>
+__device__ __forceinline__ void tile_step_fast2_fp8(WaveState<2, 64>& st, const uint16_t* kl, const uint16_t* vl, int kperm,
+                                                    int g, int li, int dc0, float c2, int nvalid) {
+  bf16x8 ka[2][2];
+  read_k8(ka[0], kl, kperm, g);
+  read_k8(ka[1], kl, 32 + kperm, g);
+  const f32x16 zero = {};
+  f32x16 s0[2], s1[2];
+  s0[0] = mfma_fp8(ka[0][0], ka[0][1], st.q[0][0], st.q[0][1], zero);
+  s0[1] = mfma_fp8(ka[1][0], ka[1][1], st.q[0][0], st.q[0][1], zero);
+  const float nm0 = -st.m[0], nm1 = -st.m[1];
+  if (MASKED) scale_logits<true>(s0, c2, nm0, g, nvalid);
+  __builtin_amdgcn_sched_barrier(0);
+  // logits of block 1 | softmax of block 0
+  uint32_t pk0[2][2][4];
+  float t0 = 0.f;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    if (c == 0) s1[0] = mfma_fp8(ka[0][0], ka[0][1], st.q[1][0], st.q[1][1], zero);
+    if (c == 4) s1[1] = mfma_fp8(ka[1][0], ka[1][1], st.q[1][0], st.q[1][1], zero);
+    if (MASKED) soft_chunk(pk0, s0, t0, c);
+    else soft_chunk_sc(pk0, s0, t0, c, c2, nm0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (MASKED) scale_logits<true>(s1, c2, nm1, g, nvalid);
+  bf16x8 p0[2][2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int mm = 0; mm < 2; ++mm)
+      p0[kb][mm] = __builtin_bit_cast(bf16x8, (uint4){pk0[kb][mm][0], pk0[kb][mm][1], pk0[kb][mm][2], pk0[kb][mm][3]});
+  if (__any(!(t0 <= 65536.f)))
+    t0 = fast_exact_fp8<MASKED>(p0, st.q[0][0], st.q[0][1], st.m[0], st.l[0], st.o[0], kl, kperm, g, nvalid, c2);
+  st.l[0] += t0;
+  // V^T operands (shared by both blocks)
+  lds_u16* vl3 = (lds_u16*)(vl);
+  bf16x8 va[2][2][2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int mm = 0; mm < 2; ++mm) {
+      const int key = kb * 32 + 16 * g + 8 * mm + (li >> 2);
+#pragma unroll
+      for (int db = 0; db < 2; ++db) {
+        const int col = db * 32 + dc0 + 4 * (li & 3);
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vl3 + lds_off<64>(key, col >> 3) + (col & 4)));
+        const s16x4 hi =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vl3 + lds_off<64>(key + 4, col >> 3) + (col & 4)));
+        va[kb][mm][db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+    }
+  __builtin_amdgcn_sched_barrier(0);
+  // output update of block 0 | softmax of block 1
+  uint32_t pk1[2][2][4];
+  float t1 = 0.f;
+  if (MASKED) {
+    soft_chunk(pk1, s1, t1, 0);
+    soft_chunk(pk1, s1, t1, 1);
+  } else {
+    soft_chunk_sc(pk1, s1, t1, 0, c2, nm1);
+    soft_chunk_sc(pk1, s1, t1, 1, c2, nm1);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int kb = i >> 2, mm = (i >> 1) & 1, db = i & 1;
+    st.o[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[kb][mm][db], p0[kb][mm], st.o[0][db], 0, 0, 0);
+    if (i + 2 < 8) {
+      if (MASKED) soft_chunk(pk1, s1, t1, i + 2);
+      else soft_chunk_sc(pk1, s1, t1, i + 2, c2, nm1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  bf16x8 p1[2][2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int mm = 0; mm < 2; ++mm)
+      p1[kb][mm] = __builtin_bit_cast(bf16x8, (uint4){pk1[kb][mm][0], pk1[kb][mm][1], pk1[kb][mm][2], pk1[kb][mm][3]});
+  if (__any(!(t1 <= 65536.f)))
+    t1 = fast_exact_fp8<MASKED>(p1, st.q[1][0], st.q[1][1], st.m[1], st.l[1], st.o[1], kl, kperm, g, nvalid, c2);
+  st.l[1] += t1;
+  // output update of block 1
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int mm = 0; mm < 2; ++mm)
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+        st.o[1][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[kb][mm][db], p1[kb][mm], st.o[1][db], 0, 0, 0);
+}
+
+template <int QB, bool MASKED, int KM, int D, bool FP8 = false>
 __device__ __forceinline__ void tile_step_fast(WaveState<QB, D>& st, const uint16_t* kl, const uint16_t* vl, int kperm,
                                                int g, int li, int dc0, float c2, int nvalid, const MaskTile<KM>& mt) {
-  constexpr bool kPre = D == 64;  // Q pre-scaled to log2 units (head dim 64) or exact (head dim 128)
+  // Q pre-scaled to log2 units (bf16, head dim 64) or exact (head dim 128, fp8)
+  constexpr bool kPre = D == 64 && !FP8;
   static_assert(KM == 0 || QB == 1, "a kept mask runs with one query block per wave");
   static_assert(QB == 1 || D == 64, "two query blocks per wave only at head dim 64");
+  static_assert(!FP8 || (D == 64 && KM == 0), "fp8 Q / K at head dim 64 without a mask");
   if constexpr (QB == 2) {
-    tile_step_fast2<MASKED>(st, kl, vl, kperm, g, li, dc0, nvalid);
+    if constexpr (FP8) tile_step_fast2_fp8<MASKED>(st, kl, vl, kperm, g, li, dc0, c2, nvalid);
+    else tile_step_fast2<MASKED>(st, kl, vl, kperm, g, li, dc0, nvalid);
     return;
   }
   f32x16 s[QB][2];
@@ -461,13 +680,20 @@ __device__ __forceinline__ void tile_step_fast(WaveState<QB, D>& st, const uint1
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
     const int key = kb * 32 + kperm;
+    if constexpr (FP8) {
+      bf16x8 ka[2];
+      read_k8(ka, kl, key, g);
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kl + lds_off<D>(key, 2 * ks + g));
+      for (int qb = 0; qb < QB; ++qb) s[qb][kb] = mfma_fp8(ka[0], ka[1], st.q[qb][0], st.q[qb][1], (f32x16){});
+    } else {
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
-        s[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, st.q[qb][ks], (!kPre && ks == 0) ? (f32x16){} : s[qb][kb],
-                                                            0, 0, 0);
+      for (int ks = 0; ks < D / 16; ++ks) {
+        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kl + lds_off<D>(key, 2 * ks + g));
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+          s[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, st.q[qb][ks], (!kPre && ks == 0) ? (f32x16){} : s[qb][kb],
+                                                              0, 0, 0);
+      }
     }
   }
   if constexpr (!kPre) {
@@ -518,10 +744,16 @@ __device__ __forceinline__ void tile_step_fast(WaveState<QB, D>& st, const uint1
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const int key = kb * 32 + kperm;
+        if constexpr (FP8) {
+          bf16x8 ka[2];
+          read_k8(ka, kl, key, g);
+          sx[kb] = mfma_fp8(ka[0], ka[1], st.q[qb][0], st.q[qb][1], (f32x16){});
+        } else {
 #pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) {
-          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kl + lds_off<D>(key, 2 * ks + g));
-          sx[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, st.q[qb][ks], ks == 0 ? (f32x16){} : sx[kb], 0, 0, 0);
+          for (int ks = 0; ks < D / 16; ++ks) {
+            const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kl + lds_off<D>(key, 2 * ks + g));
+            sx[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, st.q[qb][ks], ks == 0 ? (f32x16){} : sx[kb], 0, 0, 0);
+          }
         }
       }
       if constexpr (!kPre) {
@@ -606,12 +838,13 @@ __device__ __forceinline__ void tile_step_fast(WaveState<QB, D>& st, const uint1
 
 // One 64-key tile: logits, online softmax, P V.  MASKED handles partial tiles (keys >= nvalid are
 // -inf) and the optional store of the tile's logits (text tiles of the warmup emission).
-template <int QB, bool MASKED, bool EXACT_SUM, int KM, int D>
+template <int QB, bool MASKED, bool EXACT_SUM, int KM, int D, bool FP8 = false>
 __device__ __forceinline__ void tile_step(WaveState<QB, D>& st, const uint16_t* kl, const uint16_t* vl, int kperm,
                                           int g, int li, int dc0, float c2, int nvalid, float* const (&xo)[QB],
                                           float scale, const MaskTile<KM>& mt) {
+  static_assert(!FP8 || !EXACT_SUM, "fp8 Q / K on the fast path only");
   if constexpr (!EXACT_SUM) {
-    tile_step_fast<QB, MASKED, KM, D>(st, kl, vl, kperm, g, li, dc0, c2, nvalid, mt);
+    tile_step_fast<QB, MASKED, KM, D, FP8>(st, kl, vl, kperm, g, li, dc0, c2, nvalid, mt);
     return;
   }
   static_assert(KM == 0 || QB == 1, "a kept mask runs with one query block per wave");
@@ -798,10 +1031,12 @@ __device__ __forceinline__ void store_lse_img(const AttnArgs& a, const WaveState
   }
 }
 
-template <bool GATHER, int QB, bool EXACT_SUM, int KM, int KS, int D>
+template <bool GATHER, int QB, bool EXACT_SUM, int KM, int KS, int D, bool FP8 = false>
 __global__ __launch_bounds__(kThreads * KS) __attribute__((amdgpu_waves_per_eu(2))) void k_attn_mfma(AttnArgs a) {
   static_assert(KS == 1 || (KS == 2 && !EXACT_SUM && KM == 0), "key halves only on the mask-free fast path");
   static_assert(D == 64 || D == 128, "head dim 64 or 128");
+  static_assert(!FP8 || (D == 64 && !EXACT_SUM && KM == 0), "fp8 Q / K: head dim 64, mask-free fast path");
+  constexpr size_t kRowK = FP8 ? D : 2 * D;  // bytes per K row
   constexpr int kRowsW = 32 * QB;
   constexpr int kBM = kWaves * kRowsW;
   // Two LDS buffers as distinct objects: every read and every DMA target below names one of them
@@ -857,10 +1092,17 @@ __global__ __launch_bounds__(kThreads * KS) __attribute__((amdgpu_waves_per_eu(2
     const int rr = active ? (GATHER ? a.rows[r] : r) : 0;
     valid[qb] = active && rr >= 0 && rr < a.N;
     row[qb] = valid[qb] ? rr : 0;
-    const bf16x8* qp =
-        reinterpret_cast<const bf16x8*>(static_cast<const uint16_t*>(a.q) + (bh * a.N + row[qb]) * D);
+    if constexpr (FP8) {
+      // the fp8 Q operand: bytes 32g .. 32g + 31 of the row (the other two entries of st.q stay unused)
+      const uint8_t* qp8 = static_cast<const uint8_t*>(a.q) + (bh * a.N + row[qb]) * D + 32 * g;
+      st.q[qb][0] = *reinterpret_cast<const bf16x8*>(qp8);
+      st.q[qb][1] = *reinterpret_cast<const bf16x8*>(qp8 + 16);
+    } else {
+      const bf16x8* qp =
+          reinterpret_cast<const bf16x8*>(static_cast<const uint16_t*>(a.q) + (bh * a.N + row[qb]) * D);
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) st.q[qb][ks] = qp[2 * ks + g];
+      for (int ks = 0; ks < D / 16; ++ks) st.q[qb][ks] = qp[2 * ks + g];
+    }
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -884,8 +1126,12 @@ __global__ __launch_bounds__(kThreads * KS) __attribute__((amdgpu_waves_per_eu(2
   }
   // the warmup emission only runs on the exact-sum path (the host picks it whenever an output asks for it)
   const bool emit = EXACT_SUM && b == 0 && (a.xattn_out != nullptr || a.lse_img_out != nullptr);
-  const float c2 = a.scale * kLog2e;
-  if constexpr (!EXACT_SUM && D == 64) {  // the fast path's pre-scaled Q (head dim 64 only)
+  float c2 = a.scale * kLog2e;
+  if constexpr (FP8) {  // the (b,h) dequantisation factors of the fp8 Q and K multiply every logit
+    if (a.q_descale != nullptr) c2 *= a.q_descale[bh];
+    if (a.k_descale != nullptr) c2 *= a.k_descale[bh];
+  }
+  if constexpr (!EXACT_SUM && D == 64 && !FP8) {  // the fast path's pre-scaled Q (bf16 at head dim 64 only)
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
@@ -917,7 +1163,7 @@ __global__ __launch_bounds__(kThreads * KS) __attribute__((amdgpu_waves_per_eu(2
   MaskTile<KM> mcur, mnext;
   mask_fetch(mcur, 0);
 
-  if (t_begin < t_end) stage_issue<D, (QB > 1)>(tile_src<D>(a, bh, t_begin, n_img, tv), k_a, v_a);
+  if (t_begin < t_end) stage_issue<D, (QB > 1), FP8>(tile_src<D, FP8>(a, bh, t_begin, n_img, tv), k_a, v_a);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
@@ -926,22 +1172,25 @@ __global__ __launch_bounds__(kThreads * KS) __attribute__((amdgpu_waves_per_eu(2
   // prefetch and synchronise.
   uint32_t coff[D / 32];
   stage_offsets<D>(coff);
+  const uint32_t koff8 = FP8 ? stage8_offset() : 0u;
   // this (b,h)'s image K / V bases, opaque so that they stay in scalar registers instead of being reloaded
   // from the kernel arguments (a scalar load and its wait) every tile
-  const uint16_t* kimg = static_cast<const uint16_t*>(a.k_img) + bh * a.N * D;
+  const uint16_t* kimg = reinterpret_cast<const uint16_t*>(static_cast<const uint8_t*>(a.k_img) + bh * a.N * kRowK);
   const uint16_t* vimg = static_cast<const uint16_t*>(a.v_img) + bh * a.N * D;
   asm volatile("" : "+s"(kimg), "+s"(vimg));
   auto full_tile = [&](int t, const uint16_t* ck, const uint16_t* cv, uint16_t* nk, uint16_t* nv) {
     if (t + 1 < t_end) {
       if (t + 1 < n_full) {
-        const TileSrc src{kimg + static_cast<size_t>(t + 1) * kBN * D, vimg + static_cast<size_t>(t + 1) * kBN * D, kBN};
-        stage_issue_full<D, (QB > 1)>(src, nk, nv, coff);
+        const TileSrc src{reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(kimg) +
+                                                            static_cast<size_t>(t + 1) * kBN * kRowK),
+                          vimg + static_cast<size_t>(t + 1) * kBN * D, kBN};
+        stage_issue_full<D, (QB > 1), FP8>(src, nk, nv, coff, koff8);
       } else {
-        stage_issue<D, (QB > 1)>(tile_src<D>(a, bh, t + 1, n_img, tv), nk, nv);
+        stage_issue<D, (QB > 1), FP8>(tile_src<D, FP8>(a, bh, t + 1, n_img, tv), nk, nv);
       }
       mask_fetch(mnext, t + 1);
     }
-    tile_step<QB, false, EXACT_SUM, KM, D>(st, ck, cv, kperm, g, li, dc0, c2, kBN, no_store, a.scale, mcur);
+    tile_step<QB, false, EXACT_SUM, KM, D, FP8>(st, ck, cv, kperm, g, li, dc0, c2, kBN, no_store, a.scale, mcur);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if constexpr (KM != 0) mcur = mnext;
@@ -949,7 +1198,7 @@ __global__ __launch_bounds__(kThreads * KS) __attribute__((amdgpu_waves_per_eu(2
   auto masked_tile = [&](int t, const uint16_t* ck, const uint16_t* cv, uint16_t* nk, uint16_t* nv) {
     if (emit && t == n_img && a.lse_img_out != nullptr) store_lse_img(a, st, h, row, valid, g);
     if (t + 1 < t_end) {
-      stage_issue<D, (QB > 1)>(tile_src<D>(a, bh, t + 1, n_img, tv), nk, nv);
+      stage_issue<D, (QB > 1), FP8>(tile_src<D, FP8>(a, bh, t + 1, n_img, tv), nk, nv);
       mask_fetch(mnext, t + 1);
     }
     const bool txt = t >= n_img;
@@ -960,7 +1209,7 @@ __global__ __launch_bounds__(kThreads * KS) __attribute__((amdgpu_waves_per_eu(2
       xo[qb] = (emit && txt && a.xattn_out != nullptr && valid[qb])
                    ? a.xattn_out + (static_cast<size_t>(h) * a.N + row[qb]) * a.T + (t - n_img) * kBN
                    : nullptr;
-    tile_step<QB, true, EXACT_SUM, KM, D>(st, ck, cv, kperm, g, li, dc0, c2, nvalid, xo, a.scale, mcur);
+    tile_step<QB, true, EXACT_SUM, KM, D, FP8>(st, ck, cv, kperm, g, li, dc0, c2, nvalid, xo, a.scale, mcur);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if constexpr (KM != 0) mcur = mnext;
@@ -1047,12 +1296,12 @@ __global__ __launch_bounds__(kThreads * KS) __attribute__((amdgpu_waves_per_eu(2
   }
 }
 
-template <bool GATHER, int QB, bool EXACT_SUM, int KM, int D, int KS = 1>
+template <bool GATHER, int QB, bool EXACT_SUM, int KM, int D, int KS = 1, bool FP8 = false>
 static void launch(const AttnArgs& a, hipStream_t s) {
   constexpr int kBM = kWaves * 32 * QB;
   const int nqt = (a.R + kBM - 1) / kBM;
   const uint32_t grid = static_cast<uint32_t>(a.B) * a.H * nqt;
-  k_attn_mfma<GATHER, QB, EXACT_SUM, KM, KS, D><<<grid, kThreads * KS, 0, s>>>(a);
+  k_attn_mfma<GATHER, QB, EXACT_SUM, KM, KS, D, FP8><<<grid, kThreads * KS, 0, s>>>(a);
 }
 
 template <bool GATHER, int QB, int KM, int D>
@@ -1102,6 +1351,25 @@ static void launch_rows128(const AttnArgs& a, hipStream_t s) {
   const bool exact = a.lse != nullptr || a.lse_img_out != nullptr || a.xattn_out != nullptr;
   if (exact || waves_qb1 >= 2048.0) launch_sum<GATHER, 1, 0, 128>(a, s);
   else launch<GATHER, 1, false, 0, 128, 2>(a, s);
+}
+
+// fp8 Q / K (head dim 64, mask-free fast path): the work shapes of the bf16 fast path.
+template <bool GATHER>
+static void launch_rows64_fp8(const AttnArgs& a, hipStream_t s) {
+  const double waves_qb2 = static_cast<double>(a.B) * a.H * ((a.R + 63) / 64);
+  if (waves_qb2 >= 2048.0) launch<GATHER, 2, false, 0, 64, 1, true>(a, s);
+  else if (waves_qb2 > 1024.0) launch<GATHER, 1, false, 0, 64, 1, true>(a, s);
+  else if (waves_qb2 >= 512.0) launch<GATHER, 2, false, 0, 64, 2, true>(a, s);
+  else launch<GATHER, 1, false, 0, 64, 2, true>(a, s);
+}
+
+hipError_t launch_attn_mfma_fp8(const AttnArgs& a, hipStream_t s) {
+  if (a.R == 0) return hipSuccess;
+  if (a.mask != nullptr || a.lse != nullptr || a.xattn_out != nullptr || a.lse_img_out != nullptr)
+    return hipErrorInvalidValue;
+  if (a.rows != nullptr) launch_rows64_fp8<true>(a, s);
+  else launch_rows64_fp8<false>(a, s);
+  return hipGetLastError();
 }
 
 hipError_t launch_attn_mfma_bf16(const AttnArgs& a, int d, hipStream_t s) {

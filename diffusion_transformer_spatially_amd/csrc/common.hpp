@@ -20,6 +20,18 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return static_cast<uint16_t>(u >> 16);
 }
 
+// 16-byte loads that bypass the caches' retention (nontemporal): for inputs streamed once.
+typedef float f32x4_nt __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ float4 load_nt(const float4* p) {
+  const f32x4_nt v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_nt*>(p));
+  return make_float4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint4 load_nt(const uint4* p) {
+  typedef uint32_t u32x4_nt __attribute__((ext_vector_type(4)));
+  const u32x4_nt v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_nt*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // Workgroup id remap so that consecutive logical tiles land on the same XCD (the hardware deals
 // workgroup ids round-robin over the 8 XCDs, each with its own L2).
 __device__ __forceinline__ uint32_t xcd_remap(uint32_t x, uint32_t G) {
@@ -42,6 +54,8 @@ struct AttnArgs {
   const int32_t* rows;  // nullptr for dense
   const void* mask;
   int32_t mask_dtype, mask_B, mask_H, mask_cols;
+  const float* q_descale;  // fp8 Q / K: per-(b,h) dequantisation factors, nullptr = 1
+  const float* k_descale;
   int32_t B, H, N, T, R;  // R = number of query rows computed per (b,h)
   float scale;            // natural-log logit scale
   int32_t tv[SAFE_MAX_BATCH];

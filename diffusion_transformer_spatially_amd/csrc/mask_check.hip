@@ -21,12 +21,13 @@ __device__ __forceinline__ float mask_value(const uint8_t* p, int dtype) {
 
 __global__ void k_flag_init(int32_t* flag) { *flag = 1; }
 
-// Block a of a row span [b0, hi) inside the mask buffer [buf_lo, buf_hi): one 16-byte load when the block
-// lies inside the buffer, else byte loads of the block's bytes inside the span only (the other bytes are
-// returned as 0 and are never tested).
+// Block a of a row span [b0, hi) inside the mask buffer [buf_lo, buf_hi): one nontemporal 16-byte load when
+// the block lies inside the buffer (the mask is streamed once: 2560^2 bool 122 -> 111 us, fp32 453 -> 407 us),
+// else byte loads of the block's bytes inside the span only (the other bytes are returned as 0 and are never
+// tested).
 __device__ __forceinline__ uint4 load_block(uintptr_t a, uintptr_t buf_lo, uintptr_t buf_hi, uintptr_t b0,
                                             uintptr_t hi) {
-  if (block_whole(a, buf_lo, buf_hi)) return *reinterpret_cast<const uint4*>(a);
+  if (block_whole(a, buf_lo, buf_hi)) return load_nt(reinterpret_cast<const uint4*>(a));
   uintptr_t r0, r1;
   block_bytes(a, b0, hi, &r0, &r1);
   uint32_t w[4] = {0u, 0u, 0u, 0u};

@@ -47,9 +47,10 @@ enum {
 };
 
 enum {
-  SAFE_DTYPE_BF16 = 0, /* bfloat16, 2 bytes */
-  SAFE_DTYPE_F32 = 1,  /* float, 4 bytes */
-  SAFE_DTYPE_BOOL = 2  /* 1 byte, 0 = masked out (-inf), non-zero = kept (0) */
+  SAFE_DTYPE_BF16 = 0,     /* bfloat16, 2 bytes */
+  SAFE_DTYPE_F32 = 1,      /* float, 4 bytes */
+  SAFE_DTYPE_BOOL = 2,     /* 1 byte, 0 = masked out (-inf), non-zero = kept (0) */
+  SAFE_DTYPE_FP8_E4M3 = 3  /* 1 byte, OCP FP8 E4M3 (4 exponent bits, bias 7, 3 mantissa bits, no inf, max 448) */
 };
 
 #define SAFE_MAX_BATCH 64
@@ -63,7 +64,11 @@ enum {
  * o_i = sum_j softmax(L)_j v_j; lse_i = log sum_j exp(L_j) (natural log).  A row whose every logit
  * is -inf (possible only with a mask) gets o_i = 0 and lse_i = -inf.
  *
- * dtype           SAFE_DTYPE_BF16 or SAFE_DTYPE_F32, for q, k_*, v_*, out.
+ * dtype           SAFE_DTYPE_BF16 or SAFE_DTYPE_F32, for q, k_*, v_*, out; or SAFE_DTYPE_FP8_E4M3: q, k_img
+ *                 and k_txt are FP8 E4M3 values whose real value is the stored value times the (b,h) entry
+ *                 of q_descale / k_descale, while v_img, v_txt and out are bf16 (the probabilities stay
+ *                 bf16 for P V).  FP8 takes d == 64, no mask, no lse, no emission (else
+ *                 SAFE_ERR_UNSUPPORTED).
  * B, H, N, T, d   1 <= B <= SAFE_MAX_BATCH, H >= 1, N >= 1, T >= 0, d == 64 or d == 128 (the head
  *                 dims of the DiT backbones the pages evaluate across; other values: SAFE_ERR_UNSUPPORTED).
  * text_valid_len  HOST array [B], 0 <= Tv[b] <= T.
@@ -79,6 +84,8 @@ enum {
  *                 L[N+t] of the computed rows (slots t >= Tv[0] are not written).
  * lse_img_out     NULL or fp32 [H,N]: for batch entry 0, log-sum-exp of the image-block logits.
  *                 These two are the warmup cross-attention responses the PCSP scores are built from.
+ * q_descale       NULL (every factor 1) or device fp32 [B,H]: dequantisation factor of q per (b,h) (FP8 only).
+ * k_descale       NULL or device fp32 [B,H]: the same for k_img and k_txt (FP8 only).
  * Alignment: q, k_*, v_*, out 16-byte aligned.
  */
 typedef struct safe_attn_desc {
@@ -97,6 +104,8 @@ typedef struct safe_attn_desc {
   float* lse;
   float* xattn_out;
   float* lse_img_out;
+  const float* q_descale;
+  const float* k_descale;
 } safe_attn_desc;
 
 /* Dense anchor step (CAR, SAFE-DiT summary Methodology 3): recompute all N image rows of `out`. */

@@ -144,6 +144,72 @@ def attention_inputs(w: Workload, step: int = 0, roles: Sequence[str] = ("q", "k
     return out
 
 
+# ----------------------------------------------------------------------------- fp8 (OCP E4M3) inputs
+def _e4m3_values() -> np.ndarray:
+    """The real value of each of the 256 OCP FP8 E4M3 codes: 1 sign bit, 4 exponent bits (bias 7), 3 mantissa
+    bits; exponent 0 is subnormal (2^-6 * m/8); exponent 15 with mantissa 7 is NaN; there are no infinities
+    (largest finite 0x7E = 448)."""
+    v = np.empty(256, dtype=np.float64)
+    for c in range(256):
+        sgn = -1.0 if c & 0x80 else 1.0
+        e, m = (c >> 3) & 0xF, c & 7
+        if e == 15 and m == 7:
+            v[c] = np.nan
+        elif e == 0:
+            v[c] = sgn * 2.0 ** -6 * (m / 8.0)
+        else:
+            v[c] = sgn * 2.0 ** (e - 7) * (1.0 + m / 8.0)
+    return v
+
+
+E4M3_VALUES = _e4m3_values()
+E4M3_MAX = 448.0
+
+
+def fp8_e4m3_bits(x: np.ndarray) -> np.ndarray:
+    """Round-to-nearest-even fp32/fp64 -> E4M3 codes (uint8), saturating at +-448; NaN -> 0x7F."""
+    x = np.asarray(x, dtype=np.float64)
+    pos = E4M3_VALUES[:127]                    # codes 0..126: the non-negative finite values, increasing
+    a = np.minimum(np.abs(x), E4M3_MAX)
+    hi = np.clip(np.searchsorted(pos, a, side="left"), 0, 126)
+    lo = np.clip(hi - 1, 0, 126)
+    dlo, dhi = a - pos[lo], pos[hi] - a
+    # nearer neighbour; on a tie the even code (mantissa lsb 0)
+    code = np.where(dlo < dhi, lo, np.where(dhi < dlo, hi, np.where(lo % 2 == 0, lo, hi)))
+    code = np.where(a == pos[hi], hi, code).astype(np.uint8)
+    code = np.where(np.signbit(x), code | np.uint8(0x80), code)
+    return np.where(np.isnan(x), np.uint8(0x7F), code).astype(np.uint8)
+
+
+def fp8_quantize_heads(x: np.ndarray) -> tuple:
+    """Per-(b,h) scaled E4M3 codes of x [B,H,...]: scale = amax/448 (1 for an all-zero head) as fp32, codes of
+    x / scale.  Returns (codes uint8, scale fp32 [B,H], dequantised value codes * scale in fp64)."""
+    B, H = x.shape[:2]
+    amax = np.abs(x.reshape(B, H, -1)).max(axis=2)
+    scale = np.where(amax > 0, amax / E4M3_MAX, 1.0).astype(np.float32)
+    sc = scale.astype(np.float64).reshape((B, H) + (1,) * (x.ndim - 2))
+    codes = fp8_e4m3_bits(x.astype(np.float64) / sc)
+    return codes, scale, E4M3_VALUES[codes] * sc
+
+
+def attention_inputs_fp8(w: Workload, step: int = 0) -> Dict[str, np.ndarray]:
+    """fp8 Q and K with bf16 V: the workload's N(0,1)*std draws, Q quantised per (b,h), K_img and K_txt
+    together per (b,h) (one factor per head), V as bf16.  `q`, `k_img`, `k_txt` hold the dequantised values
+    (fp64: code value times the fp32 factor, exactly what the device's operands mean); `*_fp8` the codes."""
+    base = attention_inputs(dataclasses.replace(w, dtype="f32"), step)
+    out: Dict[str, np.ndarray] = {}
+    out["q_fp8"], out["q_descale"], out["q"] = fp8_quantize_heads(base["q"])
+    N = w.N
+    kcat = np.concatenate([base["k_img"], base["k_txt"]], axis=2)
+    codes, out["k_descale"], deq = fp8_quantize_heads(kcat)
+    out["k_img_fp8"], out["k_txt_fp8"] = codes[:, :, :N], codes[:, :, N:]
+    out["k_img"], out["k_txt"] = deq[:, :, :N], deq[:, :, N:]
+    for r in ("v_img", "v_txt"):
+        out[r + "_bits"] = f32_to_bf16_bits(base[r])
+        out[r] = bf16_bits_to_f32(out[r + "_bits"])
+    return out
+
+
 def blob_centres(w: Workload) -> np.ndarray:
     """Integer grid points (y, x) drawn uniformly from the token grid, one row per blob."""
     rng = rng_for(w.seed, "blobs")
@@ -260,4 +326,5 @@ __all__ = [
     "Workload", "WORKLOADS", "scaled", "rng_for", "aesthetic_selection", "stepcache_predictions", "hidden_states", "block_weights", "f32_to_bf16_bits", "bf16_bits_to_f32", "round_to_bf16",
     "attention_inputs", "blob_centres", "blob_bias", "pcsp_logits", "latent_eps", "initial_state",
     "random_rows", "mask_all_valid_bool", "mask_zeros_f32", "mask_row_constant_f32", "sample_rows",
+    "E4M3_VALUES", "E4M3_MAX", "fp8_e4m3_bits", "fp8_quantize_heads", "attention_inputs_fp8",
 ]

@@ -1,0 +1,170 @@
+"""GPU parity of the fp8 attention path (FP8 E4M3 Q and K with per-(b,h) factors, bf16 V and output; head dim
+64, mask-free fast path) against the fp64 oracle on the dequantised inputs."""
+import numpy as np
+import pytest
+
+import synthetic as syn
+from oracle import attention as OA
+from tests.gpu_util import assert_close, dev, host, torch
+
+pytestmark = pytest.mark.gpu
+
+
+def _fp8(codes):
+    t = torch()
+    return t.from_numpy(np.ascontiguousarray(codes)).view(t.float8_e4m3fn).cuda()
+
+
+def _tensors(inp):
+    q, ki, kt = _fp8(inp["q_fp8"]), _fp8(inp["k_img_fp8"]), _fp8(inp["k_txt_fp8"])
+    vi, vt = dev(None, inp["v_img_bits"]), dev(None, inp["v_txt_bits"])
+    return q, ki, vi, kt, vt, dev(inp["q_descale"].reshape(-1)), dev(inp["k_descale"].reshape(-1))
+
+
+def _run(lib, w, inp, rows=None, state=None, descale=True):
+    t = torch()
+    q, ki, vi, kt, vt, qd, kd = _tensors(inp)
+    if not descale:
+        qd = kd = None
+    out = t.from_numpy(state.astype(np.float32)).to(t.bfloat16).cuda() if state is not None else \
+        t.zeros(q.shape, dtype=t.bfloat16, device="cuda")
+    if rows is None:
+        lib.safe_attn_dense(q, ki, vi, kt, vt, w.tv, out, q_descale=qd, k_descale=kd)
+    else:
+        lib.safe_attn_rows(q, ki, vi, kt, vt, w.tv, dev(np.asarray(rows, dtype=np.int32)), out, q_descale=qd,
+                           k_descale=kd)
+    t.cuda.synchronize()
+    return host(out)
+
+
+def _oracle(w, inp, rows=None):
+    return OA.attention(inp["q"], inp["k_img"], inp["v_img"], inp["k_txt"], inp["v_txt"], w.tv, rows=rows)[0]
+
+
+def _w(**kw):
+    return syn.scaled(syn.WORKLOADS["dense_1024"], side=1, **kw)
+
+
+SHAPES = [(1, 1, 1, 0, (0,)), (1, 2, 64, 64, (64,)), (2, 3, 65, 40, (17, 0)), (2, 2, 127, 256, (77, 1)),
+          (1, 2, 300, 256, (65,)), (2, 2, 1000, 256, (200, 63))]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "B%dH%dN%dT%d" % s[:4])
+def test_fp8_dense_parity(lib, shape):
+    B, H, N, T, tv = shape
+    w = _w(B=B, H=H, N=N, T=T, tv=tv)
+    inp = syn.attention_inputs_fp8(w)
+    assert_close(_run(lib, w, inp), _oracle(w, inp), "bf16", f"fp8 dense {shape}")
+
+
+@pytest.mark.parametrize("k", [0, 1, 63, 65, 300])
+def test_fp8_rows_parity_and_untouched_context(lib, k):
+    w = _w(B=2, H=3, N=300, T=256, tv=(77, 5))
+    inp = syn.attention_inputs_fp8(w)
+    rows = syn.random_rows(w, k=k)
+    state = syn.initial_state(w)
+    o = _run(lib, w, inp, rows=rows, state=state)
+    C = np.setdiff1d(np.arange(w.N), rows)
+    assert np.array_equal(o[:, :, C], state[:, :, C].astype(np.float64))
+    if k:
+        assert_close(o[:, :, rows], _oracle(w, inp, rows), "bf16", f"fp8 rows k={k}")
+    if k == w.N:
+        assert np.array_equal(o, _run(lib, w, inp))
+
+
+@pytest.mark.parametrize("B,H,N,T,tv,k", [
+    (1, 8, 2000, 256, (77,), None),         # one block per wave, key halves
+    (2, 8, 2304, 256, (120, 3), None),      # two blocks per wave, key halves
+    (2, 8, 4160, 256, (77, 0), None),       # one block per wave, no split
+    (2, 24, 4096, 256, (77, 77), 1229),     # the 1024^2 rows launch
+    (1, 3, 130, 0, (0,), None),             # 3 key tiles: uneven halves
+])
+def test_fp8_work_shapes(lib, B, H, N, T, tv, k):
+    w = _w(B=B, H=H, N=N, T=T, tv=tv, k=k or 1)
+    inp = syn.attention_inputs_fp8(w)
+    if k is None:
+        assert_close(_run(lib, w, inp), _oracle(w, inp), "bf16", f"fp8 dense B{B}H{H}N{N}")
+    else:
+        rows = syn.random_rows(w, k=k)
+        state = syn.initial_state(w)
+        o = _run(lib, w, inp, rows=rows, state=state)
+        pick = rows[syn.sample_rows(len(rows), 96, seed=1)]
+        assert_close(o[:, :, pick], _oracle(w, inp, pick), "bf16", "fp8 rows 1024^2 shape")
+        C = np.setdiff1d(np.arange(w.N), rows)
+        assert np.array_equal(o[:, :, C], state[:, :, C].astype(np.float64))
+
+
+def test_fp8_factors_and_closed_forms(lib):
+    w = _w(B=2, H=2, N=257, T=256, tv=(77, 0))
+    inp = syn.attention_inputs_fp8(w)
+    # without factors the codes are taken as they are (factor 1)
+    raw = dict(inp)
+    for r, f in (("q", "q_descale"), ("k_img", "k_descale"), ("k_txt", "k_descale")):
+        raw[r] = syn.E4M3_VALUES[inp[r + "_fp8"]]
+    assert_close(_run(lib, w, raw, descale=False), _oracle(w, raw), "bf16", "fp8 without factors")
+    # V = 1: every output is 1 (the row sum adds the same bf16 probabilities P V uses)
+    ones = dict(inp, v_img_bits=np.full_like(inp["v_img_bits"], 0x3F80), v_txt_bits=np.full_like(inp["v_txt_bits"], 0x3F80))
+    assert np.max(np.abs(_run(lib, w, ones) - 1.0)) <= 1e-6
+    # Q = 0: the mean of the valid V rows
+    zq = dict(inp, q_fp8=np.zeros_like(inp["q_fp8"]), q=np.zeros_like(inp["q"]))
+    o = _run(lib, w, zq)
+    for b in range(2):
+        vals = np.concatenate([inp["v_img"][b], inp["v_txt"][b, :, : w.tv[b]]], axis=1).astype(np.float64)
+        assert_close(o[b], np.broadcast_to(vals.mean(axis=1)[:, None, :], o[b].shape), "bf16", "fp8 Q = 0")
+
+
+@pytest.mark.parametrize("std", [1.0, 3.0])
+def test_fp8_large_logits_exercise_rescaling(lib, std):
+    w = _w(B=1, H=2, N=513, T=256, tv=(100,), std=std)
+    inp = dict(syn.attention_inputs_fp8(w))
+    for r in ("v_img", "v_txt"):  # values back at the workloads' scale (0.125), as in the bf16 stress test
+        v = (inp[r] * np.float32(0.125 / std)).astype(np.float32)
+        inp[r], inp[r + "_bits"] = syn.round_to_bf16(v), syn.f32_to_bf16_bits(v)
+    assert_close(_run(lib, w, inp), _oracle(w, inp), "bf16", f"fp8 std={std}")
+
+
+def test_fp8_padding_contents_never_leak(lib):
+    w = _w(B=2, H=2, N=200, T=256, tv=(77, 3))
+    inp = syn.attention_inputs_fp8(w)
+    o1 = _run(lib, w, inp)
+    bad = dict(inp)
+    kt = inp["k_txt_fp8"].copy()
+    kt[0, :, 77:] = 0x7F  # NaN codes in the padding
+    kt[1, :, 3:] = 0x7E
+    vt = inp["v_txt_bits"].copy()
+    vt[0, :, 77:] = 0x7FC0
+    bad.update(k_txt_fp8=kt, v_txt_bits=vt)
+    assert np.array_equal(o1, _run(lib, w, bad))
+
+
+@pytest.mark.parametrize("name", ["srsu_1024"])
+def test_fp8_full_size_sampled(lib, name):
+    """The 1024^2 launches the benchmark times (dense and |S| = 1229 rows), on sampled rows."""
+    w = syn.WORKLOADS[name]
+    inp = syn.attention_inputs_fp8(w)
+    sample = syn.sample_rows(w.N, 24, seed=w.seed)
+    o = _run(lib, w, inp)
+    assert_close(o[:, :, sample], _oracle(w, inp, sample), "bf16", "fp8 dense 1024^2")
+    rows = syn.random_rows(w)
+    o = _run(lib, w, inp, rows=rows, state=np.zeros((w.B, w.H, w.N, w.d), np.float32))
+    pick = rows[syn.sample_rows(len(rows), 24, seed=w.seed)]
+    assert_close(o[:, :, pick], _oracle(w, inp, pick), "bf16", "fp8 rows 1024^2")
+
+
+def test_fp8_unsupported_requests_are_rejected(lib):
+    t = torch()
+    w = _w(B=1, H=1, N=64, T=0, tv=(0,))
+    inp = syn.attention_inputs_fp8(w)
+    q, ki, vi, kt, vt, qd, kd = _tensors(inp)
+    out = t.zeros(q.shape, dtype=t.bfloat16, device="cuda")
+    lse = t.zeros((1, 1, 64), dtype=t.float32, device="cuda")
+    mask = t.ones((1, 1, 64, 64), dtype=t.bool, device="cuda")
+    for kw in ({"lse": lse}, {"mask": mask}):
+        with pytest.raises(lib.SafeAttnError) as e:
+            lib.safe_attn_dense(q, ki, vi, kt, vt, w.tv, out, q_descale=qd, k_descale=kd, **kw)
+        assert e.value.code == 6
+    q2 = t.zeros((1, 1, 64, 128), dtype=t.float8_e4m3fn, device="cuda")
+    v2 = t.zeros((1, 1, 64, 128), dtype=t.bfloat16, device="cuda")
+    with pytest.raises(lib.SafeAttnError) as e:
+        lib.safe_attn_dense(q2, q2, v2, None, None, (0,), v2.clone())
+    assert e.value.code == 6
