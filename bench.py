@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--no-large", action="store_true", help="skip the 2560^2 attention lines")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 256 MiB device copy (for scaling HBM byte counters)")
+    ap.add_argument("--step-only", action="store_true",
+                    help="run only the 1024^2 step (eager breakdown pass and timed graph steps); for profiling it")
     ap.add_argument("--hbm-only", action="store_true",
                     help="run only the HBM-bound stages (batched / cold / cache-resident) and print them; for "
                          "profiling those launches")
@@ -308,6 +310,12 @@ def main():
                                   "the dense anchor attention (the headline graph runs every stage in order)"},
     }
 
+    if args.step_only:
+        if args.copy_calibration:
+            result["copy_calibration_bytes"] = copy_calibration(torch, dev)
+        print(json.dumps(result), flush=True)
+        return
+
     # ---------------------------------------------------------------- the mask tax on this stack
     # The redundant all-valid mask passed through (kept) instead of elided: the dense anchor launch with
     # the mask streamed from HBM into the same MFMA kernel, bool and fp32.
@@ -503,16 +511,35 @@ def time_launches(torch, fn, reps=20):
     return e0.elapsed_time(e1) / reps
 
 
+def time_rotating(torch, fns, reps=8):
+    """Average duration (ms) of `reps` back-to-back launches that alternate over the launches in `fns`, each
+    on its own buffers of more than 256 MB: a launch never finds its data in the 256 MB MALL, which holds the
+    other set's lines.  One event pair brackets them all, queued behind a spin so that they run back to back
+    (the pair's own cost spreads over the launches)."""
+    for f in fns:
+        f()
+    torch.cuda.synchronize()
+    gpu_busy(torch, 1.0)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(reps):
+        fns[i % len(fns)]()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
 def hbm_stages(dts, torch, np, syn, dev, hbm):
     """The HBM-bound stages at the 2560^2 / 3072^2 shapes, in three modes:
-      batched: one launch whose working set exceeds the 256 MB MALL (several independent instances of the
-               3072^2 shape in one launch where one instance is smaller), L2 and MALL swept before it;
-      cold:    one launch of the single-instance 2560^2 / 3072^2 shape after the same sweep;
+      batched: launches whose working set exceeds the 256 MB MALL (several independent instances of the
+               3072^2 shape in one launch where one instance is smaller), alternating over two such buffer
+               sets, 8 back-to-back launches between one event pair: every launch reads and writes HBM;
+      cold:    one launch of the single-instance 2560^2 / 3072^2 shape after a 1 GiB write + 1 GiB read sweep
+               of L2 and the MALL, with its own event pair minus the median of an empty pair after the same
+               sweep (about 2 us of event uncertainty remains);
       cache_resident: 20 back-to-back launches of the single-instance shape between one event pair, whose
                working set stays in the MALL from launch to launch -- a cache figure, not an HBM one.
-    The batched and cold launches each have their own event pair (queued behind the sweep, so the pair
-    brackets the kernel, not the host's launch), minus the median of an empty pair after the same sweep;
-    frac_hbm is reported for these two modes only."""
+    frac_hbm is reported for the first two modes only."""
     w4, w5 = syn.WORKLOADS["srsu_2560"], syn.WORKLOADS["traj_3072"]
     g = torch.Generator(device=dev)
     g.manual_seed(w4.seed + 100)
@@ -523,67 +550,81 @@ def hbm_stages(dts, torch, np, syn, dev, hbm):
         return {"ms": ms, "gbs_cache": bytes_ / (ms * 1e-3) / 1e9, "bytes": bytes_,
                 "note": "MALL-resident working set: a cache bandwidth, not an HBM fraction"}
 
-    # PCSP aggregation: 3072^2 (708 MB of valid logits: batched by size alone) and 2560^2 (297 MB)
-    for wl, tag, modes in ((w5, "3072", (batched,)), (w4, "2560", (cold, resident))):
-        H, N, T, Tv = wl.H, wl.N, wl.T, wl.tv[0]
-        x = torch.randn((H, N, T), generator=g, device=dev)
-        li = torch.randn((H, N), generator=g, device=dev) + float(np.log(N))
-        sc = torch.empty(N, dtype=torch.float32, device=dev)
-        nb = 4.0 * H * N * Tv + 4.0 * H * N + 4.0 * N
-        fn = lambda: dts.safe_pcsp_accumulate(x, li, Tv, 0, Tv, sc, False)
-        for m in modes:
-            if m is resident:
-                m["pcsp_accumulate_" + tag] = cache_line(nb, time_launches(torch, fn))
-            else:
-                m["pcsp_accumulate_" + tag] = cold_line(hbm, nb, cold_launch_ms(torch, fn, sweep))
-        if tag == "2560":
-            S = torch.empty(wl.k, dtype=torch.int32, device=dev)
-            C = torch.empty(N - wl.k, dtype=torch.int32, device=dev)
-            isn = torch.empty(N, dtype=torch.uint8, device=dev)
-            s01 = torch.empty(N, dtype=torch.float32, device=dev)
-            resident["pcsp_partition_2560"] = {
-                "ms": time_launches(torch, lambda: dts.safe_pcsp_partition(sc, wl.k, S, C, isn, s01)),
-                "note": "one workgroup over N=25600: latency-bound, no roofline"}
-        del x, li
-    # row gather / scatter: 3072^2 state with 6 instances (B = 12) in one launch, and the 2560^2 state
-    for wl, tag, Bx, modes in ((w5, "3072x6", 6 * w5.B, (batched,)), (w4, "2560", w4.B, (cold, resident))):
-        st = torch.randn((Bx, wl.H, wl.N, wl.d), generator=g, device=dev).to(torch.bfloat16)
-        rows = torch.from_numpy(syn.random_rows(wl)).to(dev)
-        packed = torch.empty((Bx, wl.H, wl.k, wl.d), dtype=torch.bfloat16, device=dev)
-        gs = 2 * 2.0 * Bx * wl.H * wl.k * wl.d
-        for name, fn in (("gather_rows_", lambda: dts.safe_gather_rows(st, rows, packed)),
-                         ("scatter_rows_", lambda: dts.safe_scatter_rows(packed, rows, st))):
-            for m in modes:
-                m[name + tag] = (cache_line(gs, time_launches(torch, fn)) if m is resident
-                                 else cold_line(hbm, gs, cold_launch_ms(torch, fn, sweep)))
-        del st, packed
-    # SW-CFG and StepCache on the 3072^2 latent [16,384,384]; batched: 10 latents' channels in one launch
+    # PCSP aggregation: 3072^2 (711 MB of valid logits per launch; two sets) and 2560^2 (297 MB)
+    H, N, T, Tv = w5.H, w5.N, w5.T, w5.tv[0]
+    sets = [(torch.randn((H, N, T), generator=g, device=dev),
+             torch.randn((H, N), generator=g, device=dev) + float(np.log(N)),
+             torch.empty(N, dtype=torch.float32, device=dev)) for _ in range(2)]
+    nb = 4.0 * H * N * Tv + 4.0 * H * N + 4.0 * N
+    batched["pcsp_accumulate_3072"] = hbm(nb, time_rotating(torch, [
+        (lambda x=x, li=li, sc=sc: dts.safe_pcsp_accumulate(x, li, Tv, 0, Tv, sc, False)) for x, li, sc in sets]))
+    del sets
+    H, N, T, Tv = w4.H, w4.N, w4.T, w4.tv[0]
+    x = torch.randn((H, N, T), generator=g, device=dev)
+    li = torch.randn((H, N), generator=g, device=dev) + float(np.log(N))
+    sc = torch.empty(N, dtype=torch.float32, device=dev)
+    nb = 4.0 * H * N * Tv + 4.0 * H * N + 4.0 * N
+    fn = lambda: dts.safe_pcsp_accumulate(x, li, Tv, 0, Tv, sc, False)
+    cold["pcsp_accumulate_2560"] = cold_line(hbm, nb, cold_launch_ms(torch, fn, sweep))
+    resident["pcsp_accumulate_2560"] = cache_line(nb, time_launches(torch, fn))
+    S = torch.empty(w4.k, dtype=torch.int32, device=dev)
+    C = torch.empty(N - w4.k, dtype=torch.int32, device=dev)
+    isn = torch.empty(N, dtype=torch.uint8, device=dev)
+    s01 = torch.empty(N, dtype=torch.float32, device=dev)
+    resident["pcsp_partition_2560"] = {
+        "ms": time_launches(torch, lambda: dts.safe_pcsp_partition(sc, w4.k, S, C, isn, s01)),
+        "note": "one workgroup over N=25600: latency-bound, no roofline"}
+    del x, li
+    # row gather / scatter: 3072^2 states with 6 instances (B = 12) per launch (two sets), and the 2560^2 state
+    wl, Bx = w5, 6 * w5.B
+    rows5 = torch.from_numpy(syn.random_rows(wl)).to(dev)
+    sets = [(torch.randn((Bx, wl.H, wl.N, wl.d), generator=g, device=dev).to(torch.bfloat16),
+             torch.empty((Bx, wl.H, wl.k, wl.d), dtype=torch.bfloat16, device=dev)) for _ in range(2)]
+    gs = 2 * 2.0 * Bx * wl.H * wl.k * wl.d
+    batched["gather_rows_3072x6"] = hbm(gs, time_rotating(torch, [
+        (lambda st=st, pk=pk: dts.safe_gather_rows(st, rows5, pk)) for st, pk in sets]))
+    batched["scatter_rows_3072x6"] = hbm(gs, time_rotating(torch, [
+        (lambda st=st, pk=pk: dts.safe_scatter_rows(pk, rows5, st)) for st, pk in sets]))
+    del sets
+    wl = w4
+    st = torch.randn((wl.B, wl.H, wl.N, wl.d), generator=g, device=dev).to(torch.bfloat16)
+    rows4 = torch.from_numpy(syn.random_rows(wl)).to(dev)
+    packed = torch.empty((wl.B, wl.H, wl.k, wl.d), dtype=torch.bfloat16, device=dev)
+    gs = 2 * 2.0 * wl.B * wl.H * wl.k * wl.d
+    for name, fn in (("gather_rows_2560", lambda: dts.safe_gather_rows(st, rows4, packed)),
+                     ("scatter_rows_2560", lambda: dts.safe_scatter_rows(packed, rows4, st))):
+        cold[name] = cold_line(hbm, gs, cold_launch_ms(torch, fn, sweep))
+        resident[name] = cache_line(gs, time_launches(torch, fn))
+    del st, packed
+    # SW-CFG and StepCache on the 3072^2 latent [16,384,384]; batched: 10 latents' channels per launch
     C5, Hl, Wl = w5.latent
-    for reps, tag, modes in ((10, "3072x10", (batched,)), (1, "3072", (cold, resident))):
-        Cx = C5 * reps
-        eps = torch.randn((2, Cx, Hl, Wl), generator=g, device=dev)
-        s5 = torch.rand(w5.N, generator=g, device=dev)
-        cout = torch.empty((Cx, Hl, Wl), dtype=torch.float32, device=dev)
-        cb = 3 * 4.0 * Cx * Hl * Wl + 4.0 * w5.N
-        fn = lambda: dts.safe_swcfg_combine(eps, s5, w5.side, w5.g_ctx, w5.g_sens, cout)
-        for m in modes:
-            m["swcfg_combine_" + tag] = (cache_line(cb, time_launches(torch, fn)) if m is resident
-                                         else cold_line(hbm, cb, cold_launch_ms(torch, fn, sweep)))
-        # StepCache reuses eps[0] / eps[1] as the two full predictions
-        sb = 12.0 * Cx * Hl * Wl
-        fn = lambda: dts.safe_stepcache_extrapolate(eps[0], eps[1], 1.0 / 3.0, cout)
-        for m in modes:
-            m["stepcache_" + tag] = (cache_line(sb, time_launches(torch, fn)) if m is resident
-                                     else cold_line(hbm, sb, cold_launch_ms(torch, fn, sweep)))
-        del eps, cout
-    # the elision scan on the 2560^2 all-valid image mask (655 MB bool, 2.62 GB fp32): batched by size
+    s5 = torch.rand(w5.N, generator=g, device=dev)
+    Cx = 10 * C5
+    sets = [(torch.randn((2, Cx, Hl, Wl), generator=g, device=dev),
+             torch.empty((Cx, Hl, Wl), dtype=torch.float32, device=dev)) for _ in range(2)]
+    batched["swcfg_combine_3072x10"] = hbm(3 * 4.0 * Cx * Hl * Wl + 4.0 * w5.N, time_rotating(torch, [
+        (lambda e=e, o=o: dts.safe_swcfg_combine(e, s5, w5.side, w5.g_ctx, w5.g_sens, o)) for e, o in sets]))
+    batched["stepcache_3072x10"] = hbm(12.0 * Cx * Hl * Wl, time_rotating(torch, [
+        (lambda e=e, o=o: dts.safe_stepcache_extrapolate(e[0], e[1], 1.0 / 3.0, o)) for e, o in sets]))
+    del sets
+    eps = torch.randn((2, C5, Hl, Wl), generator=g, device=dev)
+    cout = torch.empty((C5, Hl, Wl), dtype=torch.float32, device=dev)
+    cb, sb = 3 * 4.0 * C5 * Hl * Wl + 4.0 * w5.N, 12.0 * C5 * Hl * Wl
+    for name, nbytes, fn in (
+            ("swcfg_combine_3072", cb, lambda: dts.safe_swcfg_combine(eps, s5, w5.side, w5.g_ctx, w5.g_sens, cout)),
+            ("stepcache_3072", sb, lambda: dts.safe_stepcache_extrapolate(eps[0], eps[1], 1.0 / 3.0, cout))):
+        cold[name] = cold_line(hbm, nbytes, cold_launch_ms(torch, fn, sweep))
+        resident[name] = cache_line(nbytes, time_launches(torch, fn))
+    del eps, cout
+    # the elision scan on the 2560^2 all-valid image mask (655 MB bool, 2.62 GB fp32: one launch each exceeds
+    # the MALL), two masks of each kind alternated
     lflag = torch.zeros(1, dtype=torch.int32, device=dev)
-    for dt, esz in ((torch.bool, 1.0), (torch.float32, 4.0)):
-        m = (torch.ones if dt == torch.bool else torch.zeros)((1, 1, w4.N, w4.N), dtype=dt, device=dev)
-        batched["mask_scan_2560_" + ("bool" if dt == torch.bool else "f32")] = cold_line(
-            hbm, esz * w4.N * w4.N, cold_launch_ms(torch, lambda: dts.safe_mask_check_launch(m, w4.N, w4.T, w4.tv, lflag),
-                                                   sweep, reps=5))
-        del m
+    for dt, esz, tag in ((torch.bool, 1.0, "bool"), (torch.float32, 4.0, "f32")):
+        mk = (torch.ones if dt == torch.bool else torch.zeros)
+        masks = [mk((1, 1, w4.N, w4.N), dtype=dt, device=dev) for _ in range(2)]
+        batched["mask_scan_2560_" + tag] = hbm(esz * w4.N * w4.N, time_rotating(torch, [
+            (lambda m=m: dts.safe_mask_check_launch(m, w4.N, w4.T, w4.tv, lflag)) for m in masks], reps=4))
+        del masks
     src = torch.empty(256 << 20, dtype=torch.float32, device=dev).fill_(1.0)  # 1 GiB
     del sweep
     dst = torch.empty_like(src)
@@ -595,9 +636,10 @@ def hbm_stages(dts, torch, np, syn, dev, hbm):
             "shapes": "PCSP x [24,N,256] fp32 (3072^2: N=36864, Tv=200; 2560^2: N=25600, Tv=120); gather/scatter "
                       "state [B,24,N,64] bf16 (3072^2 x6: B=12, k=7373; 2560^2: B=2, k=5120); SW-CFG / StepCache "
                       "[2,C,384,384] / [C,384,384] fp32 (x10: C=160; single: C=16); mask [1,1,25600,25600]",
-            "note": "batched and cold: one launch, its own HIP event pair after a 1 GiB write + 1 GiB read sweep, "
-                    "minus the empty pair (ms_raw, event_pair_ms); the kernel trace of the same launches is "
-                    "in profiles/hbm_stages_large.md"}
+            "note": "batched: 8 back-to-back launches alternating over two buffer sets larger than the MALL, one "
+                    "event pair (4 launches for the mask scan); cold: one launch after a 1 GiB write + 1 GiB read "
+                    "sweep, its own event pair minus the empty pair (ms_raw, event_pair_ms); the kernel trace of "
+                    "the same launches is in profiles/hbm_stages_large.md"}
 
 
 def trajectory_3072(dts, torch, np, syn, dev, reps=2):

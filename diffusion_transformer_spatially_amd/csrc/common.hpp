@@ -32,6 +32,35 @@ __device__ __forceinline__ uint4 load_nt(const uint4* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+__device__ __forceinline__ void store_nt(float4* p, float4 v) {
+  const f32x4_nt w = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(w, reinterpret_cast<f32x4_nt*>(p));
+}
+__device__ __forceinline__ void store_nt(uint4* p, uint4 v) {
+  typedef uint32_t u32x4_nt __attribute__((ext_vector_type(4)));
+  const u32x4_nt w = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(w, reinterpret_cast<u32x4_nt*>(p));
+}
+
+// Streaming launches: a launch that moves more bytes than the 256 MB MALL (the last-level cache in front of
+// HBM) cannot keep its data cache-resident, so its once-used inputs and its outputs go through nontemporal
+// loads and stores (measured on MI355X with back-to-back launches over buffers larger than the MALL: row
+// gather 103 -> 90 us, SW-CFG 52 -> 47 us, StepCache 49 -> 44 us, PCSP 129 -> 118 us, mask scan 122 -> 111 us);
+// smaller launches keep plain accesses, so that data a previous kernel left in the MALL is used (with
+// nontemporal accesses the cache-resident 28 MB SW-CFG took 6.8 instead of 4.5 us).
+constexpr double kStreamBytes = 256.0 * 1024 * 1024;
+
+template <bool NT, class T>
+__device__ __forceinline__ T load_s(const T* p) {
+  if constexpr (NT) return load_nt(p);
+  else return *p;
+}
+template <bool NT, class T>
+__device__ __forceinline__ void store_s(T* p, T v) {
+  if constexpr (NT) store_nt(p, v);
+  else *p = v;
+}
+
 // Workgroup id remap so that consecutive logical tiles land on the same XCD (the hardware deals
 // workgroup ids round-robin over the 8 XCDs, each with its own L2).
 __device__ __forceinline__ uint32_t xcd_remap(uint32_t x, uint32_t G) {

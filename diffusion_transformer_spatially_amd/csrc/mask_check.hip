@@ -21,65 +21,6 @@ __device__ __forceinline__ float mask_value(const uint8_t* p, int dtype) {
 
 __global__ void k_flag_init(int32_t* flag) { *flag = 1; }
 
-// Block a of a row span [b0, hi) inside the mask buffer [buf_lo, buf_hi): one nontemporal 16-byte load when
-// the block lies inside the buffer (the mask is streamed once: 2560^2 bool 122 -> 111 us, fp32 453 -> 407 us),
-// else byte loads of the block's bytes inside the span only (the other bytes are returned as 0 and are never
-// tested).
-__device__ __forceinline__ uint4 load_block(uintptr_t a, uintptr_t buf_lo, uintptr_t buf_hi, uintptr_t b0,
-                                            uintptr_t hi) {
-  if (block_whole(a, buf_lo, buf_hi)) return load_nt(reinterpret_cast<const uint4*>(a));
-  uintptr_t r0, r1;
-  block_bytes(a, b0, hi, &r0, &r1);
-  uint32_t w[4] = {0u, 0u, 0u, 0u};
-  for (uintptr_t e = r0; e < r1; ++e) {
-    const uint32_t j = static_cast<uint32_t>(e - a);
-    w[j >> 2] |= static_cast<uint32_t>(*reinterpret_cast<const uint8_t*>(e)) << (8 * (j & 3));
-  }
-  return make_uint4(w[0], w[1], w[2], w[3]);
-}
-
-__global__ __launch_bounds__(kMaskThreads) void k_mask_check(const uint8_t* __restrict__ mask, uintptr_t buf_lo,
-                                                             uintptr_t buf_hi, int dtype, int esize, int cols,
-                                                             int ncheck, int zero_required, int32_t* flag,
-                                                             float* __restrict__ c_out, int early) {
-  const uint32_t row = blockIdx.x;
-  if (early && __atomic_load_n(flag, __ATOMIC_RELAXED) == 0) return;
-  const uint8_t* base = mask + static_cast<size_t>(row) * cols * esize;
-  const float first = mask_value(base, dtype);
-  bool ok = isfinite(first) && !(zero_required && first != 0.f);
-  // Aligned 16-byte blocks covering [base, base + ncheck * esize).
-  const uintptr_t b0 = reinterpret_cast<uintptr_t>(base);
-  const uintptr_t hi = b0 + static_cast<uintptr_t>(ncheck) * esize;
-  const RowBlocks rb = row_blocks(b0, hi);
-  for (uint32_t blk = threadIdx.x; ok && blk < rb.n; blk += kMaskThreads) {
-    const uintptr_t a = rb.lo + static_cast<uintptr_t>(blk) * 16;
-    const uint4 v = load_block(a, buf_lo, buf_hi, b0, hi);
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    if (dtype == SAFE_DTYPE_BOOL) {
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const uintptr_t ea = a + j;
-        if (ea < b0 || ea >= hi) continue;
-        const float m = ((w[j >> 2] >> (8 * (j & 3))) & 0xffu) ? 0.f : -INFINITY;
-        ok = ok && (m == first);
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uintptr_t ea = a + 4 * j;
-        if (ea < b0 || ea >= hi) continue;
-        ok = ok && (__uint_as_float(w[j]) == first);
-      }
-    }
-  }
-  const int all_ok = __syncthreads_and(ok ? 1 : 0);
-  if (threadIdx.x == 0) {
-    if (!all_ok) __atomic_store_n(flag, 0, __ATOMIC_RELAXED);
-    if (c_out != nullptr) c_out[row] = all_ok ? first : NAN;
-  }
-}
-
-
 // A byte of w is zero iff the corresponding byte of the result has its top bit set.
 __device__ __forceinline__ uint32_t zero_bytes(uint32_t w) { return (w - 0x01010101u) & ~w & 0x80808080u; }
 
@@ -115,28 +56,104 @@ __device__ __forceinline__ bool block_ok(uint4 v, uintptr_t a, uintptr_t b0, uin
   return ok;
 }
 
-constexpr int kScanRows = 4;
+// One mask entry as an additive value.
+__device__ __forceinline__ float entry_value(const uint8_t* p, int dtype) { return mask_value(p, dtype); }
 
+template <bool NT>
+__global__ __launch_bounds__(kMaskThreads) void k_mask_check(const uint8_t* __restrict__ mask, uintptr_t buf_lo,
+                                                             uintptr_t buf_hi, int dtype, int esize, int cols,
+                                                             int ncheck, int zero_required, int32_t* flag,
+                                                             float* __restrict__ c_out, int early) {
+  const uint32_t row = blockIdx.x;
+  if (early && __atomic_load_n(flag, __ATOMIC_RELAXED) == 0) return;
+  const uint8_t* base = mask + static_cast<size_t>(row) * cols * esize;
+  const float first = mask_value(base, dtype);
+  bool ok = isfinite(first) && !(zero_required && first != 0.f);
+  // Whole aligned 16-byte blocks of [base, base + ncheck * esize) with unconditional loads, then the entries
+  // outside them (buffer ends only) one at a time.
+  const uintptr_t b0 = reinterpret_cast<uintptr_t>(base);
+  const uintptr_t hi = b0 + static_cast<uintptr_t>(ncheck) * esize;
+  const RowBlocks rb = row_blocks(b0, hi, buf_lo, buf_hi);
+  const uint8_t* wp = base + (rb.wlo - b0);
+  for (uint32_t blk = threadIdx.x; ok && blk < rb.nw; blk += kMaskThreads) {
+    const uintptr_t a = rb.wlo + static_cast<uintptr_t>(blk) * 16;
+    ok = block_ok(load_s<NT>(reinterpret_cast<const uint4*>(wp) + blk), a, b0, hi, dtype, first);
+  }
+  uintptr_t e[4];
+  row_edges(b0, hi, rb, &e[0], &e[1], &e[2], &e[3]);
+  for (int r = 0; r < 2; ++r)
+    for (uintptr_t x = e[2 * r] + static_cast<uintptr_t>(threadIdx.x) * esize; ok && x < e[2 * r + 1];
+         x += static_cast<uintptr_t>(kMaskThreads) * esize)
+      ok = entry_value(base + (x - b0), dtype) == first;
+  const int all_ok = __syncthreads_and(ok ? 1 : 0);
+  if (threadIdx.x == 0) {
+    if (!all_ok) __atomic_store_n(flag, 0, __ATOMIC_RELAXED);
+    if (c_out != nullptr) c_out[row] = all_ok ? first : NAN;
+  }
+}
+
+
+constexpr int kScanRows = 4;
+constexpr int kScanUnroll = 2;  // 16-byte loads per row and thread issued before any is tested
+
+template <bool NT>
 __global__ __launch_bounds__(kMaskThreads) void k_mask_scan(const uint8_t* __restrict__ mask, uintptr_t buf_lo,
                                                             uintptr_t buf_hi, int dtype, int esize, int cols,
                                                             int nrows, int ncheck, int zero_required, int32_t* flag) {
   bool ok = true;
   for (int r0 = blockIdx.x * kScanRows; r0 < nrows; r0 += gridDim.x * kScanRows) {
     if (__atomic_load_n(flag, __ATOMIC_RELAXED) == 0) return;
+    // the workgroup's rows (a row past the end repeats the last row, whose verdict it then cannot change)
+    const uint8_t* base[kScanRows];
+    float first[kScanRows];
+    RowBlocks rb[kScanRows];
+    uint32_t nmax = 0;
 #pragma unroll
     for (int rr = 0; rr < kScanRows; ++rr) {
-      const int row = r0 + rr;
-      if (row >= nrows) break;
-      const uint8_t* base = mask + static_cast<size_t>(row) * cols * esize;
-      const float first = mask_value(base, dtype);
-      ok = ok && isfinite(first) && !(zero_required && first != 0.f);
-      const uintptr_t b0 = reinterpret_cast<uintptr_t>(base);
-      const uintptr_t hi = b0 + static_cast<uintptr_t>(ncheck) * esize;
-      const RowBlocks rb = row_blocks(b0, hi);
-      for (uint32_t blk = threadIdx.x; blk < rb.n; blk += kMaskThreads) {
-        const uintptr_t a = rb.lo + static_cast<uintptr_t>(blk) * 16;
-        ok = block_ok(load_block(a, buf_lo, buf_hi, b0, hi), a, b0, hi, dtype, first) && ok;
+      const int row = min(r0 + rr, nrows - 1);
+      base[rr] = mask + static_cast<size_t>(row) * cols * esize;
+      first[rr] = mask_value(base[rr], dtype);
+      ok = ok && isfinite(first[rr]) && !(zero_required && first[rr] != 0.f);
+      const uintptr_t b0 = reinterpret_cast<uintptr_t>(base[rr]);
+      rb[rr] = row_blocks(b0, b0 + static_cast<uintptr_t>(ncheck) * esize, buf_lo, buf_hi);
+      nmax = max(nmax, rb[rr].nw);
+    }
+    // whole blocks: kScanRows x kScanUnroll loads in flight per thread; a block index past a row's last block
+    // reloads that row's last block (never out of its row, result ignored)
+    for (uint32_t j0 = threadIdx.x; j0 < nmax; j0 += kMaskThreads * kScanUnroll) {
+      uint4 v[kScanRows][kScanUnroll];
+#pragma unroll
+      for (int rr = 0; rr < kScanRows; ++rr) {
+        const uint4* wp = reinterpret_cast<const uint4*>(base[rr] + (rb[rr].wlo - reinterpret_cast<uintptr_t>(base[rr])));
+#pragma unroll
+        for (int u = 0; u < kScanUnroll; ++u) {
+          const uint32_t blk = j0 + u * kMaskThreads;
+          v[rr][u] = rb[rr].nw > 0 ? load_s<NT>(wp + min(blk, rb[rr].nw - 1)) : make_uint4(0u, 0u, 0u, 0u);
+        }
       }
+#pragma unroll
+      for (int rr = 0; rr < kScanRows; ++rr) {
+        const uintptr_t b0 = reinterpret_cast<uintptr_t>(base[rr]);
+        const uintptr_t hi = b0 + static_cast<uintptr_t>(ncheck) * esize;
+#pragma unroll
+        for (int u = 0; u < kScanUnroll; ++u) {
+          const uint32_t blk = j0 + u * kMaskThreads;
+          const uintptr_t a = rb[rr].wlo + static_cast<uintptr_t>(blk) * 16;
+          ok = (blk >= rb[rr].nw || block_ok(v[rr][u], a, b0, hi, dtype, first[rr])) && ok;
+        }
+      }
+    }
+    // entries outside the whole blocks (the ends of a buffer whose base or length is not a multiple of 16)
+#pragma unroll
+    for (int rr = 0; rr < kScanRows; ++rr) {
+      const uintptr_t b0 = reinterpret_cast<uintptr_t>(base[rr]);
+      const uintptr_t hi = b0 + static_cast<uintptr_t>(ncheck) * esize;
+      uintptr_t e[4];
+      row_edges(b0, hi, rb[rr], &e[0], &e[1], &e[2], &e[3]);
+      for (int q = 0; q < 2; ++q)
+        for (uintptr_t x = e[2 * q] + static_cast<uintptr_t>(threadIdx.x) * esize; x < e[2 * q + 1];
+             x += static_cast<uintptr_t>(kMaskThreads) * esize)
+          ok = ok && entry_value(base[rr] + (x - b0), dtype) == first[rr];
     }
   }
   const int all_ok = __syncthreads_and(ok ? 1 : 0);
@@ -158,24 +175,31 @@ hipError_t launch_mask_check(const void* mask, int mask_dtype, int mB, int mH, i
   // the whole mask buffer: no load leaves it
   const uintptr_t buf_lo = reinterpret_cast<uintptr_t>(mask);
   const uintptr_t buf_hi = buf_lo + static_cast<uintptr_t>(mB) * mH * N * static_cast<uintptr_t>(cols) * esize;
+  const bool nt = static_cast<double>(buf_hi - buf_lo) > kStreamBytes;
   if (c_out == nullptr) {
     const size_t slice_bytes = static_cast<size_t>(mH) * N * cols * esize;
     const int nrows = mH * N;
     const uint32_t grid = static_cast<uint32_t>(std::min<int64_t>((nrows + kScanRows - 1) / kScanRows, 2048));
     for (int b = 0; b < mB; ++b) {
       const int tspan = mB == 1 ? tmax_all : tv[b];
-      k_mask_scan<<<grid, kMaskThreads, 0, s>>>(static_cast<const uint8_t*>(mask) + b * slice_bytes, buf_lo, buf_hi,
-                                                mask_dtype, esize, cols, nrows, ncheck_of(tspan), zero_of(tspan), flag);
+      if (nt)
+        k_mask_scan<true><<<grid, kMaskThreads, 0, s>>>(static_cast<const uint8_t*>(mask) + b * slice_bytes, buf_lo,
+                                                        buf_hi, mask_dtype, esize, cols, nrows, ncheck_of(tspan),
+                                                        zero_of(tspan), flag);
+      else
+        k_mask_scan<false><<<grid, kMaskThreads, 0, s>>>(static_cast<const uint8_t*>(mask) + b * slice_bytes, buf_lo,
+                                                         buf_hi, mask_dtype, esize, cols, nrows, ncheck_of(tspan),
+                                                         zero_of(tspan), flag);
     }
   } else if (mB == 1) {
     const int nc = ncheck_of(tmax_all), z = zero_of(tmax_all);
-    k_mask_check<<<static_cast<uint32_t>(mH) * N, kMaskThreads, 0, s>>>(
+    (nt ? k_mask_check<true> : k_mask_check<false>)<<<static_cast<uint32_t>(mH) * N, kMaskThreads, 0, s>>>(
         static_cast<const uint8_t*>(mask), buf_lo, buf_hi, mask_dtype, esize, cols, nc, z, flag, c_out, early);
   } else {
     const size_t slice_bytes = static_cast<size_t>(mH) * N * cols * esize;
     for (int b = 0; b < mB; ++b) {
       const int nc = ncheck_of(tv[b]), z = zero_of(tv[b]);
-      k_mask_check<<<static_cast<uint32_t>(mH) * N, kMaskThreads, 0, s>>>(
+      (nt ? k_mask_check<true> : k_mask_check<false>)<<<static_cast<uint32_t>(mH) * N, kMaskThreads, 0, s>>>(
           static_cast<const uint8_t*>(mask) + b * slice_bytes, buf_lo, buf_hi, mask_dtype, esize, cols, nc, z, flag,
           c_out ? c_out + static_cast<size_t>(b) * mH * N : nullptr, early);
     }

@@ -116,11 +116,11 @@ __global__ __launch_bounds__(kPcspThreads) void k_pcsp_accumulate(const float* _
 
 // Batched form for Tv <= 64*TV4 with float4 rows: each 16-lane group issues the loads of JB (head,
 // token) rows at once, with their image log-sum-exp values, and then reduces them from registers, so
-// HBM latency is paid once per batch instead of once per row.  The logits are read once, with
-// nontemporal loads (3072^2, 711 MB: 129 -> 120 us in one launch, 2560^2 cold: 53 -> 49 us).  The loads are unconditional (addresses
+// HBM latency is paid once per batch instead of once per row.  The logits are read once: nontemporal loads
+// when the launch streams more than the MALL holds (NT).  The loads are unconditional (addresses
 // of padded slots and of pairs past the end are clamped to valid memory and their values discarded
 // afterwards), so no load sits under divergent control flow and the waits stay exact.
-template <int TV4, bool SEL>
+template <int TV4, bool SEL, bool NT>
 __global__ __launch_bounds__(kPcspThreads) void k_pcsp_accumulate_b(const float* __restrict__ x,
                                                                    const float* __restrict__ lse_img, int H, int N,
                                                                    int T, int Tv, int c0, int c1,
@@ -152,7 +152,7 @@ __global__ __launch_bounds__(kPcspThreads) void k_pcsp_accumulate_b(const float*
 #pragma unroll
       for (int c = 0; c < TV4; ++c) {
         const int t = lane * 4 + 64 * c;
-        v[jj][c] = load_nt(reinterpret_cast<const float4*>(row + (t < Tv ? t : 0)));
+        v[jj][c] = load_s<NT>(reinterpret_cast<const float4*>(row + (t < Tv ? t : 0)));
       }
       li[jj] = lse_img != nullptr ? lse_img[ri] : 0.f;
     }
@@ -218,12 +218,19 @@ static void pcsp_launch(const float* x, const float* lse_img, int H, int N, int 
                    (!SEL || reinterpret_cast<uintptr_t>(sel) % 4 == 0);
   if (vec && Tv <= 256) {
     const int tv4 = Tv <= 64 ? 1 : Tv <= 128 ? 2 : Tv <= 192 ? 3 : 4;
-    switch (tv4) {
-      case 1: k_pcsp_accumulate_b<1, SEL><<<blocks, kPcspThreads, lds, s>>>(x, lse_img, H, N, T, Tv, c0, c1, sel, scores, accumulate); break;
-      case 2: k_pcsp_accumulate_b<2, SEL><<<blocks, kPcspThreads, lds, s>>>(x, lse_img, H, N, T, Tv, c0, c1, sel, scores, accumulate); break;
-      case 3: k_pcsp_accumulate_b<3, SEL><<<blocks, kPcspThreads, lds, s>>>(x, lse_img, H, N, T, Tv, c0, c1, sel, scores, accumulate); break;
-      default: k_pcsp_accumulate_b<4, SEL><<<blocks, kPcspThreads, lds, s>>>(x, lse_img, H, N, T, Tv, c0, c1, sel, scores, accumulate); break;
+    const bool nt = 4.0 * H * N * Tv > kStreamBytes;
+#define PCSP_B(TV, NTV) k_pcsp_accumulate_b<TV, SEL, NTV><<<blocks, kPcspThreads, lds, s>>>(x, lse_img, H, N, T, Tv, c0, c1, sel, scores, accumulate)
+    switch (tv4 * 2 + (nt ? 1 : 0)) {
+      case 2: PCSP_B(1, false); break;
+      case 3: PCSP_B(1, true); break;
+      case 4: PCSP_B(2, false); break;
+      case 5: PCSP_B(2, true); break;
+      case 6: PCSP_B(3, false); break;
+      case 7: PCSP_B(3, true); break;
+      case 8: PCSP_B(4, false); break;
+      default: PCSP_B(4, true); break;
     }
+#undef PCSP_B
   } else if (T % 4 == 0 && reinterpret_cast<uintptr_t>(x) % 16 == 0)
     k_pcsp_accumulate<true, SEL><<<blocks, kPcspThreads, lds, s>>>(x, lse_img, H, N, T, Tv, c0, c1, sel, scores, accumulate, H);
   else

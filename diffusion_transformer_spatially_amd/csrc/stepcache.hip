@@ -1,6 +1,7 @@
 // StepCache (AccelAes technical summary, 2. Methodology B.3): between full steps the noise prediction is
 // the line through the last two full predictions, out = eps_b + w (eps_b - eps_a).  Elementwise and
-// HBM-bound: 8 bytes read and 4 written per element.  out may alias an input element for element, so
+// HBM-bound: 8 bytes read and 4 written per element (nontemporal when the launch moves more than the MALL
+// holds).  out may alias an input element for element, so
 // the pointers are not restrict-qualified (each element is read before it is written, by one thread).
 #include "common.hpp"
 
@@ -9,19 +10,20 @@ namespace safe {
 __device__ __forceinline__ float extrap(float a, float b, float w) { return fmaf(w, b - a, b); }
 
 // One float4 per thread; the thread just past the last full vector also takes the 1-3 trailing elements.
+template <bool NT>
 __global__ __launch_bounds__(256) void k_stepcache_vec(const float* a, const float* b,
                                                        float w, float* out, size_t n) {
   const size_t e = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   const size_t n4 = n / 4;
   if (e < n4) {
-    const float4 va = reinterpret_cast<const float4*>(a)[e];
-    const float4 vb = reinterpret_cast<const float4*>(b)[e];
+    const float4 va = load_s<NT>(reinterpret_cast<const float4*>(a) + e);
+    const float4 vb = load_s<NT>(reinterpret_cast<const float4*>(b) + e);
     float4 o;
     o.x = extrap(va.x, vb.x, w);
     o.y = extrap(va.y, vb.y, w);
     o.z = extrap(va.z, vb.z, w);
     o.w = extrap(va.w, vb.w, w);
-    reinterpret_cast<float4*>(out)[e] = o;
+    store_s<NT>(reinterpret_cast<float4*>(out) + e, o);
   } else if (e == n4) {
     for (size_t i = 4 * n4; i < n; ++i) out[i] = extrap(a[i], b[i], w);
   }
@@ -40,7 +42,8 @@ hipError_t launch_stepcache(const float* eps_a, const float* eps_b, size_t n, fl
                      reinterpret_cast<uintptr_t>(out)) % 16) == 0;
   if (vec) {
     const size_t threads = n / 4 + 1;  // the extra thread takes the tail (if any)
-    k_stepcache_vec<<<static_cast<uint32_t>((threads + 255) / 256), 256, 0, s>>>(eps_a, eps_b, w, out, n);
+    auto kern = 12.0 * n > kStreamBytes ? k_stepcache_vec<true> : k_stepcache_vec<false>;
+    kern<<<static_cast<uint32_t>((threads + 255) / 256), 256, 0, s>>>(eps_a, eps_b, w, out, n);
   } else {
     k_stepcache_scalar<<<static_cast<uint32_t>((n + 255) / 256), 256, 0, s>>>(eps_a, eps_b, w, out, n);
   }

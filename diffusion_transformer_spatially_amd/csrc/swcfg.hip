@@ -1,6 +1,7 @@
 // SW-CFG combine (SAFE-DiT technical summary, Methodology 4; AccelAes summary B.2, spatial CFG):
 // gamma_i = g_ctx + (g_sens - g_ctx) s_i per token, out = eps_u + gamma (eps_c - eps_u) per latent
-// pixel.  Elementwise and HBM-bound: 8 bytes read and 4 written per pixel, float4 vectors along x.
+// pixel.  Elementwise and HBM-bound: 8 bytes read and 4 written per pixel, float4 vectors along x
+// (nontemporal when the launch moves more than the MALL holds).
 // The pixel -> token index arithmetic must stay cheaper than the memory traffic, so the vector path
 // divides through float reciprocals (exactly, see fdiv) instead of 32-bit integer divisions.
 #include "common.hpp"
@@ -22,14 +23,15 @@ __device__ __forceinline__ uint32_t fdiv(uint32_t a, FastDiv d) {
   return q;
 }
 
+template <bool NT>
 __global__ __launch_bounds__(256) void k_swcfg_vec(const float4* __restrict__ ec4, const float4* __restrict__ eu4,
                                                    const float* __restrict__ sv, FastDiv wl4, FastDiv hl,
                                                    uint32_t side, FastDiv ph, FastDiv pw, float g_ctx, float g_d,
                                                    float4* __restrict__ out4, uint32_t total4) {
   const uint32_t e = blockIdx.x * blockDim.x + threadIdx.x;
   if (e >= total4) return;
-  const float4 c = ec4[e];
-  const float4 u = eu4[e];
+  const float4 c = load_s<NT>(ec4 + e);
+  const float4 u = load_s<NT>(eu4 + e);
   const uint32_t row = fdiv(e, wl4);           // c * Hl + y
   const uint32_t x0 = (e - row * wl4.b) * 4;
   const uint32_t y = row - fdiv(row, hl) * hl.b;
@@ -50,7 +52,7 @@ __global__ __launch_bounds__(256) void k_swcfg_vec(const float4* __restrict__ ec
     o.z = guided(c.z, u.z, fmaf(g_d, sv[trow + x0 + 2], g_ctx));
     o.w = guided(c.w, u.w, fmaf(g_d, sv[trow + x0 + 3], g_ctx));
   }
-  out4[e] = o;
+  store_s<NT>(out4 + e, o);
 }
 
 __global__ __launch_bounds__(256) void k_swcfg_scalar(const float* __restrict__ ec, const float* __restrict__ eu,
@@ -75,7 +77,9 @@ hipError_t launch_swcfg(const float* eps, const float* sv, int C, int Hl, int Wl
     // one float4 per thread; the index arithmetic uses the float-reciprocal division (exact below 2^24)
     const uint32_t total4 = total / 4;
     auto fd = [](uint32_t b) { return FastDiv{b, 1.0f / static_cast<float>(b)}; };
-    k_swcfg_vec<<<(total4 + 255) / 256, 256, 0, s>>>(
+    const bool nt = 12.0 * total > kStreamBytes;  // two predictions read, one written
+    auto kern = nt ? k_swcfg_vec<true> : k_swcfg_vec<false>;
+    kern<<<(total4 + 255) / 256, 256, 0, s>>>(
         reinterpret_cast<const float4*>(eps), reinterpret_cast<const float4*>(eps + total), sv, fd(Wl / 4), fd(Hl),
         side, fd(ph), fd(pw), g_ctx, g_d, reinterpret_cast<float4*>(out), total4);
   } else {

@@ -237,9 +237,9 @@ _SPAN_CHECK = r"""
 #include "mask_span.hpp"
 #include <cstdio>
 #include <vector>
-// Walks the blocks the mask-scan kernels visit for every row of a mask placed at every byte offset of a
-// guarded arena, with the read decisions of mask_span.hpp, and checks that each byte read lies inside the
-// mask buffer and that every byte of each row's checked span is read.
+// Walks the reads the mask-scan kernels make for every row of a mask placed at every byte offset of a
+// guarded arena, with the decisions of mask_span.hpp (whole aligned blocks, then single entries), and checks
+// that each byte read lies inside the mask buffer and that every byte of each row's checked span is read.
 int main() {
   using namespace safe;
   long cases = 0;
@@ -259,18 +259,27 @@ int main() {
                 const uintptr_t b0 = buf_lo + static_cast<uintptr_t>(r) * cols * es;
                 const uintptr_t hi = b0 + static_cast<uintptr_t>(ncheck) * es;
                 std::vector<char> seen(hi - b0, 0);
-                const RowBlocks rb = row_blocks(b0, hi);
-                for (uint32_t blk = 0; blk < rb.n; ++blk) {
-                  const uintptr_t a = rb.lo + static_cast<uintptr_t>(blk) * 16;
-                  uintptr_t r0 = a, r1 = a + 16;
-                  if (!block_whole(a, buf_lo, buf_hi)) block_bytes(a, b0, hi, &r0, &r1);
-                  if (r0 < buf_lo || r1 > buf_hi) {
+                const RowBlocks rb = row_blocks(b0, hi, buf_lo, buf_hi);
+                // whole 16-byte blocks: aligned, inside the buffer
+                for (uint32_t blk = 0; blk < rb.nw; ++blk) {
+                  const uintptr_t a = rb.wlo + static_cast<uintptr_t>(blk) * 16;
+                  if ((a & 15) != 0 || a < buf_lo || a + 16 > buf_hi) {
                     std::printf("OUT es=%d off=%d N=%d cols=%d rows=%d ncheck=%d r=%d blk=%u\n", es, off, N, cols,
                                 nrows, ncheck, r, blk);
                     return 1;
                   }
-                  for (uintptr_t e = r0; e < r1; ++e)
+                  for (uintptr_t e = a; e < a + 16; ++e)
                     if (e >= b0 && e < hi) seen[e - b0] = 1;
+                }
+                // entries read one at a time: inside the row span, whole entries
+                uintptr_t e[4];
+                row_edges(b0, hi, rb, &e[0], &e[1], &e[2], &e[3]);
+                for (int q = 0; q < 2; ++q) {
+                  if (e[2 * q] < b0 || e[2 * q + 1] > hi || (e[2 * q] - b0) % es != 0 || (e[2 * q + 1] - b0) % es != 0) {
+                    std::printf("EDGE es=%d off=%d N=%d r=%d\n", es, off, N, r);
+                    return 1;
+                  }
+                  for (uintptr_t x = e[2 * q]; x < e[2 * q + 1]; ++x) seen[x - b0] = 1;
                 }
                 for (size_t i = 0; i < seen.size(); ++i)
                   if (!seen[i]) {
