@@ -623,7 +623,7 @@ def hbm_stages(dts, torch, np, syn, dev, hbm):
         mk = (torch.ones if dt == torch.bool else torch.zeros)
         masks = [mk((1, 1, w4.N, w4.N), dtype=dt, device=dev) for _ in range(2)]
         batched["mask_scan_2560_" + tag] = hbm(esz * w4.N * w4.N, time_rotating(torch, [
-            (lambda m=m: dts.safe_mask_check_launch(m, w4.N, w4.T, w4.tv, lflag)) for m in masks], reps=4))
+            (lambda m=m: dts.safe_mask_check_launch(m, w4.N, w4.T, w4.tv, lflag)) for m in masks]))
         del masks
     src = torch.empty(256 << 20, dtype=torch.float32, device=dev).fill_(1.0)  # 1 GiB
     del sweep
@@ -637,7 +637,7 @@ def hbm_stages(dts, torch, np, syn, dev, hbm):
                       "state [B,24,N,64] bf16 (3072^2 x6: B=12, k=7373; 2560^2: B=2, k=5120); SW-CFG / StepCache "
                       "[2,C,384,384] / [C,384,384] fp32 (x10: C=160; single: C=16); mask [1,1,25600,25600]",
             "note": "batched: 8 back-to-back launches alternating over two buffer sets larger than the MALL, one "
-                    "event pair (4 launches for the mask scan); cold: one launch after a 1 GiB write + 1 GiB read "
+                    "event pair; cold: one launch after a 1 GiB write + 1 GiB read "
                     "sweep, its own event pair minus the empty pair (ms_raw, event_pair_ms); the kernel trace of "
                     "the same launches is in profiles/hbm_stages_large.md"}
 

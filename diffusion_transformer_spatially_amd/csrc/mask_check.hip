@@ -94,9 +94,10 @@ __global__ __launch_bounds__(kMaskThreads) void k_mask_check(const uint8_t* __re
 
 
 constexpr int kScanRows = 4;
-constexpr int kScanUnroll = 2;  // 16-byte loads per row and thread issued before any is tested
 
-template <bool NT>
+// U: 16-byte loads per row and thread issued before any is tested (2 for rows of 512 blocks or more; a row
+// of 4096 bytes is one block per thread, and a second load would only repeat the last block).
+template <bool NT, int U>
 __global__ __launch_bounds__(kMaskThreads) void k_mask_scan(const uint8_t* __restrict__ mask, uintptr_t buf_lo,
                                                             uintptr_t buf_hi, int dtype, int esize, int cols,
                                                             int nrows, int ncheck, int zero_required, int32_t* flag) {
@@ -118,15 +119,15 @@ __global__ __launch_bounds__(kMaskThreads) void k_mask_scan(const uint8_t* __res
       rb[rr] = row_blocks(b0, b0 + static_cast<uintptr_t>(ncheck) * esize, buf_lo, buf_hi);
       nmax = max(nmax, rb[rr].nw);
     }
-    // whole blocks: kScanRows x kScanUnroll loads in flight per thread; a block index past a row's last block
+    // whole blocks: kScanRows x U loads in flight per thread; a block index past a row's last block
     // reloads that row's last block (never out of its row, result ignored)
-    for (uint32_t j0 = threadIdx.x; j0 < nmax; j0 += kMaskThreads * kScanUnroll) {
-      uint4 v[kScanRows][kScanUnroll];
+    for (uint32_t j0 = threadIdx.x; j0 < nmax; j0 += kMaskThreads * U) {
+      uint4 v[kScanRows][U];
 #pragma unroll
       for (int rr = 0; rr < kScanRows; ++rr) {
         const uint4* wp = reinterpret_cast<const uint4*>(base[rr] + (rb[rr].wlo - reinterpret_cast<uintptr_t>(base[rr])));
 #pragma unroll
-        for (int u = 0; u < kScanUnroll; ++u) {
+        for (int u = 0; u < U; ++u) {
           const uint32_t blk = j0 + u * kMaskThreads;
           v[rr][u] = rb[rr].nw > 0 ? load_s<NT>(wp + min(blk, rb[rr].nw - 1)) : make_uint4(0u, 0u, 0u, 0u);
         }
@@ -136,7 +137,7 @@ __global__ __launch_bounds__(kMaskThreads) void k_mask_scan(const uint8_t* __res
         const uintptr_t b0 = reinterpret_cast<uintptr_t>(base[rr]);
         const uintptr_t hi = b0 + static_cast<uintptr_t>(ncheck) * esize;
 #pragma unroll
-        for (int u = 0; u < kScanUnroll; ++u) {
+        for (int u = 0; u < U; ++u) {
           const uint32_t blk = j0 + u * kMaskThreads;
           const uintptr_t a = rb[rr].wlo + static_cast<uintptr_t>(blk) * 16;
           ok = (blk >= rb[rr].nw || block_ok(v[rr][u], a, b0, hi, dtype, first[rr])) && ok;
@@ -182,14 +183,12 @@ hipError_t launch_mask_check(const void* mask, int mask_dtype, int mB, int mH, i
     const uint32_t grid = static_cast<uint32_t>(std::min<int64_t>((nrows + kScanRows - 1) / kScanRows, 2048));
     for (int b = 0; b < mB; ++b) {
       const int tspan = mB == 1 ? tmax_all : tv[b];
-      if (nt)
-        k_mask_scan<true><<<grid, kMaskThreads, 0, s>>>(static_cast<const uint8_t*>(mask) + b * slice_bytes, buf_lo,
-                                                        buf_hi, mask_dtype, esize, cols, nrows, ncheck_of(tspan),
-                                                        zero_of(tspan), flag);
-      else
-        k_mask_scan<false><<<grid, kMaskThreads, 0, s>>>(static_cast<const uint8_t*>(mask) + b * slice_bytes, buf_lo,
-                                                         buf_hi, mask_dtype, esize, cols, nrows, ncheck_of(tspan),
-                                                         zero_of(tspan), flag);
+      const int nc = ncheck_of(tspan), z = zero_of(tspan);
+      const uint8_t* mb = static_cast<const uint8_t*>(mask) + b * slice_bytes;
+      const bool wide = static_cast<int64_t>(nc) * esize >= 512 * 16;
+      auto kern = nt ? (wide ? k_mask_scan<true, 2> : k_mask_scan<true, 1>)
+                     : (wide ? k_mask_scan<false, 2> : k_mask_scan<false, 1>);
+      kern<<<grid, kMaskThreads, 0, s>>>(mb, buf_lo, buf_hi, mask_dtype, esize, cols, nrows, nc, z, flag);
     }
   } else if (mB == 1) {
     const int nc = ncheck_of(tmax_all), z = zero_of(tmax_all);
