@@ -1047,6 +1047,9 @@ __global__ __launch_bounds__(kThreads * KS) __attribute__((amdgpu_waves_per_eu(2
   __shared__ __attribute__((aligned(16))) uint16_t v_as[KS][kTileElems<D>];
   __shared__ __attribute__((aligned(16))) uint16_t k_bs[KS][kTileElems<D>];
   __shared__ __attribute__((aligned(16))) uint16_t v_bs[KS][kTileElems<D>];
+  // Key halves at head dim 128: each half synchronises its four waves by itself (see tile_barrier below).
+  constexpr bool kHalfBarrier = KS == 2 && D == 128;
+  __shared__ uint32_t half_arrivals[2];
   // key half of this wave (KS = 2: waves 0-3 take the first half of the key tiles, waves 4-7 the rest)
   const int half = KS == 1 ? 0 : __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 8));
   uint16_t* const k_a = k_as[half];
@@ -1115,14 +1118,14 @@ __global__ __launch_bounds__(kThreads * KS) __attribute__((amdgpu_waves_per_eu(2
   const int n_full = a.N / kBN;  // image tiles with all 64 keys valid
   const int n_txt = (tv + kBN - 1) / kBN;
   const int ntiles = n_img + n_txt;
-  // this wave's key tiles [t_begin, t_end); with two key halves the shorter half passes `pad` extra
-  // barriers so that both halves pass the same number
+  // this wave's key tiles [t_begin, t_end); with two key halves under the workgroup barrier the shorter
+  // half passes `pad` extra barriers so that both halves pass the same number
   int t_begin = 0, t_end = ntiles, pad = 0;
   if constexpr (KS == 2) {
     const int n0 = (ntiles + 1) >> 1;
     t_begin = half ? n0 : 0;
     t_end = half ? ntiles : n0;
-    pad = half ? 2 * n0 - ntiles : 0;
+    pad = half && !kHalfBarrier ? 2 * n0 - ntiles : 0;
   }
   // the warmup emission only runs on the exact-sum path (the host picks it whenever an output asks for it)
   const bool emit = EXACT_SUM && b == 0 && (a.xattn_out != nullptr || a.lse_img_out != nullptr);
@@ -1164,8 +1167,33 @@ __global__ __launch_bounds__(kThreads * KS) __attribute__((amdgpu_waves_per_eu(2
   mask_fetch(mcur, 0);
 
   if (t_begin < t_end) stage_issue<D, (QB > 1), FP8>(tile_src<D, FP8>(a, bh, t_begin, n_img, tv), k_a, v_a);
+  if (kHalfBarrier && threadIdx.x < 2) half_arrivals[threadIdx.x] = 0u;
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  // End of a tile: the tile copies of every wave that reads this buffer have landed and no wave reads the
+  // buffer the next copy overwrites.  Normally the workgroup barrier.  Key halves at head dim 128 (one query
+  // block per wave, so a wave's matrix work and its softmax alternate instead of overlapping) use a barrier
+  // of the half's four waves only: under the workgroup barrier the two waves that share a SIMD, one from
+  // each half, run their matrix and their softmax phases at the same time; apart, they overlap (+7% on the
+  // 1024^2 sensitive-row launch; at head dim 64 the staggered query blocks already overlap inside a wave and
+  // the split barrier measured 3-6% slower).  Each wave waits for its own copies and LDS reads, adds one to
+  // its half's counter and sleeps until the counter shows four arrivals per tile passed.  The halves share
+  // no tile buffer, and the four waves of a half run the same tiles, so each passes the same count.
+  uint32_t passed = 0;
+  auto tile_barrier = [&]() {
+    __builtin_amdgcn_s_waitcnt(0);
+    if constexpr (!kHalfBarrier) {
+      __syncthreads();
+    } else {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      if (L == 0) __hip_atomic_fetch_add(&half_arrivals[half], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      passed += 4u;
+      while (__builtin_amdgcn_readfirstlane(__hip_atomic_load(&half_arrivals[half], __ATOMIC_RELAXED,
+                                                              __HIP_MEMORY_SCOPE_WORKGROUP)) < passed)
+        __builtin_amdgcn_s_sleep(1);
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    }
+  };
 
   float* const no_store[QB] = {};
   // One tile: prefetch tile t+1 into the other buffer, compute on this one, then wait for the
@@ -1191,8 +1219,7 @@ __global__ __launch_bounds__(kThreads * KS) __attribute__((amdgpu_waves_per_eu(2
       mask_fetch(mnext, t + 1);
     }
     tile_step<QB, false, EXACT_SUM, KM, D, FP8>(st, ck, cv, kperm, g, li, dc0, c2, kBN, no_store, a.scale, mcur);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    tile_barrier();
     if constexpr (KM != 0) mcur = mnext;
   };
   auto masked_tile = [&](int t, const uint16_t* ck, const uint16_t* cv, uint16_t* nk, uint16_t* nv) {
@@ -1210,8 +1237,7 @@ __global__ __launch_bounds__(kThreads * KS) __attribute__((amdgpu_waves_per_eu(2
                    ? a.xattn_out + (static_cast<size_t>(h) * a.N + row[qb]) * a.T + (t - n_img) * kBN
                    : nullptr;
     tile_step<QB, true, EXACT_SUM, KM, D, FP8>(st, ck, cv, kperm, g, li, dc0, c2, nvalid, xo, a.scale, mcur);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    tile_barrier();
     if constexpr (KM != 0) mcur = mnext;
   };
 
@@ -1235,6 +1261,7 @@ __global__ __launch_bounds__(kThreads * KS) __attribute__((amdgpu_waves_per_eu(2
 
   if constexpr (KS == 2) {
     for (int i = 0; i < pad; ++i) __syncthreads();
+    if constexpr (kHalfBarrier) __syncthreads();  // both halves are done with their tile buffers
     // merge the second key half into the first through LDS (the tile buffers are idle now): per query
     // block, the partner wave's running max, row sum and output accumulators, each lane with the
     // lane of the same index (same rows, same register layout).  The first half of the accumulator

@@ -61,7 +61,9 @@ def test_d128_rows_parity_and_untouched_context(lib, k):
     (2, 8, 4160, 256, (77, 0), None),       # 2080 one-block waves: no split
     (2, 24, 4096, 256, (77, 77), 1229),     # the 1024^2 rows launch (1872 waves): halves, gathered rows
     (1, 3, 193, 0, (0,), None),             # 4 key tiles: halves of 2 and 2 (ragged tail in the second)
-    (1, 3, 130, 0, (0,), None),             # 3 key tiles: the second half passes one extra barrier
+    (1, 3, 130, 0, (0,), None),             # 3 key tiles: halves of 2 and 1
+    (1, 3, 40, 0, (0,), None),              # 1 key tile: the second half has none
+    (2, 2, 64, 256, (70, 3), None),         # 3 and 2 key tiles by batch entry (text tiles in both halves)
 ])
 def test_d128_work_shapes(lib, B, H, N, T, tv, k):
     w = _w("srsu_1024", B=B, H=H, N=N, T=T, tv=tv)
