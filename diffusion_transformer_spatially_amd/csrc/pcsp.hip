@@ -266,6 +266,48 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
+// Whole-wave all-reduce without LDS: the four DPP steps of each 16-lane row (as group16_* above), then
+// the row-pair and half-wave exchanges of v_permlane16_swap / v_permlane32_swap, combining what each lane
+// holds with what its partner row holds.  Every lane ends with the result.  (A __shfl_xor ladder is six
+// dependent ds_bpermute round trips per value.)
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_allreduce(uint32_t v, Op op) {
+  v = op(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(v), static_cast<int>(v), kDppXor1, 0xf, 0xf, false)));
+  v = op(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(v), static_cast<int>(v), kDppXor2, 0xf, 0xf, false)));
+  v = op(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(v), static_cast<int>(v), kDppHalfMirror, 0xf, 0xf, false)));
+  v = op(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(v), static_cast<int>(v), kDppMirror, 0xf, 0xf, false)));
+  const auto r16 = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = op(r16[0], r16[1]);
+  const auto r32 = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return op(r32[0], r32[1]);
+}
+__device__ __forceinline__ uint32_t wave_and(uint32_t v) { return wave_allreduce(v, [](uint32_t a, uint32_t b) { return a & b; }); }
+__device__ __forceinline__ uint32_t wave_or(uint32_t v) { return wave_allreduce(v, [](uint32_t a, uint32_t b) { return a | b; }); }
+__device__ __forceinline__ float wave_fmin(float v) {
+  return __uint_as_float(wave_allreduce(__float_as_uint(v), [](uint32_t a, uint32_t b) {
+    return __float_as_uint(fminf(__uint_as_float(a), __uint_as_float(b)));
+  }));
+}
+__device__ __forceinline__ float wave_fmax(float v) {
+  return __uint_as_float(wave_allreduce(__float_as_uint(v), [](uint32_t a, uint32_t b) {
+    return __float_as_uint(fmaxf(__uint_as_float(a), __uint_as_float(b)));
+  }));
+}
+
+// Inclusive sum over lanes 0 .. L of the wave without LDS: row shifts by 1, 2, 4 and 8 (lanes past the row
+// start add 0) give each 16-lane row its own scan; then the last lane of rows 0 and 2 is broadcast into rows 1
+// and 3, and the last lane of row 1 (by then the total of rows 0 and 1) into rows 2 and 3.
+__device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t v) {
+  constexpr int kRowShr = 0x110, kRowBcast15 = 0x142, kRowBcast31 = 0x143;
+  v += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), kRowShr + 1, 0xf, 0xf, false));
+  v += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), kRowShr + 2, 0xf, 0xf, false));
+  v += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), kRowShr + 4, 0xf, 0xf, false));
+  v += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), kRowShr + 8, 0xf, 0xf, false));
+  v += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), kRowBcast15, 0xa, 0xf, false));
+  v += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), kRowBcast31, 0xc, 0xf, false));
+  return v;
+}
+
 // Exclusive block prefix count of a per-thread flag and the block total.  wcnt: [kPartWaves] LDS slots
 // used by this call only (alternate two sets between consecutive calls so one barrier suffices).
 __device__ __forceinline__ uint32_t block_flag_scan(bool flag, uint32_t* wcnt, uint32_t* total) {
@@ -298,7 +340,8 @@ __global__ __launch_bounds__(kPartThreads) void k_partition(const float* __restr
   float lo = INFINITY, hi = -INFINITY;
   if (s01 != nullptr) {
     for (int i = tid; i < N; i += kPartThreads) { const float a = scores[i]; lo = fminf(lo, a); hi = fmaxf(hi, a); }
-    for (int o = 32; o >= 1; o >>= 1) { lo = fminf(lo, __shfl_xor(lo, o, 64)); hi = fmaxf(hi, __shfl_xor(hi, o, 64)); }
+    lo = wave_fmin(lo);
+    hi = wave_fmax(hi);
     if (lane == 0) { red_lo[w] = lo; red_hi[w] = hi; }
     __syncthreads();
     lo = red_lo[0]; hi = red_hi[0];
@@ -323,12 +366,7 @@ __global__ __launch_bounds__(kPartThreads) void k_partition(const float* __restr
         uint32_t c[4], loc = 0;
 #pragma unroll
         for (int j = 0; j < 4; ++j) { c[j] = hist[255 - 4 * lane - j]; loc += c[j]; }
-        uint32_t inc = loc;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          const uint32_t y = __shfl_up(inc, o, 64);
-          if (lane >= o) inc += y;
-        }
+        const uint32_t inc = wave_inclusive_sum(loc);
         const uint32_t exc = inc - loc;
         if (exc < remaining && remaining <= inc) {
           uint32_t acc = exc;
@@ -383,14 +421,17 @@ __global__ __launch_bounds__(kPartThreads) void k_partition(const float* __restr
 // Register-resident form for N <= 1024 * IPT.  Wave w owns the CH = 64 * IPT consecutive indices
 // [w * CH, (w + 1) * CH); lane l holds item j at index w * CH + 64 j + l, so every load is coalesced
 // and, for each j, the wave's 64 lanes cover 64 consecutive indices.  The keys are loaded once and stay
-// in registers for every pass.  The radix select starts at the highest bit in which the keys differ
-// (block AND / OR of the keys), so the leading bits that all keys share -- sign and exponent for scores
-// of one magnitude -- cost no pass, and no pass piles every key onto one histogram bin.  The output
-// walks each wave's items in index order with ballots (rank among the wave's earlier lanes by mbcnt,
-// running totals in scalars); one block scan of the per-wave totals gives each wave its base.  Slots
-// past N hold key 0 (the NaN key) and take part in the counts: they are the lowest keys and, among
-// equal keys, the highest indices, so they never reach S (k <= N) and never move the k-th largest key;
-// only the AND / OR and the stores skip them.
+// in registers for every pass.  The radix select runs on the offsets key - kmin of the valid keys (block
+// min / max; subtracting kmin keeps the order and the ties), from the highest bit of kmax - kmin down, in
+// the fewest passes of at most 9 bits: the leading bits that every key shares cost no pass, and the first
+// digit cuts the keys' actual range into up to 512 bins.  (On the keys themselves, the first digit of
+// scores spanning a few binades is mostly exponent bits, which piles the keys onto two or three bins, and
+// LDS atomics of a wave on one address run one lane at a time: that pass took six times as long as the
+// next.)  Wave reductions use DPP and the lane-swap instructions, not LDS.  The output walks each wave's items in
+// index order with ballots (rank among the wave's earlier lanes by mbcnt, running totals in scalars); one
+// block scan of the per-wave totals gives each wave its base.  Slots past N hold key 0 (the NaN key): they
+// are left out of the counts, and in the output they are the highest indices, so they never reach S
+// (k <= N); the stores skip them.
 __device__ __forceinline__ float key_value(uint32_t key) {
   if (key == 0u) return NAN;
   return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
@@ -402,88 +443,111 @@ __device__ __forceinline__ uint32_t lanes_below(unsigned long long b) {
                                    __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(b), 0u));
 }
 
-template <int IPT>
-__global__ __launch_bounds__(kPartThreads) void k_partition_reg(const float* __restrict__ scores, int N, int k,
+template <int IPT, int NT = kPartThreads, int DB = 9>
+__global__ __launch_bounds__(NT) void k_partition_reg(const float* __restrict__ scores, int N, int k,
                                                                 int32_t* __restrict__ S, int32_t* __restrict__ C,
                                                                 uint8_t* __restrict__ is_sens,
                                                                 float* __restrict__ s01) {
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t wred[4][kPartWaves];
-  __shared__ uint32_t sel_digit, sel_above;
+  // pass p counts into hist[p & 1] (digits of up to DB bits); the other is cleared meanwhile
+  constexpr int kBins = 1 << DB, kBinsPerLane = kBins / 64;
+  static_assert(kBinsPerLane % 4 == 0, "whole 16-byte reads of the bins");
+  __shared__ __attribute__((aligned(16))) uint32_t hist[2][kBins];
+  constexpr int kW = NT / 64;  // waves
+  __shared__ uint32_t wred[4][kW];  // per-wave min / max
+  __shared__ uint32_t wcnt[2][kW];  // per-wave output counts
+  __shared__ uint32_t sel_digit, sel_above, sel_count;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int base = w * 64 * IPT + lane;  // index of item j: base + 64 j
 
   uint32_t key[IPT];
-  uint32_t kand = 0xffffffffu, kor = 0u;
+  uint32_t kmin = 0xffffffffu, kmax = 0u;
   float lo = INFINITY, hi = -INFINITY;
 #pragma unroll
   for (int j = 0; j < IPT; ++j) {
     const int i = base + 64 * j;
     const float a = i < N ? scores[i] : NAN;
     key[j] = order_key(a);
-    kand &= i < N ? key[j] : 0xffffffffu;
-    kor |= i < N ? key[j] : 0u;
+    kmin = min(kmin, i < N ? key[j] : 0xffffffffu);
+    kmax = max(kmax, i < N ? key[j] : 0u);
     lo = fminf(lo, a);
     hi = fmaxf(hi, a);
   }
-  for (int o = 32; o >= 1; o >>= 1) {
-    kand &= __shfl_xor(kand, o, 64);
-    kor |= __shfl_xor(kor, o, 64);
-    lo = fminf(lo, __shfl_xor(lo, o, 64));
-    hi = fmaxf(hi, __shfl_xor(hi, o, 64));
-  }
+  kmin = wave_allreduce(kmin, [](uint32_t x, uint32_t y) { return min(x, y); });
+  kmax = wave_allreduce(kmax, [](uint32_t x, uint32_t y) { return max(x, y); });
+  lo = wave_fmin(lo);
+  hi = wave_fmax(hi);
   if (lane == 0) {
-    wred[0][w] = kand;
-    wred[1][w] = kor;
+    wred[0][w] = kmin;
+    wred[1][w] = kmax;
     wred[2][w] = __float_as_uint(lo);
     wred[3][w] = __float_as_uint(hi);
   }
+  for (int t = tid; t < 2 * kBins; t += NT) hist[t / kBins][t % kBins] = 0;
   __syncthreads();
 #pragma unroll
-  for (int j = 0; j < kPartWaves; ++j) {
-    kand &= wred[0][j];
-    kor |= wred[1][j];
+  for (int j = 0; j < kW; ++j) {
+    kmin = min(kmin, wred[0][j]);
+    kmax = max(kmax, wred[1][j]);
     lo = fminf(lo, __uint_as_float(wred[2][j]));
     hi = fmaxf(hi, __uint_as_float(wred[3][j]));
   }
-  __syncthreads();
   const bool all_nan = !(lo <= hi);
+  // offsets from here on; slots past N get 0 (never above K*, and the last in index order among equal ones)
+#pragma unroll
+  for (int j = 0; j < IPT; ++j) key[j] = base + 64 * j < N ? key[j] - kmin : 0u;
 
-  // ---- radix select of the k-th largest key over the bits in which the keys differ
-  uint32_t prefix = 0, pmask = 0, remaining = static_cast<uint32_t>(k);
+  // ---- radix select of the k-th largest offset key - kmin of the valid keys, over the fewest passes of at
+  // most DB bits that cover kmax - kmin, of near-equal widths (25 bits: 9 + 8 + 8; with 8-bit digits, four
+  // passes took 1k clocks more at N = 4096)
+  uint32_t prefix = 0, remaining = static_cast<uint32_t>(k);
+  uint32_t total_eq = static_cast<uint32_t>(N);  // valid keys equal to K* (all of them when all are equal)
   if (k > 0) {
-    const uint32_t diff = kand ^ kor;
-    int hb = diff != 0u ? 31 - __clz(diff) : -1;  // highest differing bit; -1: all keys equal
-    pmask = hb < 0 ? 0xffffffffu : hb == 31 ? 0u : ~((2u << hb) - 1u);
-    prefix = kand & pmask;
-    while (hb >= 0) {
-      const int lob = hb >= 7 ? hb - 7 : 0;
-      const uint32_t dmask = (2u << (hb - lob)) - 1u;
-      if (tid < 256) hist[tid] = 0;
-      __syncthreads();
+    const uint32_t span = kmax - kmin;  // every valid offset lies in [0, span]
+    const int nbits = span != 0u ? 32 - __clz(span) : 0;
+    const int npass = (nbits + DB - 1) / DB;
+    uint32_t pmask = nbits == 32 ? 0u : ~((1u << nbits) - 1u);  // bits already decided (zero in every offset)
+    int hb = nbits - 1;
+    for (int pass = 0; pass < npass; ++pass) {
+      const int width = (hb + npass - pass) / (npass - pass);  // ceil(bits left / passes left) <= DB
+      const int lob = hb + 1 - width;
+      const uint32_t dmask = (1u << width) - 1u;
+      uint32_t* const h = hist[pass & 1];
 #pragma unroll
       for (int j = 0; j < IPT; ++j)
-        if ((key[j] & pmask) == prefix) atomicAdd(&hist[(key[j] >> lob) & dmask], 1u);
+        if (base + 64 * j < N && (key[j] & pmask) == prefix) atomicAdd(&h[(key[j] >> lob) & dmask], 1u);
       __syncthreads();
+      if (w != 0)  // the next pass's bins (last read two passes ago), while wave 0 scans this pass's
+        for (int t = tid - 64; t < kBins; t += NT - 64) hist[(pass + 1) & 1][t] = 0;
       if (w == 0) {
-        // lane l owns bins 255-4l .. 252-4l (descending); find where the running count from the top
-        // first reaches `remaining`
-        uint32_t c[4], loc = 0;
+        // lane l owns the kBinsPerLane bins below kBins - kBinsPerLane * l (descending; bins past dmask stay
+        // 0); find where the running count from the top first reaches `remaining`
+        const uint4* hp = reinterpret_cast<const uint4*>(h + kBins - kBinsPerLane * (lane + 1));
+        uint32_t c[kBinsPerLane];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) { c[j] = hist[255 - 4 * lane - j]; loc += c[j]; }
-        uint32_t inc = loc;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          const uint32_t y = __shfl_up(inc, o, 64);
-          if (lane >= o) inc += y;
+        for (int u = 0; u < kBinsPerLane / 4; ++u) {
+          const uint4 v = hp[u];
+          const int q = kBinsPerLane - 1 - 4 * u;  // c[q] = the highest bin of this read
+          c[q] = v.x;
+          c[q - 1] = v.y;
+          c[q - 2] = v.z;
+          c[q - 3] = v.w;
         }
+        uint32_t loc = 0;
+#pragma unroll
+        for (int q = 0; q < kBinsPerLane; ++q) loc += c[q];
+        const uint32_t inc = wave_inclusive_sum(loc);
         const uint32_t exc = inc - loc;
         if (exc < remaining && remaining <= inc) {
           uint32_t acc = exc;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            if (acc + c[j] >= remaining) { sel_digit = 255u - 4u * lane - j; sel_above = acc; break; }
-            acc += c[j];
+          for (int q = 0; q < kBinsPerLane; ++q) {
+            if (acc + c[q] >= remaining) {
+              sel_digit = kBins - 1u - kBinsPerLane * lane - q;
+              sel_above = acc;
+              sel_count = c[q];
+              break;
+            }
+            acc += c[q];
           }
         }
       }
@@ -492,36 +556,47 @@ __global__ __launch_bounds__(kPartThreads) void k_partition_reg(const float* __r
       prefix |= sel_digit << lob;
       pmask |= dmask << lob;
       hb = lob - 1;
+      total_eq = sel_count;  // after the last pass: the keys whose offset is K*
     }
   }
-  const uint32_t kstar = prefix;
+  const uint32_t kstar = prefix;  // the k-th largest offset
   const uint32_t need = (k > 0) ? remaining : 0u;  // how many keys equal to K* are taken
 
-  // ---- output.  Pass 1: each wave's count of keys equal to K*; block scan -> the wave's base rank.
-  uint32_t w_eq = 0;
-#pragma unroll
-  for (int j = 0; j < IPT; ++j) w_eq += static_cast<uint32_t>(__popcll(__ballot(k > 0 && key[j] == kstar)));
-  if (lane == 0) wred[0][w] = w_eq;
-  __syncthreads();
+  // ---- output.  When every key equal to K* is taken (always without ties at the boundary), S is the set of
+  // offsets >= K*; otherwise the equal keys are taken in index order, which needs each wave's count of them
+  // first.  Slots past N are never selected (and come last among equal keys).
+  const bool all_eq_taken = need == total_eq;
+  auto selected = [&](int j, unsigned long long be, uint32_t run) -> bool {
+    if (k <= 0) return false;
+    if (all_eq_taken) return base + 64 * j < N && key[j] >= kstar;
+    const bool eq = (be >> lane) & 1ull;
+    return key[j] > kstar || (eq && run + lanes_below(be) < need);
+  };
+  // Pass 1 (ties only): each wave's count of keys equal to K*; block scan -> the wave's base rank.
   uint32_t eq_run = 0;
-  for (int j = 0; j < w; ++j) eq_run += wred[0][j];
-  // Pass 2: each wave's count of selected keys (equal keys in index order against `need`).
+  if (k > 0 && !all_eq_taken) {
+    uint32_t w_eq = 0;
+#pragma unroll
+    for (int j = 0; j < IPT; ++j) w_eq += static_cast<uint32_t>(__popcll(__ballot(key[j] == kstar)));
+    if (lane == 0) wcnt[0][w] = w_eq;
+    __syncthreads();
+    for (int j = 0; j < w; ++j) eq_run += wcnt[0][j];
+  }
+  // Pass 2: each wave's count of selected keys; block scan -> the wave's base slot in S.
   uint32_t w_sel = 0;
   {
     uint32_t run = eq_run;
 #pragma unroll
     for (int j = 0; j < IPT; ++j) {
       const unsigned long long be = __ballot(k > 0 && key[j] == kstar);
-      const bool eq = (be >> lane) & 1ull;
-      const bool sel = k > 0 && (key[j] > kstar || (eq && run + lanes_below(be) < need));
-      w_sel += static_cast<uint32_t>(__popcll(__ballot(sel)));
+      w_sel += static_cast<uint32_t>(__popcll(__ballot(selected(j, be, run))));
       run += static_cast<uint32_t>(__popcll(be));
     }
   }
-  if (lane == 0) wred[1][w] = w_sel;
+  if (lane == 0) wcnt[1][w] = w_sel;
   __syncthreads();
   uint32_t s_run = 0;
-  for (int j = 0; j < w; ++j) s_run += wred[1][j];
+  for (int j = 0; j < w; ++j) s_run += wcnt[1][j];
   // Pass 3: write S, C, is_sens and s01 in index order.  The bound goes through an empty asm so that
   // the compiler does not keep the IPT lane masks of the load loop alive until here (they spill).
   int n_end = N;
@@ -530,8 +605,7 @@ __global__ __launch_bounds__(kPartThreads) void k_partition_reg(const float* __r
   for (int j = 0; j < IPT; ++j) {
     const int i = base + 64 * j;
     const unsigned long long be = __ballot(k > 0 && key[j] == kstar);
-    const bool eq = (be >> lane) & 1ull;
-    const bool sel = k > 0 && (key[j] > kstar || (eq && eq_run + lanes_below(be) < need));
+    const bool sel = selected(j, be, eq_run);
     const unsigned long long bs = __ballot(sel);
     const uint32_t s_pos = s_run + lanes_below(bs);
     if (i < n_end) {
@@ -539,7 +613,7 @@ __global__ __launch_bounds__(kPartThreads) void k_partition_reg(const float* __r
       else C[static_cast<uint32_t>(i) - s_pos] = i;
       is_sens[i] = sel ? 1 : 0;
       if (s01 != nullptr) {
-        const float a = key_value(key[j]);
+        const float a = key_value(key[j] + kmin);
         float v;
         if (a != a || all_nan) v = NAN;
         else if (hi > lo) v = (a - lo) / (hi - lo);
