@@ -11,10 +11,10 @@
 //    instruction makes output register r of lane half g hold feature 16 g + r, i.e. every lane ends with
 //    16 consecutive features of one token: the epilogue (bias, GELU, bf16 pack) runs in registers and
 //    stores 32 contiguous bytes per lane, wherever the token's row lives;
-//  * wide products (D -> F, QKV): 256 features x 256 tokens per 8-wave workgroup (one per CU, two waves per
-//    SIMD), each wave 128 x 64 (4 x 2 blocks of 32 x 32): 128 flop per byte loaded, 6 KB of LDS reads per
-//    8 matrix instructions; narrow products (F -> D): 128 x 128 per 4-wave workgroup (enough workgroups to
-//    fill the GPU); K streams through double-buffered LDS (two distinct objects per operand) filled by
+//  * wide products (D -> F, QKV): 256 (or 192) features x 256 tokens per 8-wave workgroup (one per CU, two
+//    waves per SIMD), each wave 128 x 64 (4 x 2 blocks of 32 x 32): 128 flop per byte loaded, 6 KB of LDS
+//    reads per 8 matrix instructions; 192 where 256-feature tiles would leave many CUs idle; narrow
+//    products (F -> D): 128 x 128 per 4-wave workgroup (enough workgroups to fill the GPU); K streams through double-buffered LDS (two distinct objects per operand) filled by
 //    direct global -> LDS copies, which are pinned ahead of the stage's matrix work, in stages of 64 on the
 //    wide products and of 128 on the narrow ones (one 4-wave workgroup per CU with 128 KB of LDS: twice the
 //    matrix work per barrier, enough to cover the next stage's copy); within a stage the operands of K step
@@ -252,18 +252,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
       store16<OUT, GELU>(a, t0 + wt * 64 + tb * 32 + qi, j0 + wj * 64 + jb * 32 + 16 * g, acc[jb][tb]);
 }
 
-// 256 features x 256 tokens per 8-wave workgroup (one per CU, two waves per SIMD): waves 2 (features) x 4
-// (tokens), each 128 x 64 (4 x 2 blocks of 32 x 32), so every 16-element K step reads 6 KB of LDS per wave
-// for 8 matrix instructions and the tile brings 128 flop per byte loaded (twice the 128 x 128 tile); K in
-// stages of 64 through two 64 KB LDS buffers; one stage is about 2k cycles of matrix work per SIMD, long
-// enough to cover the copy of the next.
-template <int IN, int OUT, bool GELU>
+// JB features (256 or 192) x 256 tokens per 8-wave workgroup (one per CU, two waves per SIMD): waves 2
+// (features) x 4 (tokens), each JB / 2 x 64 (JB / 64 x 2 blocks of 32 x 32), so at JB = 256 every 16-element
+// K step reads 6 KB of LDS per wave for 8 matrix instructions and the tile brings 128 flop per byte loaded
+// (twice the 128 x 128 tile); K in stages of 64 through two LDS buffers per operand; one stage is about 2k
+// cycles of matrix work per SIMD.  JB = 192 serves products whose 256-feature tiles would leave a large
+// part of the GPU idle (QKV at the 1024^2 shapes: 180 tiles of 256 on 256 CUs, 240 of 192).
+template <int IN, int OUT, bool GELU, int JB = 256>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k_rows_gemm_big(RowsGemmArgs a) {
-  constexpr int kJB = 256, kTB = 256, kElems = 256 * kKs;
-  __shared__ __attribute__((aligned(16))) uint16_t w_a[kElems];
-  __shared__ __attribute__((aligned(16))) uint16_t w_b[kElems];
-  __shared__ __attribute__((aligned(16))) uint16_t x_a[kElems];
-  __shared__ __attribute__((aligned(16))) uint16_t x_b[kElems];
+  static_assert(JB == 256 || JB == 192, "feature tile");
+  constexpr int kJB = JB, kTB = 256, kWElems = JB * kKs, kXElems = 256 * kKs;
+  constexpr int kJW = JB / 64;  // 32-feature blocks per wave
+  __shared__ __attribute__((aligned(16))) uint16_t w_a[kWElems];
+  __shared__ __attribute__((aligned(16))) uint16_t w_b[kWElems];
+  __shared__ __attribute__((aligned(16))) uint16_t x_a[kXElems];
+  __shared__ __attribute__((aligned(16))) uint16_t x_b[kXElems];
 
   const int T = a.B * a.k;
   const int nt = (T + kTB - 1) / kTB;
@@ -279,14 +282,20 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k
   const int g = lane >> 5;
   const int kperm = 16 * ((qi >> 2) & 1) + 4 * (qi >> 3) + (qi & 3);
 
-  // copy sources: slot p = u * 512 + threadIdx.x of a 256-row tile holds row p / 8, chunk (p % 8) ^ swizzle(row)
-  const uint16_t* wsrc[4];
+  // copy sources: slot p = u * 512 + threadIdx.x of a tile holds row p / 8, chunk (p % 8) ^ swizzle(row);
+  // JB / 64 slots per thread for the weight tile, 4 for the token tile
+  const uint16_t* wsrc[kJW];
   const uint16_t* xsrc[4];
+#pragma unroll
+  for (int u = 0; u < kJW; ++u) {
+    const int p = u * 512 + static_cast<int>(threadIdx.x);
+    const int row = p >> 3;
+    wsrc[u] = a.w + static_cast<size_t>(j0 + row) * a.Din + ((p & 7) ^ gswz_w(row)) * 8;
+  }
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int p = u * 512 + static_cast<int>(threadIdx.x);
     const int row = p >> 3;
-    wsrc[u] = a.w + static_cast<size_t>(j0 + row) * a.Din + ((p & 7) ^ gswz_w(row)) * 8;
     const int c = (p & 7) ^ gswz_x(row);
     const int t = min(t0 + row, T - 1);
     size_t xr;
@@ -304,26 +313,28 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int base = u * 512 + wave * 64;
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(wsrc[u] + k0),
-                                       (__attribute__((address_space(3))) void*)(wl + base * 8), 16, 0, 0);
+      if (u < kJW)
+        __builtin_amdgcn_global_load_lds(static_cast<const void*>(wsrc[u < kJW ? u : 0] + k0),
+                                         (__attribute__((address_space(3))) void*)(wl + base * 8), 16, 0, 0);
       __builtin_amdgcn_global_load_lds(static_cast<const void*>(xsrc[u] + k0),
                                        (__attribute__((address_space(3))) void*)(xl + base * 8), 16, 0, 0);
     }
   };
 
-  f32x16 acc[4][2];
+  f32x16 acc[kJW][2];
 #pragma unroll
-  for (int jb = 0; jb < 4; ++jb)
+  for (int jb = 0; jb < kJW; ++jb)
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[jb][tb][i] = 0.f;
 
   auto compute = [&](const uint16_t* wl, const uint16_t* xl) {
-    bf16x8 wa[2][4], xb[2][2];
+    bf16x8 wa[2][kJW], xb[2][2];
     auto ld = [&](int ks, int slot) {
 #pragma unroll
-      for (int jb = 0; jb < 4; ++jb) wa[slot][jb] = *reinterpret_cast<const bf16x8*>(wl + goff_w(wj * 128 + jb * 32 + kperm, 2 * ks + g));
+      for (int jb = 0; jb < kJW; ++jb)
+        wa[slot][jb] = *reinterpret_cast<const bf16x8*>(wl + goff_w(wj * (JB / 2) + jb * 32 + kperm, 2 * ks + g));
 #pragma unroll
       for (int tb = 0; tb < 2; ++tb) xb[slot][tb] = *reinterpret_cast<const bf16x8*>(xl + goff_x(wt * 64 + tb * 32 + qi, 2 * ks + g));
     };
@@ -333,7 +344,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k
       if (ks + 1 < kKs / 16) ld(ks + 1, (ks + 1) & 1);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int jb = 0; jb < 4; ++jb)
+      for (int jb = 0; jb < kJW; ++jb)
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
           acc[jb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa[ks & 1][jb], xb[ks & 1][tb], acc[jb][tb], 0, 0, 0);
@@ -363,17 +374,29 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k
 #pragma unroll
   for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-    for (int jb = 0; jb < 4; ++jb)
-      store16<OUT, GELU>(a, t0 + wt * 64 + tb * 32 + qi, j0 + wj * 128 + jb * 32 + 16 * g, acc[jb][tb]);
+    for (int jb = 0; jb < kJW; ++jb)
+      store16<OUT, GELU>(a, t0 + wt * 64 + tb * 32 + qi, j0 + wj * (JB / 2) + jb * 32 + 16 * g, acc[jb][tb]);
 }
 
 template <int IN, int OUT, bool GELU>
 static hipError_t launch_gemm(const RowsGemmArgs& a, hipStream_t s) {
   const int T = a.B * a.k;
-  if (a.Dout % 256 == 0 && a.Dout >= 2048) {
-    // wide products (the FFN's D -> F, QKV): 256 x 256 tiles still give at least 8 tiles across features
-    const uint32_t grid = static_cast<uint32_t>((T + 255) / 256) * static_cast<uint32_t>(a.Dout / 256);
-    k_rows_gemm_big<IN, OUT, GELU><<<grid, 512, 0, s>>>(a);
+  if (a.Dout >= 2048 && (a.Dout % 256 == 0 || a.Dout % 192 == 0)) {
+    // wide products (the FFN's D -> F, QKV): 256 or 192 features x 256 tokens, whichever finishes its
+    // rounds of one workgroup per CU sooner (a workgroup's time taken as its feature count, 5% more per
+    // feature at 192 for the smaller flop per byte): QKV at the 1024^2 shapes takes 192 (one round of 240
+    // tiles against one of 180), the FFN's D -> F 256 (240 tiles against two rounds of 320)
+    const int tt = (T + 255) / 256;
+    auto cost = [&](int jb) {
+      if (a.Dout % jb != 0) return 1e30;
+      const int rounds = (tt * (a.Dout / jb) + 255) / 256;
+      return static_cast<double>(rounds) * jb * (jb == 192 ? 1.05 : 1.0);
+    };
+    if (cost(192) < cost(256)) {
+      k_rows_gemm_big<IN, OUT, GELU, 192><<<static_cast<uint32_t>(tt * (a.Dout / 192)), 512, 0, s>>>(a);
+    } else {
+      k_rows_gemm_big<IN, OUT, GELU, 256><<<static_cast<uint32_t>(tt * (a.Dout / 256)), 512, 0, s>>>(a);
+    }
     return hipGetLastError();
   }
   const uint32_t grid = static_cast<uint32_t>((T + kTT - 1) / kTT) * static_cast<uint32_t>(a.Dout / kJT);
