@@ -371,6 +371,7 @@ def main():
     result["attention_d128_1024"] = attention_large(dts, torch, syn, dev, syn.WORKLOADS["dense_1024_d128"], stream,
                                                     reps=10)[-1]
     result["attention_fp8_1024"] = attention_fp8(dts, torch, syn, dev, syn.WORKLOADS["srsu_1024"])
+    result["attention_fp8_d128_1024"] = attention_fp8(dts, torch, syn, dev, syn.WORKLOADS["dense_1024_d128"])
     if not args.no_large:
         result["attention_fp8_2560"] = attention_fp8(dts, torch, syn, dev, syn.WORKLOADS["srsu_2560"], reps=3)
     result["aesmask_stepcache"] = next_rows(dts, torch, np, syn, dev, hbm, not args.no_large)

@@ -44,8 +44,8 @@ safe_status check_attn(const safe_attn_desc* d) {
     if (d->mask_dtype == SAFE_DTYPE_F32 && (reinterpret_cast<uintptr_t>(d->mask) & 3u) != 0) return SAFE_ERR_ALIGN;
   }
   if (d->dtype == SAFE_DTYPE_FP8_E4M3) {
-    // fp8 Q / K: the mask-free fast path at head dim 64 only
-    if (d->d != 64 || d->mask != nullptr || d->lse != nullptr || d->xattn_out != nullptr || d->lse_img_out != nullptr)
+    // fp8 Q / K: the mask-free fast path (head dim 64 or 128)
+    if ((d->d != 64 && d->d != 128) || d->mask != nullptr || d->lse != nullptr || d->xattn_out != nullptr || d->lse_img_out != nullptr)
       return SAFE_ERR_UNSUPPORTED;
     if ((reinterpret_cast<uintptr_t>(d->q_descale) & 3u) != 0 || (reinterpret_cast<uintptr_t>(d->k_descale) & 3u) != 0)
       return SAFE_ERR_ALIGN;
@@ -96,7 +96,7 @@ bool mfma_takes_mask(const safe_attn_desc* d) {
 safe_status run_attn(const safe_attn_desc* d, const int32_t* rows, int R, hipStream_t s) {
   const AttnArgs a = make_args(d, rows, R);
   if (R == 0) return SAFE_OK;
-  if (d->dtype == SAFE_DTYPE_FP8_E4M3) return from_hip(launch_attn_mfma_fp8(a, s));
+  if (d->dtype == SAFE_DTYPE_FP8_E4M3) return from_hip(launch_attn_mfma_fp8(a, d->d, s));
   if (d->dtype == SAFE_DTYPE_BF16 && (d->mask == nullptr || mfma_takes_mask(d)))
     return from_hip(launch_attn_mfma_bf16(a, d->d, s));
   return from_hip(launch_attn_generic(a, d->dtype, d->d, s));

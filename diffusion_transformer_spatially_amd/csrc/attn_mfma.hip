@@ -134,14 +134,25 @@ __device__ __forceinline__ void stage_issue(const TileSrc& s, uint16_t* kl, uint
   const int lane = threadIdx.x & 63;
   int wslot = __builtin_amdgcn_readfirstlane(static_cast<int>((threadIdx.x >> 6) & 3)) * 64;
   if (OPAQUE) asm volatile("" : "+s"(wslot));
-  if constexpr (FP8) {
-    static_assert(D == 64, "fp8 K tiles at head dim 64");
+  if constexpr (FP8 && D == 64) {
     const int p = wslot + lane;  // one 16-byte slot per thread: 64 rows x 4 chunks
     const int row = p >> 2;
     const int c = (p & 3) ^ swz8(row);
     const int srow = row < s.nvalid ? row : s.nvalid - 1;
     __builtin_amdgcn_global_load_lds(static_cast<const void*>(s.k8() + srow * 64 + c * 16),
                                      (__attribute__((address_space(3))) void*)(kl + wslot * 8), 16, 0, 0);
+  } else if constexpr (FP8) {
+    // head dim 128: 128-byte rows, laid out as the bf16 head-dim-64 K tile (8 chunks, swz<64>)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int base = u * kWaves * 64 + wslot;
+      const int p = base + lane;
+      const int row = p >> 3;
+      const int c = (p & 7) ^ swz<64>(row);
+      const int srow = row < s.nvalid ? row : s.nvalid - 1;
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(s.k8() + srow * 128 + c * 16),
+                                       (__attribute__((address_space(3))) void*)(kl + base * 8), 16, 0, 0);
+    }
   }
 #pragma unroll
   for (int u = 0; u < kBN * kChunks / (kWaves * 64); ++u) {
@@ -175,23 +186,33 @@ __device__ __forceinline__ void stage_offsets(uint32_t (&off)[D / 32]) {
   }
 }
 
-// koff8: the fp8 K copy's per-lane byte offset within a full tile (FP8 only).
-__device__ __forceinline__ uint32_t stage8_offset() {
-  const int p = static_cast<int>(threadIdx.x & 255);
-  const int row = p >> 2;
-  return static_cast<uint32_t>(row * 64 + (((p & 3) ^ swz8(row)) << 4));
+// koff8: the fp8 K copy's per-lane byte offsets within a full tile (FP8 only), one per copy instruction:
+// head dim 64 one (64-byte rows), head dim 128 two (128-byte rows: the offsets of the bf16 head-dim-64 K copy).
+template <int D>
+__device__ __forceinline__ void stage8_offsets(uint32_t (&off)[D / 64]) {
+  if constexpr (D == 64) {
+    const int p = static_cast<int>(threadIdx.x & 255);
+    const int row = p >> 2;
+    off[0] = static_cast<uint32_t>(row * 64 + (((p & 3) ^ swz8(row)) << 4));
+  } else {
+    stage_offsets<64>(off);
+  }
 }
 
 template <int D, bool OPAQUE, bool FP8 = false>
 __device__ __forceinline__ void stage_issue_full(const TileSrc& s, uint16_t* kl, uint16_t* vl, const uint32_t (&off)[D / 32],
-                                                 uint32_t koff8 = 0) {
+                                                 const uint32_t (&koff8)[D / 64]) {
   int wslot = __builtin_amdgcn_readfirstlane(static_cast<int>((threadIdx.x >> 6) & 3)) * 64;
   if (OPAQUE) asm volatile("" : "+s"(wslot));
   const char* kb = reinterpret_cast<const char*>(s.k);
   const char* vb = reinterpret_cast<const char*>(s.v);
-  if constexpr (FP8)
-    __builtin_amdgcn_global_load_lds(static_cast<const void*>(kb + koff8),
-                                     (__attribute__((address_space(3))) void*)(kl + wslot * 8), 16, 0, 0);
+  if constexpr (FP8) {
+#pragma unroll
+    for (int u = 0; u < D / 64; ++u)
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(kb + koff8[u]),
+                                       (__attribute__((address_space(3))) void*)(kl + (u * kWaves * 64 + wslot) * 8), 16, 0,
+                                       0);
+  }
 #pragma unroll
   for (int u = 0; u < D / 32; ++u) {
     const int base = u * kWaves * 64 + wslot;
@@ -215,11 +236,32 @@ __device__ __forceinline__ f32x16 mfma_fp8(bf16x8 a0, bf16x8 a1, bf16x8 b0, bf16
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c, 0, 0, 0, 127, 0, 127);
 }
 
-// A lane's fp8 K operand of key row `key` (chunks 2g and 2g + 1).
-__device__ __forceinline__ void read_k8(bf16x8 (&ka)[2], const uint16_t* kl, int key, int g) {
-  const uint8_t* kb = reinterpret_cast<const uint8_t*>(kl);
-  ka[0] = *reinterpret_cast<const bf16x8*>(kb + lds8_off(key, 2 * g));
-  ka[1] = *reinterpret_cast<const bf16x8*>(kb + lds8_off(key, 2 * g + 1));
+// A lane's fp8 K operand of key row `key` for bytes 64j .. 64j + 63 of the row: chunks 4j + 2g and 4j + 2g + 1
+// (head dim 64: 64-byte rows; head dim 128: 128-byte rows in the layout of the bf16 head-dim-64 tile).
+template <int D = 64>
+__device__ __forceinline__ void read_k8(bf16x8 (&ka)[2], const uint16_t* kl, int key, int g, int j = 0) {
+  if constexpr (D == 64) {
+    const uint8_t* kb = reinterpret_cast<const uint8_t*>(kl);
+    ka[0] = *reinterpret_cast<const bf16x8*>(kb + lds8_off(key, 2 * g));
+    ka[1] = *reinterpret_cast<const bf16x8*>(kb + lds8_off(key, 2 * g + 1));
+  } else {
+    ka[0] = *reinterpret_cast<const bf16x8*>(kl + lds_off<64>(key, 4 * j + 2 * g));
+    ka[1] = *reinterpret_cast<const bf16x8*>(kl + lds_off<64>(key, 4 * j + 2 * g + 1));
+  }
+}
+
+// fp8 S^T block of 32 keys (rows kb*32 + kperm of the tile) x the wave's 32 queries over the whole head dim:
+// one fp8 instruction per 64 bytes of the rows; the Q operand holds bytes 64j + 32g .. +31 in q[2j], q[2j+1].
+template <int D>
+__device__ __forceinline__ f32x16 logits_fp8(const uint16_t* kl, int key, int g, const bf16x8 (&q)[D / 16]) {
+  f32x16 s = {};
+#pragma unroll
+  for (int j = 0; j < D / 64; ++j) {
+    bf16x8 ka[2];
+    read_k8<D>(ka, kl, key, g, j);
+    s = mfma_fp8(ka[0], ka[1], q[2 * j], q[2 * j + 1], s);
+  }
+  return s;
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
@@ -659,7 +701,7 @@ __device__ __forceinline__ void tile_step_fast(WaveState<QB, D>& st, const uint1
   constexpr bool kPre = D == 64 && !FP8;
   static_assert(KM == 0 || QB == 1, "a kept mask runs with one query block per wave");
   static_assert(QB == 1 || D == 64, "two query blocks per wave only at head dim 64");
-  static_assert(!FP8 || (D == 64 && KM == 0), "fp8 Q / K at head dim 64 without a mask");
+  static_assert(!FP8 || KM == 0, "fp8 Q / K without a mask");
   if constexpr (QB == 2) {
     if constexpr (FP8) tile_step_fast2_fp8<MASKED>(st, kl, vl, kperm, g, li, dc0, c2, nvalid);
     else tile_step_fast2<MASKED>(st, kl, vl, kperm, g, li, dc0, nvalid);
@@ -681,10 +723,8 @@ __device__ __forceinline__ void tile_step_fast(WaveState<QB, D>& st, const uint1
   for (int kb = 0; kb < 2; ++kb) {
     const int key = kb * 32 + kperm;
     if constexpr (FP8) {
-      bf16x8 ka[2];
-      read_k8(ka, kl, key, g);
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) s[qb][kb] = mfma_fp8(ka[0], ka[1], st.q[qb][0], st.q[qb][1], (f32x16){});
+      for (int qb = 0; qb < QB; ++qb) s[qb][kb] = logits_fp8<D>(kl, key, g, st.q[qb]);
     } else {
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
@@ -745,9 +785,7 @@ __device__ __forceinline__ void tile_step_fast(WaveState<QB, D>& st, const uint1
       for (int kb = 0; kb < 2; ++kb) {
         const int key = kb * 32 + kperm;
         if constexpr (FP8) {
-          bf16x8 ka[2];
-          read_k8(ka, kl, key, g);
-          sx[kb] = mfma_fp8(ka[0], ka[1], st.q[qb][0], st.q[qb][1], (f32x16){});
+          sx[kb] = logits_fp8<D>(kl, key, g, st.q[qb]);
         } else {
 #pragma unroll
           for (int ks = 0; ks < D / 16; ++ks) {
@@ -1035,7 +1073,7 @@ template <bool GATHER, int QB, bool EXACT_SUM, int KM, int KS, int D, bool FP8 =
 __global__ __launch_bounds__(kThreads * KS) __attribute__((amdgpu_waves_per_eu(2))) void k_attn_mfma(AttnArgs a) {
   static_assert(KS == 1 || (KS == 2 && !EXACT_SUM && KM == 0), "key halves only on the mask-free fast path");
   static_assert(D == 64 || D == 128, "head dim 64 or 128");
-  static_assert(!FP8 || (D == 64 && !EXACT_SUM && KM == 0), "fp8 Q / K: head dim 64, mask-free fast path");
+  static_assert(!FP8 || (!EXACT_SUM && KM == 0 && (D == 64 || QB == 1)), "fp8 Q / K: mask-free fast path");
   constexpr size_t kRowK = FP8 ? D : 2 * D;  // bytes per K row
   constexpr int kRowsW = 32 * QB;
   constexpr int kBM = kWaves * kRowsW;
@@ -1096,10 +1134,14 @@ __global__ __launch_bounds__(kThreads * KS) __attribute__((amdgpu_waves_per_eu(2
     valid[qb] = active && rr >= 0 && rr < a.N;
     row[qb] = valid[qb] ? rr : 0;
     if constexpr (FP8) {
-      // the fp8 Q operand: bytes 32g .. 32g + 31 of the row (the other two entries of st.q stay unused)
+      // the fp8 Q operand: bytes 64j + 32g .. 64j + 32g + 31 of the row in q[2j], q[2j + 1] (the other
+      // entries of st.q stay unused)
       const uint8_t* qp8 = static_cast<const uint8_t*>(a.q) + (bh * a.N + row[qb]) * D + 32 * g;
-      st.q[qb][0] = *reinterpret_cast<const bf16x8*>(qp8);
-      st.q[qb][1] = *reinterpret_cast<const bf16x8*>(qp8 + 16);
+#pragma unroll
+      for (int j = 0; j < D / 64; ++j) {
+        st.q[qb][2 * j] = *reinterpret_cast<const bf16x8*>(qp8 + 64 * j);
+        st.q[qb][2 * j + 1] = *reinterpret_cast<const bf16x8*>(qp8 + 64 * j + 16);
+      }
     } else {
       const bf16x8* qp =
           reinterpret_cast<const bf16x8*>(static_cast<const uint16_t*>(a.q) + (bh * a.N + row[qb]) * D);
@@ -1200,7 +1242,8 @@ __global__ __launch_bounds__(kThreads * KS) __attribute__((amdgpu_waves_per_eu(2
   // prefetch and synchronise.
   uint32_t coff[D / 32];
   stage_offsets<D>(coff);
-  const uint32_t koff8 = FP8 ? stage8_offset() : 0u;
+  uint32_t koff8[D / 64] = {};
+  if constexpr (FP8) stage8_offsets<D>(koff8);
   // this (b,h)'s image K / V bases, opaque so that they stay in scalar registers instead of being reloaded
   // from the kernel arguments (a scalar load and its wait) every tile
   const uint16_t* kimg = reinterpret_cast<const uint16_t*>(static_cast<const uint8_t*>(a.k_img) + bh * a.N * kRowK);
@@ -1390,12 +1433,25 @@ static void launch_rows64_fp8(const AttnArgs& a, hipStream_t s) {
   else launch<GATHER, 1, false, 0, 64, 2, true>(a, s);
 }
 
-hipError_t launch_attn_mfma_fp8(const AttnArgs& a, hipStream_t s) {
+// fp8 Q / K at head dim 128: the mask-free work shapes of the bf16 head-dim-128 path.
+template <bool GATHER>
+static void launch_rows128_fp8(const AttnArgs& a, hipStream_t s) {
+  const double waves_qb1 = static_cast<double>(a.B) * a.H * ((a.R + 31) / 32);
+  if (waves_qb1 >= 2048.0) launch<GATHER, 1, false, 0, 128, 1, true>(a, s);
+  else launch<GATHER, 1, false, 0, 128, 2, true>(a, s);
+}
+
+hipError_t launch_attn_mfma_fp8(const AttnArgs& a, int d, hipStream_t s) {
   if (a.R == 0) return hipSuccess;
   if (a.mask != nullptr || a.lse != nullptr || a.xattn_out != nullptr || a.lse_img_out != nullptr)
     return hipErrorInvalidValue;
-  if (a.rows != nullptr) launch_rows64_fp8<true>(a, s);
-  else launch_rows64_fp8<false>(a, s);
+  if (d == 128) {
+    if (a.rows != nullptr) launch_rows128_fp8<true>(a, s);
+    else launch_rows128_fp8<false>(a, s);
+  } else {
+    if (a.rows != nullptr) launch_rows64_fp8<true>(a, s);
+    else launch_rows64_fp8<false>(a, s);
+  }
   return hipGetLastError();
 }
 

@@ -1,5 +1,5 @@
 """GPU parity of the fp8 attention path (FP8 E4M3 Q and K with per-(b,h) factors, bf16 V and output; head dim
-64, mask-free fast path) against the fp64 oracle on the dequantised inputs."""
+64 and 128, mask-free fast path) against the fp64 oracle on the dequantised inputs."""
 import numpy as np
 import pytest
 
@@ -43,6 +43,10 @@ def _oracle(w, inp, rows=None):
 
 def _w(**kw):
     return syn.scaled(syn.WORKLOADS["dense_1024"], side=1, **kw)
+
+
+def _w128(**kw):
+    return syn.scaled(syn.WORKLOADS["dense_1024"], side=1, d=128, **kw)
 
 
 SHAPES = [(1, 1, 1, 0, (0,)), (1, 2, 64, 64, (64,)), (2, 3, 65, 40, (17, 0)), (2, 2, 127, 256, (77, 1)),
@@ -165,6 +169,84 @@ def test_fp8_unsupported_requests_are_rejected(lib):
         assert e.value.code == 6
     q2 = t.zeros((1, 1, 64, 128), dtype=t.float8_e4m3fn, device="cuda")
     v2 = t.zeros((1, 1, 64, 128), dtype=t.bfloat16, device="cuda")
-    with pytest.raises(lib.SafeAttnError) as e:
-        lib.safe_attn_dense(q2, q2, v2, None, None, (0,), v2.clone())
+    with pytest.raises(lib.SafeAttnError) as e:  # head dim 128 takes fp8, but not with an lse
+        lib.safe_attn_dense(q2, q2, v2, None, None, (0,), v2.clone(), lse=lse)
     assert e.value.code == 6
+
+
+# ---- head dim 128: two fp8 instructions per 32-key half, one query block per wave
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "B%dH%dN%dT%d" % s[:4])
+def test_fp8_d128_dense_parity(lib, shape):
+    B, H, N, T, tv = shape
+    w = _w128(B=B, H=H, N=N, T=T, tv=tv)
+    inp = syn.attention_inputs_fp8(w)
+    assert_close(_run(lib, w, inp), _oracle(w, inp), "bf16", f"fp8 d128 dense {shape}")
+
+
+@pytest.mark.parametrize("k", [0, 1, 63, 65, 300])
+def test_fp8_d128_rows_parity_and_untouched_context(lib, k):
+    w = _w128(B=2, H=3, N=300, T=256, tv=(77, 5))
+    inp = syn.attention_inputs_fp8(w)
+    rows = syn.random_rows(w, k=k)
+    state = syn.initial_state(w)
+    o = _run(lib, w, inp, rows=rows, state=state)
+    C = np.setdiff1d(np.arange(w.N), rows)
+    assert np.array_equal(o[:, :, C], state[:, :, C].astype(np.float64))
+    if k:
+        assert_close(o[:, :, rows], _oracle(w, inp, rows), "bf16", f"fp8 d128 rows k={k}")
+    if k == w.N:
+        assert np.array_equal(o, _run(lib, w, inp))
+
+
+@pytest.mark.parametrize("B,H,N,T,tv,k", [
+    (1, 8, 2000, 256, (77,), None),         # 504 one-block waves: key halves
+    (2, 8, 4160, 256, (77, 0), None),       # 2080 one-block waves: no split
+    (2, 24, 4096, 256, (77, 77), 1229),     # the 1024^2 rows launch (1872 waves): halves, gathered rows
+    (1, 3, 130, 0, (0,), None),             # 3 key tiles: halves of 2 and 1
+    (1, 3, 40, 0, (0,), None),              # 1 key tile: the second half has none
+])
+def test_fp8_d128_work_shapes(lib, B, H, N, T, tv, k):
+    w = _w128(B=B, H=H, N=N, T=T, tv=tv, k=k or 1)
+    inp = syn.attention_inputs_fp8(w)
+    if k is None:
+        assert_close(_run(lib, w, inp), _oracle(w, inp), "bf16", f"fp8 d128 dense B{B}H{H}N{N}")
+    else:
+        rows = syn.random_rows(w, k=k)
+        state = syn.initial_state(w)
+        o = _run(lib, w, inp, rows=rows, state=state)
+        pick = rows[syn.sample_rows(len(rows), 96, seed=1)]
+        assert_close(o[:, :, pick], _oracle(w, inp, pick), "bf16", "fp8 d128 rows 1024^2 shape")
+        C = np.setdiff1d(np.arange(w.N), rows)
+        assert np.array_equal(o[:, :, C], state[:, :, C].astype(np.float64))
+
+
+def test_fp8_d128_closed_forms_and_stress(lib):
+    w = _w128(B=2, H=2, N=257, T=256, tv=(77, 0))
+    inp = syn.attention_inputs_fp8(w)
+    ones = dict(inp, v_img_bits=np.full_like(inp["v_img_bits"], 0x3F80), v_txt_bits=np.full_like(inp["v_txt_bits"], 0x3F80))
+    assert np.max(np.abs(_run(lib, w, ones) - 1.0)) <= 1e-6
+    zq = dict(inp, q_fp8=np.zeros_like(inp["q_fp8"]), q=np.zeros_like(inp["q"]))
+    o = _run(lib, w, zq)
+    for b in range(2):
+        vals = np.concatenate([inp["v_img"][b], inp["v_txt"][b, :, : w.tv[b]]], axis=1).astype(np.float64)
+        assert_close(o[b], np.broadcast_to(vals.mean(axis=1)[:, None, :], o[b].shape), "bf16", "fp8 d128 Q = 0")
+    # sharper rows (logit std near 9 at head dim 128): the lazy-max rescaling on fp8 logits
+    w = _w128(B=1, H=2, N=513, T=256, tv=(100,), std=3.0)
+    inp = dict(syn.attention_inputs_fp8(w))
+    for r in ("v_img", "v_txt"):
+        v = (inp[r] * np.float32(0.125 / 3.0)).astype(np.float32)
+        inp[r], inp[r + "_bits"] = syn.round_to_bf16(v), syn.f32_to_bf16_bits(v)
+    assert_close(_run(lib, w, inp), _oracle(w, inp), "bf16", "fp8 d128 std=3")
+
+
+def test_fp8_d128_full_size_sampled(lib):
+    """The 1024^2 shapes at head dim 128 (dense and |S| = 1229 rows), on sampled rows."""
+    w = syn.WORKLOADS["dense_1024_d128"]
+    inp = syn.attention_inputs_fp8(w)
+    sample = syn.sample_rows(w.N, 24, seed=w.seed)
+    o = _run(lib, w, inp)
+    assert_close(o[:, :, sample], _oracle(w, inp, sample), "bf16", "fp8 d128 dense 1024^2")
+    rows = syn.random_rows(w)
+    o = _run(lib, w, inp, rows=rows, state=np.zeros((w.B, w.H, w.N, w.d), np.float32))
+    pick = rows[syn.sample_rows(len(rows), 24, seed=w.seed)]
+    assert_close(o[:, :, pick], _oracle(w, inp, pick), "bf16", "fp8 d128 rows 1024^2")
