@@ -49,6 +49,8 @@ def parse():
     ap.add_argument("--hbm-only", action="store_true",
                     help="run only the HBM-bound stages (batched / cold / cache-resident) and print them; for "
                          "profiling those launches")
+    ap.add_argument("--block-only", action="store_true",
+                    help="run only the sensitive-row block products (FFN, QKV) and print them; for profiling them")
     return ap.parse_args()
 
 
@@ -72,6 +74,12 @@ def main():
         gbs_ = lambda b, ms: b / (ms * 1e-3) / 1e9
         hbm_ = lambda b, ms: {"ms": ms, "gbs": gbs_(b, ms), "frac_hbm": gbs_(b, ms) / HBM_PEAK_GBS, "bytes": b}
         out = {"hbm": hbm_stages(dts, torch, np, syn, dev, hbm_)}
+        if args.copy_calibration:
+            out["copy_calibration_bytes"] = copy_calibration(torch, dev)
+        print(json.dumps(out), flush=True)
+        return
+    if args.block_only:
+        out = {"srsu_block": srsu_block(dts, torch, np, syn, dev)}
         if args.copy_calibration:
             out["copy_calibration_bytes"] = copy_calibration(torch, dev)
         print(json.dumps(out), flush=True)
