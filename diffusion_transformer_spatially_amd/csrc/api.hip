@@ -14,6 +14,16 @@ inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 
 
 safe_status from_hip(hipError_t e) { return e == hipSuccess ? SAFE_OK : SAFE_ERR_HIP; }
 
+// A kept mask runs on the MFMA kernel when each lane's 16-entry mask chunks are aligned and never cross a
+// mask row (N and the row length multiples of 16, 16-byte aligned base), no emission is asked (the
+// emission of masked logits stays on the generic kernel) and, at head dim 128, the mask is bool (fp32
+// mask chunks do not fit in registers beside a 128-dim block's accumulators); otherwise on the generic
+// kernel.
+bool mfma_takes_mask(const safe_attn_desc* d) {
+  return d->xattn_out == nullptr && d->lse_img_out == nullptr && d->N % 16 == 0 && d->mask_cols % 16 == 0 &&
+         (reinterpret_cast<uintptr_t>(d->mask) & 15u) == 0 && (d->d == 64 || d->mask_dtype == SAFE_DTYPE_BOOL);
+}
+
 safe_status check_attn(const safe_attn_desc* d) {
   if (d == nullptr) return SAFE_ERR_NULL;
   if (d->dtype != SAFE_DTYPE_BF16 && d->dtype != SAFE_DTYPE_F32 && d->dtype != SAFE_DTYPE_FP8_E4M3)
@@ -44,9 +54,8 @@ safe_status check_attn(const safe_attn_desc* d) {
     if (d->mask_dtype == SAFE_DTYPE_F32 && (reinterpret_cast<uintptr_t>(d->mask) & 3u) != 0) return SAFE_ERR_ALIGN;
   }
   if (d->dtype == SAFE_DTYPE_FP8_E4M3) {
-    // fp8 Q / K: the mask-free fast path (head dim 64 or 128)
-    if ((d->d != 64 && d->d != 128) || d->mask != nullptr || d->lse != nullptr || d->xattn_out != nullptr || d->lse_img_out != nullptr)
-      return SAFE_ERR_UNSUPPORTED;
+    // fp8 Q / K run on the MFMA kernel only: a kept mask must be one it takes (see mfma_takes_mask)
+    if ((d->d != 64 && d->d != 128) || (d->mask != nullptr && !mfma_takes_mask(d))) return SAFE_ERR_UNSUPPORTED;
     if ((reinterpret_cast<uintptr_t>(d->q_descale) & 3u) != 0 || (reinterpret_cast<uintptr_t>(d->k_descale) & 3u) != 0)
       return SAFE_ERR_ALIGN;
   }
@@ -81,16 +90,6 @@ AttnArgs make_args(const safe_attn_desc* d, const int32_t* rows, int R) {
   a.scale = d->scale == 0.f ? 1.0f / std::sqrt(static_cast<float>(d->d)) : d->scale;
   for (int b = 0; b < d->B; ++b) a.tv[b] = d->text_valid_len[b];
   return a;
-}
-
-// A kept mask runs on the MFMA kernel when each lane's 16-entry mask chunks are aligned and never cross a
-// mask row (N and the row length multiples of 16, 16-byte aligned base), no emission is asked (the
-// emission of masked logits stays on the generic kernel) and, at head dim 128, the mask is bool (fp32
-// mask chunks do not fit in registers beside a 128-dim block's accumulators); otherwise on the generic
-// kernel.
-bool mfma_takes_mask(const safe_attn_desc* d) {
-  return d->xattn_out == nullptr && d->lse_img_out == nullptr && d->N % 16 == 0 && d->mask_cols % 16 == 0 &&
-         (reinterpret_cast<uintptr_t>(d->mask) & 15u) == 0 && (d->d == 64 || d->mask_dtype == SAFE_DTYPE_BOOL);
 }
 
 safe_status run_attn(const safe_attn_desc* d, const int32_t* rows, int R, hipStream_t s) {

@@ -701,7 +701,6 @@ __device__ __forceinline__ void tile_step_fast(WaveState<QB, D>& st, const uint1
   constexpr bool kPre = D == 64 && !FP8;
   static_assert(KM == 0 || QB == 1, "a kept mask runs with one query block per wave");
   static_assert(QB == 1 || D == 64, "two query blocks per wave only at head dim 64");
-  static_assert(!FP8 || KM == 0, "fp8 Q / K without a mask");
   if constexpr (QB == 2) {
     if constexpr (FP8) tile_step_fast2_fp8<MASKED>(st, kl, vl, kperm, g, li, dc0, c2, nvalid);
     else tile_step_fast2<MASKED>(st, kl, vl, kperm, g, li, dc0, nvalid);
@@ -880,18 +879,24 @@ template <int QB, bool MASKED, bool EXACT_SUM, int KM, int D, bool FP8 = false>
 __device__ __forceinline__ void tile_step(WaveState<QB, D>& st, const uint16_t* kl, const uint16_t* vl, int kperm,
                                           int g, int li, int dc0, float c2, int nvalid, float* const (&xo)[QB],
                                           float scale, const MaskTile<KM>& mt) {
-  static_assert(!FP8 || !EXACT_SUM, "fp8 Q / K on the fast path only");
   if constexpr (!EXACT_SUM) {
     tile_step_fast<QB, MASKED, KM, D, FP8>(st, kl, vl, kperm, g, li, dc0, c2, nvalid, mt);
     return;
   }
   static_assert(KM == 0 || QB == 1, "a kept mask runs with one query block per wave");
+  // scale: the logit scale in the units of s (for fp8, times the (b,h) factors of Q and K: s holds dot products
+  // of the codes)
   const float inv_scale = 1.f / scale;
   // ---- S^T = K Q^T
   f32x16 s[QB][2];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
     const int key = kb * 32 + kperm;
+    if constexpr (FP8) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) s[qb][kb] = logits_fp8<D>(kl, key, g, st.q[qb]);
+      continue;
+    }
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
       const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kl + lds_off<D>(key, 2 * ks + g));
@@ -971,6 +976,10 @@ __device__ __forceinline__ void tile_step(WaveState<QB, D>& st, const uint16_t* 
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const int key = kb * 32 + kperm;
+        if constexpr (FP8) {
+          sx[kb] = logits_fp8<D>(kl, key, g, st.q[qb]);
+          continue;
+        }
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks) {
           const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kl + lds_off<D>(key, 2 * ks + g));
@@ -1060,12 +1069,12 @@ __device__ __forceinline__ void tile_step(WaveState<QB, D>& st, const uint16_t* 
 
 template <int QB, int D>
 __device__ __forceinline__ void store_lse_img(const AttnArgs& a, const WaveState<QB, D>& st, int h, const int (&row)[QB],
-                                              const bool (&valid)[QB], int g) {
+                                              const bool (&valid)[QB], int g, float scale) {
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const float lt = st.l[qb] + swap_halves(st.l[qb]);
     if (valid[qb] && g == 0)
-      a.lse_img_out[static_cast<size_t>(h) * a.N + row[qb]] = lt > 0.f ? st.m[qb] * a.scale + logf(lt) : -INFINITY;
+      a.lse_img_out[static_cast<size_t>(h) * a.N + row[qb]] = lt > 0.f ? st.m[qb] * scale + logf(lt) : -INFINITY;
   }
 }
 
@@ -1073,7 +1082,7 @@ template <bool GATHER, int QB, bool EXACT_SUM, int KM, int KS, int D, bool FP8 =
 __global__ __launch_bounds__(kThreads * KS) __attribute__((amdgpu_waves_per_eu(2))) void k_attn_mfma(AttnArgs a) {
   static_assert(KS == 1 || (KS == 2 && !EXACT_SUM && KM == 0), "key halves only on the mask-free fast path");
   static_assert(D == 64 || D == 128, "head dim 64 or 128");
-  static_assert(!FP8 || (!EXACT_SUM && KM == 0 && (D == 64 || QB == 1)), "fp8 Q / K: mask-free fast path");
+  static_assert(!FP8 || D == 64 || QB == 1, "fp8 Q / K: one query block per wave at head dim 128");
   constexpr size_t kRowK = FP8 ? D : 2 * D;  // bytes per K row
   constexpr int kRowsW = 32 * QB;
   constexpr int kBM = kWaves * kRowsW;
@@ -1171,11 +1180,14 @@ __global__ __launch_bounds__(kThreads * KS) __attribute__((amdgpu_waves_per_eu(2
   }
   // the warmup emission only runs on the exact-sum path (the host picks it whenever an output asks for it)
   const bool emit = EXACT_SUM && b == 0 && (a.xattn_out != nullptr || a.lse_img_out != nullptr);
-  float c2 = a.scale * kLog2e;
-  if constexpr (FP8) {  // the (b,h) dequantisation factors of the fp8 Q and K multiply every logit
-    if (a.q_descale != nullptr) c2 *= a.q_descale[bh];
-    if (a.k_descale != nullptr) c2 *= a.k_descale[bh];
+  // the logit scale in the units of the dot products: for fp8 codes, times the (b,h) dequantisation factors of
+  // Q and K (every logit, emitted logit, lse and mask conversion takes it)
+  float scale_eff = a.scale;
+  if constexpr (FP8) {
+    if (a.q_descale != nullptr) scale_eff *= a.q_descale[bh];
+    if (a.k_descale != nullptr) scale_eff *= a.k_descale[bh];
   }
+  const float c2 = scale_eff * kLog2e;
   if constexpr (!EXACT_SUM && D == 64 && !FP8) {  // the fast path's pre-scaled Q (bf16 at head dim 64 only)
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
@@ -1261,12 +1273,12 @@ __global__ __launch_bounds__(kThreads * KS) __attribute__((amdgpu_waves_per_eu(2
       }
       mask_fetch(mnext, t + 1);
     }
-    tile_step<QB, false, EXACT_SUM, KM, D, FP8>(st, ck, cv, kperm, g, li, dc0, c2, kBN, no_store, a.scale, mcur);
+    tile_step<QB, false, EXACT_SUM, KM, D, FP8>(st, ck, cv, kperm, g, li, dc0, c2, kBN, no_store, scale_eff, mcur);
     tile_barrier();
     if constexpr (KM != 0) mcur = mnext;
   };
   auto masked_tile = [&](int t, const uint16_t* ck, const uint16_t* cv, uint16_t* nk, uint16_t* nv) {
-    if (emit && t == n_img && a.lse_img_out != nullptr) store_lse_img(a, st, h, row, valid, g);
+    if (emit && t == n_img && a.lse_img_out != nullptr) store_lse_img(a, st, h, row, valid, g, scale_eff);
     if (t + 1 < t_end) {
       stage_issue<D, (QB > 1), FP8>(tile_src<D, FP8>(a, bh, t + 1, n_img, tv), nk, nv);
       mask_fetch(mnext, t + 1);
@@ -1279,7 +1291,7 @@ __global__ __launch_bounds__(kThreads * KS) __attribute__((amdgpu_waves_per_eu(2
       xo[qb] = (emit && txt && a.xattn_out != nullptr && valid[qb])
                    ? a.xattn_out + (static_cast<size_t>(h) * a.N + row[qb]) * a.T + (t - n_img) * kBN
                    : nullptr;
-    tile_step<QB, true, EXACT_SUM, KM, D, FP8>(st, ck, cv, kperm, g, li, dc0, c2, nvalid, xo, a.scale, mcur);
+    tile_step<QB, true, EXACT_SUM, KM, D, FP8>(st, ck, cv, kperm, g, li, dc0, c2, nvalid, xo, scale_eff, mcur);
     tile_barrier();
     if constexpr (KM != 0) mcur = mnext;
   };
@@ -1300,7 +1312,7 @@ __global__ __launch_bounds__(kThreads * KS) __attribute__((amdgpu_waves_per_eu(2
     const bool odd = ((t - t_begin) & 1) != 0;
     masked_tile(t, odd ? k_b : k_a, odd ? v_b : v_a, odd ? k_a : k_b, odd ? v_a : v_b);
   }
-  if (emit && n_txt == 0 && a.lse_img_out != nullptr) store_lse_img(a, st, h, row, valid, g);
+  if (emit && n_txt == 0 && a.lse_img_out != nullptr) store_lse_img(a, st, h, row, valid, g, scale_eff);
 
   if constexpr (KS == 2) {
     for (int i = 0; i < pad; ++i) __syncthreads();
@@ -1362,7 +1374,7 @@ __global__ __launch_bounds__(kThreads * KS) __attribute__((amdgpu_waves_per_eu(2
         v.y = pack_bf16x2(st.o[qb][db][4 * rr + 2] * inv, st.o[qb][db][4 * rr + 3] * inv);
         *reinterpret_cast<uint2*>(orow + dc) = v;
       }
-    if (a.lse != nullptr && g == 0) a.lse[bh * a.N + row[qb]] = lt > 0.f ? st.m[qb] * a.scale + logf(lt) : -INFINITY;
+    if (a.lse != nullptr && g == 0) a.lse[bh * a.N + row[qb]] = lt > 0.f ? st.m[qb] * scale_eff + logf(lt) : -INFINITY;
   }
 }
 
@@ -1374,11 +1386,11 @@ static void launch(const AttnArgs& a, hipStream_t s) {
   k_attn_mfma<GATHER, QB, EXACT_SUM, KM, KS, D, FP8><<<grid, kThreads * KS, 0, s>>>(a);
 }
 
-template <bool GATHER, int QB, int KM, int D>
+template <bool GATHER, int QB, int KM, int D, bool FP8 = false>
 static void launch_sum(const AttnArgs& a, hipStream_t s) {
   const bool exact = a.lse != nullptr || a.lse_img_out != nullptr || a.xattn_out != nullptr;
-  if (exact) launch<GATHER, QB, true, KM, D>(a, s);
-  else launch<GATHER, QB, false, KM, D>(a, s);
+  if (exact) launch<GATHER, QB, true, KM, D, 1, FP8>(a, s);
+  else launch<GATHER, QB, false, KM, D, 1, FP8>(a, s);
 }
 
 template <bool GATHER>
@@ -1423,28 +1435,38 @@ static void launch_rows128(const AttnArgs& a, hipStream_t s) {
   else launch<GATHER, 1, false, 0, 128, 2>(a, s);
 }
 
-// fp8 Q / K (head dim 64, mask-free fast path): the work shapes of the bf16 fast path.
+// fp8 Q / K: the work shapes of the bf16 kernel at each head dim (a kept mask and the exact-sum path with one
+// query block per wave, the fast path's key split), with the fp8 logit instructions.
 template <bool GATHER>
 static void launch_rows64_fp8(const AttnArgs& a, hipStream_t s) {
+  if (a.mask != nullptr) {
+    if (a.mask_dtype == SAFE_DTYPE_BOOL) launch_sum<GATHER, 1, 1, 64, true>(a, s);
+    else launch_sum<GATHER, 1, 2, 64, true>(a, s);
+    return;
+  }
   const double waves_qb2 = static_cast<double>(a.B) * a.H * ((a.R + 63) / 64);
-  if (waves_qb2 >= 2048.0) launch<GATHER, 2, false, 0, 64, 1, true>(a, s);
-  else if (waves_qb2 > 1024.0) launch<GATHER, 1, false, 0, 64, 1, true>(a, s);
+  const bool exact = a.lse != nullptr || a.lse_img_out != nullptr || a.xattn_out != nullptr;
+  if (waves_qb2 >= 2048.0) launch_sum<GATHER, 2, 0, 64, true>(a, s);
+  else if (exact || waves_qb2 > 1024.0) launch_sum<GATHER, 1, 0, 64, true>(a, s);
   else if (waves_qb2 >= 512.0) launch<GATHER, 2, false, 0, 64, 2, true>(a, s);
   else launch<GATHER, 1, false, 0, 64, 2, true>(a, s);
 }
 
-// fp8 Q / K at head dim 128: the mask-free work shapes of the bf16 head-dim-128 path.
 template <bool GATHER>
 static void launch_rows128_fp8(const AttnArgs& a, hipStream_t s) {
+  if (a.mask != nullptr) {  // bool only (the host rejects an fp32 mask here)
+    launch_sum<GATHER, 1, 1, 128, true>(a, s);
+    return;
+  }
   const double waves_qb1 = static_cast<double>(a.B) * a.H * ((a.R + 31) / 32);
-  if (waves_qb1 >= 2048.0) launch<GATHER, 1, false, 0, 128, 1, true>(a, s);
+  const bool exact = a.lse != nullptr || a.lse_img_out != nullptr || a.xattn_out != nullptr;
+  if (exact || waves_qb1 >= 2048.0) launch_sum<GATHER, 1, 0, 128, true>(a, s);
   else launch<GATHER, 1, false, 0, 128, 2, true>(a, s);
 }
 
 hipError_t launch_attn_mfma_fp8(const AttnArgs& a, int d, hipStream_t s) {
   if (a.R == 0) return hipSuccess;
-  if (a.mask != nullptr || a.lse != nullptr || a.xattn_out != nullptr || a.lse_img_out != nullptr)
-    return hipErrorInvalidValue;
+  if (d == 128 && a.mask != nullptr && a.mask_dtype != SAFE_DTYPE_BOOL) return hipErrorInvalidValue;
   if (d == 128) {
     if (a.rows != nullptr) launch_rows128_fp8<true>(a, s);
     else launch_rows128_fp8<false>(a, s);

@@ -1,5 +1,6 @@
 """GPU parity of the fp8 attention path (FP8 E4M3 Q and K with per-(b,h) factors, bf16 V and output; head dim
-64 and 128, mask-free fast path) against the fp64 oracle on the dequantised inputs."""
+64 and 128; the fast path, the exact-sum path with lse and emission, kept masks) against the fp64 oracle on the
+dequantised inputs."""
 import numpy as np
 import pytest
 
@@ -156,22 +157,94 @@ def test_fp8_full_size_sampled(lib, name):
 
 
 def test_fp8_unsupported_requests_are_rejected(lib):
+    """fp8 runs on the MFMA kernel only: masks it does not take are refused (there is no generic fp8 kernel)."""
     t = torch()
-    w = _w(B=1, H=1, N=64, T=0, tv=(0,))
+    w = _w(B=1, H=1, N=40, T=0, tv=(0,))
     inp = syn.attention_inputs_fp8(w)
     q, ki, vi, kt, vt, qd, kd = _tensors(inp)
     out = t.zeros(q.shape, dtype=t.bfloat16, device="cuda")
-    lse = t.zeros((1, 1, 64), dtype=t.float32, device="cuda")
-    mask = t.ones((1, 1, 64, 64), dtype=t.bool, device="cuda")
-    for kw in ({"lse": lse}, {"mask": mask}):
-        with pytest.raises(lib.SafeAttnError) as e:
-            lib.safe_attn_dense(q, ki, vi, kt, vt, w.tv, out, q_descale=qd, k_descale=kd, **kw)
-        assert e.value.code == 6
+    with pytest.raises(lib.SafeAttnError) as e:  # N not a multiple of 16
+        lib.safe_attn_dense(q, ki, vi, kt, vt, w.tv, out, mask=t.ones((1, 1, 40, 40), dtype=t.bool, device="cuda"))
+    assert e.value.code == 6
     q2 = t.zeros((1, 1, 64, 128), dtype=t.float8_e4m3fn, device="cuda")
     v2 = t.zeros((1, 1, 64, 128), dtype=t.bfloat16, device="cuda")
-    with pytest.raises(lib.SafeAttnError) as e:  # head dim 128 takes fp8, but not with an lse
-        lib.safe_attn_dense(q2, q2, v2, None, None, (0,), v2.clone(), lse=lse)
+    with pytest.raises(lib.SafeAttnError) as e:  # an fp32 mask at head dim 128
+        lib.safe_attn_dense(q2, q2, v2, None, None, (0,), v2.clone(),
+                            mask=t.zeros((1, 1, 64, 64), dtype=t.float32, device="cuda"))
     assert e.value.code == 6
+    q3 = t.zeros((1, 1, 64, 64), dtype=t.float8_e4m3fn, device="cuda")
+    v3 = t.zeros((1, 1, 64, 64), dtype=t.bfloat16, device="cuda")
+    with pytest.raises(lib.SafeAttnError) as e:  # a mask beside the emission
+        lib.safe_attn_dense(q3, q3, v3, q3[:, :, :16], v3[:, :, :16], (16,), v3.clone(),
+                            mask=t.ones((1, 1, 64, 64), dtype=t.bool, device="cuda"),
+                            xattn_out=t.zeros((1, 64, 16), dtype=t.float32, device="cuda"))
+    assert e.value.code == 6
+
+
+def _run_x(lib, w, inp, rows=None, state=None, mask=None, want_lse=True, emission=False):
+    """fp8 launch with the exact-sum outputs (lse, warmup emission) and an optional kept mask."""
+    t = torch()
+    q, ki, vi, kt, vt, qd, kd = _tensors(inp)
+    out = t.from_numpy(state.astype(np.float32)).to(t.bfloat16).cuda() if state is not None else \
+        t.zeros(q.shape, dtype=t.bfloat16, device="cuda")
+    lse = t.full((w.B, w.H, w.N), float("nan"), dtype=t.float32, device="cuda") if want_lse else None
+    xo = t.full((w.H, w.N, w.T), float("nan"), dtype=t.float32, device="cuda") if emission else None
+    li = t.full((w.H, w.N), float("nan"), dtype=t.float32, device="cuda") if emission else None
+    kw = dict(mask=mask, lse=lse, xattn_out=xo, lse_img_out=li, q_descale=qd, k_descale=kd)
+    if rows is None:
+        lib.safe_attn_dense(q, ki, vi, kt, vt, w.tv, out, **kw)
+    else:
+        lib.safe_attn_rows(q, ki, vi, kt, vt, w.tv, dev(np.asarray(rows, dtype=np.int32)), out, **kw)
+    t.cuda.synchronize()
+    return host(out), (host(lse) if want_lse else None), (host(xo) if emission else None), (host(li) if emission else None)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_fp8_lse_and_emission(lib, d):
+    """The exact-sum path on fp8 codes: output, lse, the emitted text logits (natural units, the factors applied)
+    and the image lse, against the oracle on the dequantised values."""
+    w = syn.scaled(syn.WORKLOADS["dense_1024"], side=1, d=d, B=2, H=3, N=333, T=256, tv=(77, 20))
+    inp = syn.attention_inputs_fp8(w)
+    o, lse, x, li = _run_x(lib, w, inp, emission=True)
+    ro, rlse, rx, rli = OA.attention(inp["q"], inp["k_img"], inp["v_img"], inp["k_txt"], inp["v_txt"], w.tv,
+                                     want_emission=True)
+    assert_close(o, ro, "bf16", f"fp8 d{d} exact-sum output")
+    assert np.max(np.abs(lse - rlse)) < 1e-4
+    assert np.max(np.abs(x[:, :, :77] - rx)) < 1e-5
+    assert np.max(np.abs(li - rli)) < 1e-4
+    rows = syn.random_rows(w, k=100)
+    o2, lse2, _, _ = _run_x(lib, w, inp, rows=rows, state=syn.initial_state(w))
+    ro2, rlse2 = OA.attention(inp["q"], inp["k_img"], inp["v_img"], inp["k_txt"], inp["v_txt"], w.tv, rows=rows)
+    assert_close(o2[:, :, rows], ro2, "bf16", f"fp8 d{d} exact-sum rows")
+    assert np.max(np.abs(lse2[:, :, rows] - rlse2)) < 1e-4
+
+
+@pytest.mark.parametrize("d,kind,text_cols,want_lse", [(64, "bool", True, True), (64, "f32", False, False),
+                                                       (64, "f32", True, True), (128, "bool", False, True)])
+def test_fp8_kept_masks(lib, d, kind, text_cols, want_lse):
+    """Kept masks on fp8 codes (the mask value converted to the units of the code products): dense and rows
+    against the oracle, fully masked rows give 0 and lse = -inf."""
+    from tests.test_gpu_attention import _kept_mask
+    N, T = 256, 64
+    w = syn.scaled(syn.WORKLOADS["dense_1024"], side=1, d=d, B=2, H=3, N=N, T=T, tv=(30, 64))
+    inp = syn.attention_inputs_fp8(w)
+    r = np.random.default_rng(N + d + len(kind))
+    cols = N + T if text_cols else N
+    full = (5, N - 1) if text_cols else ()
+    m = _kept_mask(r, kind, (2, 1, N, cols), N, 64, full_rows=full)
+    o, lse, _, _ = _run_x(lib, w, inp, mask=dev(m), want_lse=want_lse)
+    ro, rlse = OA.attention(inp["q"], inp["k_img"], inp["v_img"], inp["k_txt"], inp["v_txt"], w.tv, mask=m)
+    assert_close(o, ro, "bf16", f"fp8 d{d} {kind} mask")
+    if want_lse:
+        fin = np.isfinite(rlse)
+        assert np.array_equal(fin, np.isfinite(lse))
+        assert np.max(np.abs(lse[fin] - rlse[fin])) < 1e-4
+    for i in full:
+        assert np.all(o[:, :, i] == 0)
+    rows = np.array([0, 5, 77, 200, N - 1], dtype=np.int32)
+    o2, _, _, _ = _run_x(lib, w, inp, rows=rows, state=np.zeros((2, 3, N, d), np.float32), mask=dev(m), want_lse=False)
+    ro2, _ = OA.attention(inp["q"], inp["k_img"], inp["v_img"], inp["k_txt"], inp["v_txt"], w.tv, rows=rows, mask=m)
+    assert_close(o2[:, :, rows], ro2, "bf16", f"fp8 d{d} {kind} mask rows")
 
 
 # ---- head dim 128: two fp8 instructions per 32-key half, one query block per wave
