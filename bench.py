@@ -51,6 +51,8 @@ def parse():
                          "profiling those launches")
     ap.add_argument("--block-only", action="store_true",
                     help="run only the sensitive-row block products (FFN, QKV) and print them; for profiling them")
+    ap.add_argument("--trajectory-only", action="store_true",
+                    help="run only the 3072^2 trajectory line and print it; for profiling it")
     return ap.parse_args()
 
 
@@ -77,6 +79,9 @@ def main():
         if args.copy_calibration:
             out["copy_calibration_bytes"] = copy_calibration(torch, dev)
         print(json.dumps(out), flush=True)
+        return
+    if args.trajectory_only:
+        print(json.dumps({"trajectory_3072": trajectory_3072(dts, torch, np, syn, dev)}), flush=True)
         return
     if args.block_only:
         out = {"srsu_block": srsu_block(dts, torch, np, syn, dev)}
