@@ -44,7 +44,10 @@ def _ffn(lib, p, cache0, with_bias=True):
 @pytest.mark.parametrize("B,N,H,d,k,mult", [(1, 40, 2, 64, 1, 4), (2, 300, 2, 64, 77, 4), (2, 300, 2, 64, 300, 4),
                                             (2, 500, 4, 64, 129, 2), (3, 257, 2, 64, 200, 1),
                                             (2, 300, 8, 64, 77, 4), (1, 600, 8, 64, 299, 4),  # F = 2048: 256 x 256 tiles
-                                            (2, 300, 12, 64, 131, 3)])  # F = 2304: 192 x 256 tiles, ragged tokens
+                                            (2, 300, 12, 64, 131, 3),  # F = 2304: 192 x 256 tiles, ragged tokens
+                                            # D -> F with K = D = 128 (four 32-element stages: the ring's tail
+                                            # alone) on both tile widths, and K = 256 (one pass of the loop)
+                                            (1, 100, 2, 64, 37, 16), (1, 100, 2, 64, 37, 18), (2, 100, 4, 64, 50, 8)])
 def test_rows_ffn_parity_and_cache_untouched(lib, B, N, H, d, k, mult):
     p = _inputs(B, N, H, d, k, seed=N + k, ffn_mult=mult)
     cache0 = syn.round_to_bf16(np.random.default_rng(k).standard_normal((B, N, p["D"])).astype(np.float32))
