@@ -285,16 +285,17 @@ __device__ __forceinline__ void wait_vmcnt() {
 // 1024^2 shapes: 180 tiles of 256 on 256 CUs, 240 of 192).
 //
 // K streams through a ring of four LDS stages of 32 elements (four distinct objects per operand, so the
-// compiler sees that a copy in flight into one does not alias the reads of another), the copies of stage
-// s + 3 in flight while stage s is multiplied: one stage of slack more than two buffers of 64 and half the
-// first stage to wait for.  Stage s runs in two halves of 8 matrix instructions per wave:
+// compiler sees that a copy in flight into one does not alias the reads of another).  The copies of a stage
+// are issued three stages before it is multiplied (96 K elements ahead, against 64 for two buffers of 64
+// elements), and the launch waits for half as many bytes before its first matrix instruction.  Stage s runs in
+// two halves of 2 JB / 64 matrix instructions per wave (8 at JB = 256, 6 at 192):
 //   * first half: the first K step (operands read during the previous stage), with the reads of the second K
-//     step issued after its first four instructions;
+//     step issued after the first half of its instructions;
 //   * then this wave's reads of the buffer are waited for and its copies of stage s + 1 (vector-memory count,
 //     not a drain of every copy in flight), two instructions of the second half are queued, and the
 //     workgroup meets at a bare s_barrier (a fence-carrying __syncthreads would wait for every copy);
 //   * second half: the reads of the first K step of stage s + 1 and the copies of stage s + 4 into the buffer
-//     just released, interleaved with the remaining six instructions.
+//     just released, interleaved with the remaining instructions.
 // Measured on the gathered D -> F product at the 1024^2 shapes (2458 x 1536 -> 6144): 71k against 93k
 // shader cycles per workgroup for the two-buffer form with stages of 64, bitwise the same outputs.
 template <int IN, int OUT, bool GELU, int JB = 256>
