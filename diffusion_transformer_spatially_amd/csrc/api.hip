@@ -54,8 +54,6 @@ safe_status check_attn(const safe_attn_desc* d) {
     if (d->mask_dtype == SAFE_DTYPE_F32 && (reinterpret_cast<uintptr_t>(d->mask) & 3u) != 0) return SAFE_ERR_ALIGN;
   }
   if (d->dtype == SAFE_DTYPE_FP8_E4M3) {
-    // fp8 Q / K run on the MFMA kernel only: a kept mask must be one it takes (see mfma_takes_mask)
-    if ((d->d != 64 && d->d != 128) || (d->mask != nullptr && !mfma_takes_mask(d))) return SAFE_ERR_UNSUPPORTED;
     if ((reinterpret_cast<uintptr_t>(d->q_descale) & 3u) != 0 || (reinterpret_cast<uintptr_t>(d->k_descale) & 3u) != 0)
       return SAFE_ERR_ALIGN;
   }
@@ -95,9 +93,10 @@ AttnArgs make_args(const safe_attn_desc* d, const int32_t* rows, int R) {
 safe_status run_attn(const safe_attn_desc* d, const int32_t* rows, int R, hipStream_t s) {
   const AttnArgs a = make_args(d, rows, R);
   if (R == 0) return SAFE_OK;
-  if (d->dtype == SAFE_DTYPE_FP8_E4M3) return from_hip(launch_attn_mfma_fp8(a, d->d, s));
-  if (d->dtype == SAFE_DTYPE_BF16 && (d->mask == nullptr || mfma_takes_mask(d)))
-    return from_hip(launch_attn_mfma_bf16(a, d->d, s));
+  // bf16 and fp8: the MFMA kernel unless a kept mask is one it does not take (then the generic kernel)
+  const bool mfma = d->mask == nullptr || mfma_takes_mask(d);
+  if (d->dtype == SAFE_DTYPE_FP8_E4M3 && mfma) return from_hip(launch_attn_mfma_fp8(a, d->d, s));
+  if (d->dtype == SAFE_DTYPE_BF16 && mfma) return from_hip(launch_attn_mfma_bf16(a, d->d, s));
   return from_hip(launch_attn_generic(a, d->dtype, d->d, s));
 }
 

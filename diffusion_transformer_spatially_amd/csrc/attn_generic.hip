@@ -1,7 +1,9 @@
-// General attention kernel on the vector ALUs: fp32 or bf16 storage, dense or sensitive rows,
-// optional kept additive mask (fp32 or bool), optional warmup emission.  It serves the fp32 path and
-// the bf16 kept-mask calls the MFMA kernel does not take (an emission request, or N or the mask row
-// length not a multiple of 16, or an unaligned mask); all other bf16 calls run on the MFMA kernel.
+// General attention kernel on the vector ALUs: fp32 or bf16 storage (or fp8 E4M3 Q / K with bf16 V and
+// output), dense or sensitive rows, optional kept additive mask (fp32 or bool), optional warmup emission.
+// It serves the fp32 path and the bf16 / fp8 kept-mask calls the MFMA kernel does not take (an emission
+// request, N or the mask row length not a multiple of 16, an unaligned mask, or an fp32 mask at head dim
+// 128); all other bf16 and fp8 calls run on the MFMA kernel.  fp8 codes are decoded exactly to fp32 and the
+// per-(b,h) dequantisation factors of Q and K scale the dot products, as the logit scale does.
 //
 // Semantics (SAFE-DiT technical summary, Methodology 1 and 3): one joint softmax per image query row
 // over the image keys then the valid text keys (padded text slots never enter), logits scaled by
@@ -25,6 +27,16 @@ template <>
 __device__ __forceinline__ float ld<float>(const float* p, size_t i) { return p[i]; }
 template <>
 __device__ __forceinline__ float ld<uint16_t>(const uint16_t* p, size_t i) { return bf16_to_f32(p[i]); }
+// OCP E4M3 (sign, 4 exponent bits of bias 7, 3 mantissa bits; no infinities, S.1111.111 is NaN): normal codes
+// are (1 + m/8) 2^(e-7), placed directly in the fp32 exponent and mantissa fields; subnormals m 2^-9.
+template <>
+__device__ __forceinline__ float ld<uint8_t>(const uint8_t* p, size_t i) {
+  const uint32_t c = p[i];
+  const uint32_t sgn = (c & 0x80u) << 24, e = (c >> 3) & 0xfu, m = c & 7u;
+  if ((c & 0x7fu) == 0x7fu) return __uint_as_float(sgn | 0x7fc00000u);
+  if (e == 0) return __uint_as_float(sgn | __float_as_uint(static_cast<float>(m) * 0.001953125f));
+  return __uint_as_float(sgn | ((e + 120u) << 23) | (m << 20));
+}
 
 template <typename T>
 __device__ __forceinline__ void st(T* p, size_t i, float v);
@@ -33,7 +45,8 @@ __device__ __forceinline__ void st<float>(float* p, size_t i, float v) { p[i] = 
 template <>
 __device__ __forceinline__ void st<uint16_t>(uint16_t* p, size_t i, float v) { p[i] = f32_to_bf16_rne(v); }
 
-template <typename T, bool HAS_MASK, int D>
+// T: storage of V and the output (and of Q / K unless TQ says otherwise); TQ: storage of Q and K
+template <typename T, bool HAS_MASK, int D, typename TQ = T>
 __global__ __launch_bounds__(kGenThreads) void k_attn_generic(AttnArgs a) {
   constexpr int kLpr = D / kGenPart;             // threads per query row
   constexpr int kRows = kGenThreads / kLpr;      // query rows per workgroup
@@ -51,11 +64,15 @@ __global__ __launch_bounds__(kGenThreads) void k_attn_generic(AttnArgs a) {
   const bool valid_row = active && row >= 0 && row < a.N;
   if (!valid_row) row = 0;
   const int tv = a.tv[b];
-  const T* Q = static_cast<const T*>(a.q) + static_cast<size_t>(bh) * a.N * D;
-  const T* KI = static_cast<const T*>(a.k_img) + static_cast<size_t>(bh) * a.N * D;
+  const TQ* Q = static_cast<const TQ*>(a.q) + static_cast<size_t>(bh) * a.N * D;
+  const TQ* KI = static_cast<const TQ*>(a.k_img) + static_cast<size_t>(bh) * a.N * D;
   const T* VI = static_cast<const T*>(a.v_img) + static_cast<size_t>(bh) * a.N * D;
-  const T* KT = static_cast<const T*>(a.k_txt) + static_cast<size_t>(bh) * a.T * D;
+  const TQ* KT = static_cast<const TQ*>(a.k_txt) + static_cast<size_t>(bh) * a.T * D;
   const T* VT = static_cast<const T*>(a.v_txt) + static_cast<size_t>(bh) * a.T * D;
+  // the logit scale in the units of the dot products (fp8 codes: times the (b,h) factors of Q and K)
+  float scale = a.scale;
+  if (a.q_descale != nullptr) scale *= a.q_descale[bh];
+  if (a.k_descale != nullptr) scale *= a.k_descale[bh];
 
   float q[kGenPart], o[kGenPart];
 #pragma unroll
@@ -72,7 +89,6 @@ __global__ __launch_bounds__(kGenThreads) void k_attn_generic(AttnArgs a) {
            ((static_cast<size_t>(mb) * a.mask_H + mh) * a.N + row) * static_cast<size_t>(a.mask_cols) * esz;
   }
   const bool emit = (a.xattn_out != nullptr || a.lse_img_out != nullptr) && b == 0;
-  const float c2 = a.scale * kLog2e;  // logits are tracked in log2 units
   float m = -INFINITY, l = 0.f;
   const int n_img_tiles = (a.N + kGenTile - 1) / kGenTile;
   const int n_txt_tiles = (tv + kGenTile - 1) / kGenTile;
@@ -80,7 +96,7 @@ __global__ __launch_bounds__(kGenThreads) void k_attn_generic(AttnArgs a) {
     const bool txt = t >= n_img_tiles;
     const int j0 = txt ? (t - n_img_tiles) * kGenTile : t * kGenTile;
     const int nvalid = txt ? min(kGenTile, tv - j0) : min(kGenTile, a.N - j0);
-    const T* Ksrc = txt ? KT : KI;
+    const TQ* Ksrc = txt ? KT : KI;
     const T* Vsrc = txt ? VT : VI;
     __syncthreads();
     for (int e = threadIdx.x; e < kGenTile * D; e += kGenThreads) {
@@ -99,7 +115,7 @@ __global__ __launch_bounds__(kGenThreads) void k_attn_generic(AttnArgs a) {
 #pragma unroll
       for (int c = 0; c < kGenPart; ++c) acc = fmaf(q[c], ks[jj][c0 + c], acc);
       if constexpr (kLpr == 2) acc += __shfl_xor(acc, 1);  // the other half of the row's dot product
-      float z = acc * a.scale;  // natural-log logit
+      float z = acc * scale;  // natural-log logit
       if (HAS_MASK) {
         const int col = (txt ? a.N : 0) + j0 + jj;
         float mv = 0.f;
@@ -132,7 +148,6 @@ __global__ __launch_bounds__(kGenThreads) void k_attn_generic(AttnArgs a) {
     if (emit && t == n_img_tiles - 1 && a.lse_img_out != nullptr && valid_row && part == 0)
       a.lse_img_out[static_cast<size_t>(h) * a.N + row] = (l > 0.f) ? (m + log2f(l)) * kLn2 : -INFINITY;
   }
-  (void)c2;
   if (!valid_row) return;
   const float inv = l > 0.f ? 1.f / l : 0.f;
   T* O = static_cast<T*>(a.out) + static_cast<size_t>(bh) * a.N * D;
@@ -151,6 +166,9 @@ static void launch_generic(const AttnArgs& a, int dtype, hipStream_t s) {
   if (dtype == SAFE_DTYPE_F32) {
     if (mask) k_attn_generic<float, true, D><<<grid, kGenThreads, 0, s>>>(a);
     else k_attn_generic<float, false, D><<<grid, kGenThreads, 0, s>>>(a);
+  } else if (dtype == SAFE_DTYPE_FP8_E4M3) {
+    if (mask) k_attn_generic<uint16_t, true, D, uint8_t><<<grid, kGenThreads, 0, s>>>(a);
+    else k_attn_generic<uint16_t, false, D, uint8_t><<<grid, kGenThreads, 0, s>>>(a);
   } else {
     if (mask) k_attn_generic<uint16_t, true, D><<<grid, kGenThreads, 0, s>>>(a);
     else k_attn_generic<uint16_t, false, D><<<grid, kGenThreads, 0, s>>>(a);

@@ -67,10 +67,10 @@ enum {
  * dtype           SAFE_DTYPE_BF16 or SAFE_DTYPE_F32, for q, k_*, v_*, out; or SAFE_DTYPE_FP8_E4M3: q, k_img
  *                 and k_txt are FP8 E4M3 values whose real value is the stored value times the (b,h) entry
  *                 of q_descale / k_descale, while v_img, v_txt and out are bf16 (the probabilities stay
- *                 bf16 for P V).  FP8 takes d == 64 or 128, the lse and the warmup emission as bf16 does,
- *                 and a kept mask only where the MFMA kernel takes one: N and the mask row length
- *                 multiples of 16, a 16-byte aligned mask, no emission beside it, and at d == 128 a bool
- *                 mask (else SAFE_ERR_UNSUPPORTED).
+ *                 bf16 for P V).  FP8 takes d == 64 or 128, the lse, the warmup emission and every kept
+ *                 mask as bf16 does (the masks the MFMA kernel does not take -- N or the mask row length
+ *                 not a multiple of 16, an unaligned mask, a mask beside the emission, an fp32 mask at
+ *                 d == 128 -- run on the general kernel, which decodes the codes exactly to fp32).
  * B, H, N, T, d   1 <= B <= SAFE_MAX_BATCH, H >= 1, N >= 1, T >= 0, d == 64 or d == 128 (the head
  *                 dims of the DiT backbones the pages evaluate across; other values: SAFE_ERR_UNSUPPORTED).
  * text_valid_len  HOST array [B], 0 <= Tv[b] <= T.

@@ -1,6 +1,6 @@
 """GPU parity of the fp8 attention path (FP8 E4M3 Q and K with per-(b,h) factors, bf16 V and output; head dim
-64 and 128; the fast path, the exact-sum path with lse and emission, kept masks) against the fp64 oracle on the
-dequantised inputs."""
+64 and 128; the fast path, the exact-sum path with lse and emission, kept masks on the MFMA kernel and on the
+general kernel) against the fp64 oracle on the dequantised inputs."""
 import numpy as np
 import pytest
 
@@ -156,31 +156,6 @@ def test_fp8_full_size_sampled(lib, name):
     assert_close(o[:, :, pick], _oracle(w, inp, pick), "bf16", "fp8 rows 1024^2")
 
 
-def test_fp8_unsupported_requests_are_rejected(lib):
-    """fp8 runs on the MFMA kernel only: masks it does not take are refused (there is no generic fp8 kernel)."""
-    t = torch()
-    w = _w(B=1, H=1, N=40, T=0, tv=(0,))
-    inp = syn.attention_inputs_fp8(w)
-    q, ki, vi, kt, vt, qd, kd = _tensors(inp)
-    out = t.zeros(q.shape, dtype=t.bfloat16, device="cuda")
-    with pytest.raises(lib.SafeAttnError) as e:  # N not a multiple of 16
-        lib.safe_attn_dense(q, ki, vi, kt, vt, w.tv, out, mask=t.ones((1, 1, 40, 40), dtype=t.bool, device="cuda"))
-    assert e.value.code == 6
-    q2 = t.zeros((1, 1, 64, 128), dtype=t.float8_e4m3fn, device="cuda")
-    v2 = t.zeros((1, 1, 64, 128), dtype=t.bfloat16, device="cuda")
-    with pytest.raises(lib.SafeAttnError) as e:  # an fp32 mask at head dim 128
-        lib.safe_attn_dense(q2, q2, v2, None, None, (0,), v2.clone(),
-                            mask=t.zeros((1, 1, 64, 64), dtype=t.float32, device="cuda"))
-    assert e.value.code == 6
-    q3 = t.zeros((1, 1, 64, 64), dtype=t.float8_e4m3fn, device="cuda")
-    v3 = t.zeros((1, 1, 64, 64), dtype=t.bfloat16, device="cuda")
-    with pytest.raises(lib.SafeAttnError) as e:  # a mask beside the emission
-        lib.safe_attn_dense(q3, q3, v3, q3[:, :, :16], v3[:, :, :16], (16,), v3.clone(),
-                            mask=t.ones((1, 1, 64, 64), dtype=t.bool, device="cuda"),
-                            xattn_out=t.zeros((1, 64, 16), dtype=t.float32, device="cuda"))
-    assert e.value.code == 6
-
-
 def _run_x(lib, w, inp, rows=None, state=None, mask=None, want_lse=True, emission=False):
     """fp8 launch with the exact-sum outputs (lse, warmup emission) and an optional kept mask."""
     t = torch()
@@ -245,6 +220,50 @@ def test_fp8_kept_masks(lib, d, kind, text_cols, want_lse):
     o2, _, _, _ = _run_x(lib, w, inp, rows=rows, state=np.zeros((2, 3, N, d), np.float32), mask=dev(m), want_lse=False)
     ro2, _ = OA.attention(inp["q"], inp["k_img"], inp["v_img"], inp["k_txt"], inp["v_txt"], w.tv, rows=rows, mask=m)
     assert_close(o2[:, :, rows], ro2, "bf16", f"fp8 d{d} {kind} mask rows")
+
+
+@pytest.mark.parametrize("d,case", [(64, "n40"), (128, "f32"), (64, "emission"), (128, "emission"), (64, "unaligned")])
+def test_fp8_masks_on_the_general_kernel(lib, d, case):
+    """Kept masks the MFMA kernel does not take (N not a multiple of 16, an fp32 mask at head dim 128, a mask
+    beside the warmup emission, a bool mask at an odd address) run on the general kernel with the fp8 codes decoded
+    exactly: output, lse, a fully masked row (0 and -inf), the emitted text logits and image lse, and gathered
+    rows, against the oracle on the dequantised values."""
+    from tests.test_gpu_attention import _kept_mask
+    t = torch()
+    N, T = (40, 64) if case == "n40" else (96, 64)
+    w = syn.scaled(syn.WORKLOADS["dense_1024"], side=1, d=d, B=2, H=2, N=N, T=T, tv=(30, 64))
+    inp = syn.attention_inputs_fp8(w)
+    r = np.random.default_rng(N + d + len(case))
+    kind = "f32" if case == "f32" else "bool"
+    m = _kept_mask(r, kind, (2, 1, N, N + T), N, 64, full_rows=(3,))
+    md = dev(m)
+    if case == "unaligned":
+        flat = t.zeros(m.size + 1, dtype=t.bool, device="cuda")
+        flat[1:] = md.reshape(-1)
+        md = flat[1:].view(m.shape)
+        assert md.data_ptr() % 16 != 0
+    emission = case == "emission"
+    o, lse, x, li = _run_x(lib, w, inp, mask=md, want_lse=True, emission=emission)
+    ref = OA.attention(inp["q"], inp["k_img"], inp["v_img"], inp["k_txt"], inp["v_txt"], w.tv, mask=m,
+                       want_emission=emission)
+    ro, rlse = ref[0], ref[1]
+    assert_close(o, ro, "bf16", f"fp8 d{d} {case} general kernel")
+    fin = np.isfinite(rlse)
+    assert np.array_equal(fin, np.isfinite(lse))
+    assert np.max(np.abs(lse[fin] - rlse[fin])) < 1e-4
+    assert np.all(o[:, :, 3] == 0) and np.all(np.isneginf(lse[:, :, 3]))
+    if emission:
+        rx, rli = ref[2], ref[3]
+        xv = x[:, :, :w.tv[0]]
+        assert np.array_equal(np.isfinite(xv), np.isfinite(rx))
+        assert np.max(np.abs(xv[np.isfinite(rx)] - rx[np.isfinite(rx)])) < 1e-5
+        fl = np.isfinite(rli)
+        assert np.array_equal(fl, np.isfinite(li))
+        assert np.max(np.abs(li[fl] - rli[fl])) < 1e-4
+    rows = np.array([0, 3, 17, N - 1], dtype=np.int32)
+    o2, _, _, _ = _run_x(lib, w, inp, rows=rows, state=np.zeros((2, 2, N, d), np.float32), mask=md, want_lse=False)
+    ro2, _ = OA.attention(inp["q"], inp["k_img"], inp["v_img"], inp["k_txt"], inp["v_txt"], w.tv, rows=rows, mask=m)
+    assert_close(o2[:, :, rows], ro2, "bf16", f"fp8 d{d} {case} general kernel rows")
 
 
 # ---- head dim 128: two fp8 instructions per 32-key half, one query block per wave
