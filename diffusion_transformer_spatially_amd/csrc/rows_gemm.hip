@@ -28,7 +28,9 @@
 //  * output rows: packed [T, Dout], scattered to row S[r] of [B, N, Dout] (the FFN cache: context rows
 //    untouched), or split into head-major Q / K / V [B, H, N, d] at row S[r] (16 consecutive features
 //    never cross a head of d = 64 channels);
-//  * the workgroup id is remapped so that the workgroups sharing one weight tile run on one XCD.
+//  * the workgroup id is remapped so that consecutive tiles run on one XCD: on the wide products the tiles
+//    of one weight tile, on the narrow product (K four times longer, 1.5 MB per operand tile) a block of
+//    about five token tiles by six feature tiles, so that its L2 holds the operands of that block only.
 #include <type_traits>
 
 #include "common.hpp"
@@ -145,6 +147,20 @@ __device__ __forceinline__ void store16(const RowsGemmArgs& a, int t, int f0, co
   reinterpret_cast<uint4*>(dst)[1] = hi;
 }
 
+// Launch-order index -> (token tile, feature tile) of the narrow product: token tiles in groups of kGroupT, and
+// inside a group the token tile varies fastest, so the consecutive indices that run on one XCD cover a block of
+// a few token tiles by a few feature tiles (5 x 6 of the 20 x 12 tiles at the 1024^2 shapes) and its L2 holds the
+// input rows and weight rows of that block only.
+constexpr int kGroupT = 5;
+__device__ __forceinline__ void grouped_tile(uint32_t lid, int nt, int nj, int& tt, int& jt) {
+  const int per = kGroupT * nj;
+  const int grp = static_cast<int>(lid) / per;
+  const int within = static_cast<int>(lid) - grp * per;
+  const int gt = min(kGroupT, nt - grp * kGroupT);
+  tt = grp * kGroupT + within % gt;
+  jt = within / gt;
+}
+
 template <int IN, int OUT, bool GELU>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_rows_gemm(RowsGemmArgs a) {
   constexpr int kK2 = 128;  // K elements per stage: 256-byte rows of 16 chunks
@@ -157,7 +173,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   const int nt = (T + kTT - 1) / kTT;
   const uint32_t G = static_cast<uint32_t>(nt) * static_cast<uint32_t>(a.Dout / kJT);
   const uint32_t lid = xcd_remap(blockIdx.x, G);
-  const int jt = static_cast<int>(lid / nt), tt = static_cast<int>(lid - static_cast<uint32_t>(jt) * nt);
+  int tt, jt;
+  grouped_tile(lid, nt, a.Dout / kJT, tt, jt);
   const int j0 = jt * kJT, t0 = tt * kTT;
 
   const int lane = threadIdx.x & 63;
