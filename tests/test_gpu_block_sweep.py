@@ -11,7 +11,7 @@ from tests.gpu_util import assert_close, dev, host, torch
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 16
+N_CASES = 24
 
 
 def _bf(x):

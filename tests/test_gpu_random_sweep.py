@@ -12,7 +12,7 @@ from tests.gpu_util import assert_close, dev, host, torch
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 48
+N_CASES = 96
 
 
 def _case(i):
@@ -102,8 +102,10 @@ def test_random_case_matches_oracle(lib, i):
     if c["rows"]:
         rows = np.sort(r.choice(N, size=c["k"], replace=False)).astype(np.int32)
         call_rows = rows
-        if c["outside"]:
-            call_rows = np.concatenate([[-3, -1], rows, [N, N + 7]]).astype(np.int32)
+        if c["outside"]:  # entries outside [0, N) at both ends, keeping the call's k <= N
+            room = N - len(rows)
+            lo, hi = [-3, -1][: (room + 1) // 2], [N, N + 7][: room // 2]
+            call_rows = np.concatenate([lo, rows, hi]).astype(np.int32)
         lib.safe_attn_rows(q, ki, vi, kt, vt, c["tv"], dev(call_rows), out, **kw)
     else:
         rows = np.arange(N, dtype=np.int32)
