@@ -13,8 +13,10 @@ __device__ __forceinline__ float guided(float ec, float eu, float g) { return fm
 // gamma = g_ctx (1 - s) + g_sens s, the mix of the two scales: with s in [0, 1] and scales of one sign the two
 // products never cancel, so gamma keeps fp32 relative accuracy even where it is small beside g_ctx (the
 // form g_ctx + (g_sens - g_ctx) s rounds g_sens - g_ctx first, an absolute error of about one ulp of the larger
-// scale), and s = 0 / s = 1 give g_ctx / g_sens exactly.
-__device__ __forceinline__ float gamma_of(float s, float g_ctx, float g_sens) { return fmaf(g_sens, s, g_ctx * (1.f - s)); }
+// scale), and s = 0 / s = 1 give g_ctx / g_sens exactly; equal scales give that scale exactly (global CFG).
+__device__ __forceinline__ float gamma_of(float s, float g_ctx, float g_sens) {
+  return g_ctx == g_sens ? g_ctx : fmaf(g_sens, s, g_ctx * (1.f - s));
+}
 
 // floor(a / b) for a < 2^24 without an integer divide: the float quotient is off by at most one, and
 // one exact integer comparison each way fixes it.

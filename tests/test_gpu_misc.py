@@ -47,6 +47,8 @@ def test_swcfg_shapes_and_closed_forms(lib, C, Hl, Wl, side):
     assert np.array_equal(_cfg(lib, eps, s, side, 0.0, 0.0), eps[1].astype(np.float64))
     got = _cfg(lib, eps, s, side, 4.5, 4.5)
     _cfg_check(got, eps, np.zeros(side * side), side, 4.5, 4.5)
+    # the per-token scale is exactly the global one: every pixel matches the s = 0 launch bit for bit
+    assert np.array_equal(got, _cfg(lib, eps, np.zeros_like(s), side, 4.5, 4.5))
 
 
 # ------------------------------------------------------------------------------------ gather/scatter
