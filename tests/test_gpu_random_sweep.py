@@ -23,7 +23,7 @@ def _case(i):
     c["B"] = int(r.integers(1, 4))
     c["H"] = int(r.integers(1, 4))
     c["N"] = int([r.integers(1, 700), 16 * r.integers(1, 40), 64 * r.integers(1, 9)][r.integers(0, 3)])
-    c["T"] = int(r.choice([0, 8, 77, 128, 256]))
+    c["T"] = int(r.choice([0, 8, 77, 128, 256, 300, 1000]))
     c["tv"] = tuple(int(x) for x in r.integers(0, c["T"] + 1, size=c["B"]))
     c["rows"] = bool(r.random() < 0.5)
     c["k"] = int(r.integers(0, c["N"] + 1)) if c["rows"] else 0
