@@ -266,3 +266,64 @@ def test_mask_check_unaligned_buffer(lib, dtype):
             rok, rc = OE.is_row_constant(m, N, T, tv)
             assert ok == rok and _same(host(c).astype(np.float64), rc), (cols, tv, trial)
             assert lib.safe_mask_is_row_constant(view, N, T, tv, flag) == rok, (cols, tv, trial)
+
+
+def test_concurrent_streams_match_sequential(lib):
+    """Two streams running different entry points at once (dense attention and the block products on one,
+    sensitive-row attention, PCSP, the partition and SW-CFG on the other) give the results of running them one
+    after the other, bit for bit: no call keeps state that another call on another stream could disturb."""
+    t = torch()
+    w = syn.scaled(syn.WORKLOADS["srsu_1024"], N=1024, side=32, k=300, H=4)
+    inp = syn.attention_inputs(w)
+    bits = lambda n: t.from_numpy(inp[n + "_bits"].view(np.int16)).view(t.bfloat16).cuda()
+    q, ki, vi, kt, vt = (bits(n) for n in ("q", "k_img", "v_img", "k_txt", "v_txt"))
+    rows = dev(syn.random_rows(w))
+    x = syn.pcsp_logits(w)
+    xd, lid = dev(x["x"]), dev(x["lse_img"])
+    eps = dev(syn.latent_eps(syn.scaled(w, latent=(4, 64, 64))))
+    r = np.random.default_rng(5)
+    D, F = w.H * w.d, 4 * w.H * w.d
+    hx = t.from_numpy(r.standard_normal((w.B, w.N, D)).astype(np.float32)).to(t.bfloat16).cuda()
+    w1 = t.from_numpy((r.standard_normal((F, D)) / np.sqrt(D)).astype(np.float32)).to(t.bfloat16).cuda()
+    w2 = t.from_numpy((r.standard_normal((D, F)) / np.sqrt(F)).astype(np.float32)).to(t.bfloat16).cuda()
+    wq = t.from_numpy((r.standard_normal((3 * D, D)) / np.sqrt(D)).astype(np.float32)).to(t.bfloat16).cuda()
+    ws = t.empty(lib.safe_rows_ffn_workspace_bytes(w.B, w.k, F) // 2, dtype=t.bfloat16, device="cuda")
+    dense_out, rows_out = t.zeros_like(q), t.zeros_like(q)
+    lse = t.empty((w.B, w.H, w.N), dtype=t.float32, device="cuda")
+    cache = t.zeros_like(hx)
+    pq, pk, pv = t.zeros_like(q), t.zeros_like(q), t.zeros_like(q)
+    sc = t.empty(w.N, dtype=t.float32, device="cuda")
+    S = t.empty(w.k, dtype=t.int32, device="cuda")
+    C = t.empty(w.N - w.k, dtype=t.int32, device="cuda")
+    isn = t.empty(w.N, dtype=t.uint8, device="cuda")
+    s01 = t.empty(w.N, dtype=t.float32, device="cuda")
+    cfg = t.empty(eps.shape[1:], dtype=t.float32, device="cuda")
+    outs = (dense_out, lse, cache, pq, pk, pv, rows_out, sc, S, C, isn, s01, cfg)
+
+    def first(stream=None):
+        lib.safe_attn_dense(q, ki, vi, kt, vt, w.tv, dense_out, lse=lse, stream=stream)
+        lib.safe_rows_ffn(hx, rows, w1, None, w2, None, cache, ws, stream=stream)
+        lib.safe_rows_qkv(hx, rows, wq, None, pq, pk, pv, stream=stream)
+
+    def second(stream=None):
+        lib.safe_attn_rows(q, ki, vi, kt, vt, w.tv, rows, rows_out, stream=stream)
+        lib.safe_pcsp_accumulate(xd, lid, w.tv[0], 0, w.tv[0], sc, False, stream=stream)
+        lib.safe_pcsp_partition(sc, w.k, S, C, isn, s01, stream=stream)
+        lib.safe_swcfg_combine(eps, s01, w.side, w.g_ctx, w.g_sens, cfg, stream=stream)
+
+    first()
+    second()
+    t.cuda.synchronize()
+    ref = [o.clone() for o in outs]
+    sa, sb = t.cuda.Stream(), t.cuda.Stream()
+    for rep in range(3):
+        for o in outs:
+            o.zero_()
+        t.cuda.synchronize()
+        with t.cuda.stream(sa):
+            first(sa)
+        with t.cuda.stream(sb):
+            second(sb)
+        t.cuda.synchronize()
+        for i, (o, rf) in enumerate(zip(outs, ref)):
+            assert t.equal(o, rf), (rep, i)
