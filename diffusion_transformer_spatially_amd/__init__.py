@@ -123,6 +123,29 @@ def _stream(stream) -> Optional[int]:
     return s.cuda_stream
 
 
+def _need(t, shape, dtype, name: str, optional: bool = True, at_least: bool = False):
+    """Shape / dtype check of a tensor handed to the library (the C ABI sees only its address, so a tensor of
+    the wrong size would be read or written past its end).  shape: a tuple, or an int for a number of
+    elements (at_least: that many or more); dtype: a torch dtype or a tuple of them."""
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch tensor")
+    if isinstance(shape, int):
+        ok_shape = t.numel() >= shape if at_least else t.numel() == shape
+    else:
+        ok_shape = tuple(t.shape) == tuple(shape)
+    if not ok_shape:
+        want = f"at least {shape} elements" if at_least else f"shape {shape}"
+        raise ValueError(f"{name} must have {want}, got {tuple(t.shape)}")
+    dts = dtype if isinstance(dtype, tuple) else (dtype,)
+    if t.dtype not in dts:
+        raise ValueError(f"{name} must be {' or '.join(str(x) for x in dts)}, got {t.dtype}")
+
+
 def _dtype_code(t) -> int:
     torch = _torch()
     if t.dtype == torch.bfloat16:
@@ -157,6 +180,13 @@ def _desc(q, k_img, v_img, k_txt, v_txt, text_valid_len: Sequence[int], out, sca
             raise ValueError("q_descale / k_descale must be fp32 with B*H entries")
     if k_txt is not None and (tuple(k_txt.shape) != (B, H, T, d) or tuple(v_txt.shape) != (B, H, T, d)):
         raise ValueError("k_txt and v_txt must be [B,H,T,d]")
+    _need(lse, (B, H, N), torch.float32, "lse")
+    _need(xattn_out, (H, N, T), torch.float32, "xattn_out")
+    _need(lse_img_out, (H, N), torch.float32, "lse_img_out")
+    if mask is not None:
+        if mask.dim() != 4 or mask.shape[2] != N:
+            raise ValueError("mask must be [mask_B, mask_H, N, mask_cols]")
+        _need(mask, tuple(mask.shape), (torch.bool, torch.float32), "mask")
     D = safe_attn_desc()
     D.dtype = _dtype_code(q)
     D.B, D.H, D.N, D.T, D.d = B, H, N, T, d
@@ -165,8 +195,6 @@ def _desc(q, k_img, v_img, k_txt, v_txt, text_valid_len: Sequence[int], out, sca
     D.text_valid_len = ctypes.cast(tv, ctypes.POINTER(ctypes.c_int32))
     D.scale = float(scale)
     if mask is not None:
-        if mask.dim() != 4 or mask.shape[2] != N:
-            raise ValueError("mask must be [mask_B, mask_H, N, mask_cols]")
         D.mask = _ptr(mask)
         D.mask_dtype = _dtype_code(mask)
         D.mask_B, D.mask_H, D.mask_cols = mask.shape[0], mask.shape[1], mask.shape[3]
@@ -202,10 +230,18 @@ def safe_attn_rows(q, k_img, v_img, k_txt, v_txt, text_valid_len, rows, out, sca
     return out
 
 
+def _mask_check_args(mask, N, flag_ws, c_out):
+    torch = _torch()
+    if mask.dim() != 4 or mask.shape[2] != N:
+        raise ValueError("mask must be [mask_B, mask_H, N, mask_cols]")
+    _need(mask, tuple(mask.shape), (torch.bool, torch.float32), "mask")
+    _need(flag_ws, 1, torch.int32, "flag_ws", optional=False)
+    _need(c_out, mask.shape[0] * mask.shape[1] * N, torch.float32, "c_out")
+
+
 def safe_mask_is_row_constant(mask, N: int, T: int, text_valid_len, flag_ws, c_out=None, stream=None) -> bool:
     """Exact elision check; synchronous (safe_mask_is_row_constant)."""
-    if mask.dim() != 4:
-        raise ValueError("mask must be [mask_B, mask_H, N, mask_cols]")
+    _mask_check_args(mask, N, flag_ws, c_out)
     B = len(text_valid_len)
     tv = (ctypes.c_int32 * B)(*[int(x) for x in text_valid_len])
     res = ctypes.c_int32(0)
@@ -219,8 +255,7 @@ def safe_mask_is_row_constant(mask, N: int, T: int, text_valid_len, flag_ws, c_o
 def safe_mask_check_launch(mask, N: int, T: int, text_valid_len, flag_ws, c_out=None, stream=None):
     """Exact elision check, launched only: flag_ws (device int32[1]) holds the verdict once the stream
     reaches this point (safe_mask_check_launch)."""
-    if mask.dim() != 4:
-        raise ValueError("mask must be [mask_B, mask_H, N, mask_cols]")
+    _mask_check_args(mask, N, flag_ws, c_out)
     B = len(text_valid_len)
     tv = (ctypes.c_int32 * B)(*[int(x) for x in text_valid_len])
     _check(load().safe_mask_check_launch(
@@ -232,7 +267,11 @@ def safe_mask_check_launch(mask, N: int, T: int, text_valid_len, flag_ws, c_out=
 
 def safe_pcsp_accumulate(x, lse_img, Tv: int, c0: int, c1: int, scores, accumulate: bool, stream=None):
     """scores (+)= per-token text-content attention mass summed over heads (safe_pcsp_accumulate)."""
+    torch = _torch()
     H, N, T = x.shape
+    _need(x, (H, N, T), torch.float32, "x")
+    _need(lse_img, (H, N), torch.float32, "lse_img")
+    _need(scores, N, torch.float32, "scores", optional=False)
     _check(load().safe_pcsp_accumulate(_ptr(x), _ptr(lse_img), H, N, T, Tv, c0, c1, _ptr(scores),
                                        1 if accumulate else 0, _stream(stream)), "safe_pcsp_accumulate")
     return scores
@@ -240,21 +279,41 @@ def safe_pcsp_accumulate(x, lse_img, Tv: int, c0: int, c1: int, scores, accumula
 
 def safe_pcsp_partition(scores, k: int, S, C, is_sens, s01=None, stream=None):
     """Exact top-k partition of the scores (safe_pcsp_partition)."""
+    torch = _torch()
     N = scores.numel()
+    _need(scores, N, torch.float32, "scores")
+    if not 0 <= k <= N:
+        raise ValueError("k must lie in [0, N]")
+    _need(S, k, torch.int32, "S", optional=(k == 0), at_least=True)
+    _need(C, N - k, torch.int32, "C", optional=(k == N), at_least=True)
+    _need(is_sens, N, torch.uint8, "is_sens", optional=False)
+    _need(s01, N, torch.float32, "s01")
     _check(load().safe_pcsp_partition(_ptr(scores), N, k, _ptr(S), _ptr(C), _ptr(is_sens), _ptr(s01),
                                       _stream(stream)), "safe_pcsp_partition")
 
 
 def safe_swcfg_combine(eps, s, side: int, g_ctx: float, g_sens: float, out, stream=None):
     """Per-token guidance combine (safe_swcfg_combine)."""
+    torch = _torch()
     _, C, Hl, Wl = eps.shape
+    _need(eps, (2, C, Hl, Wl), torch.float32, "eps")
+    _need(s, side * side, torch.float32, "s", optional=False)
+    _need(out, (C, Hl, Wl), torch.float32, "out", optional=False)
     _check(load().safe_swcfg_combine(_ptr(eps), _ptr(s), C, Hl, Wl, side, float(g_ctx), float(g_sens), _ptr(out),
                                      _stream(stream)), "safe_swcfg_combine")
     return out
 
 
+def _rows_arg(rows):
+    torch = _torch()
+    if rows.dtype != torch.int32 or rows.dim() != 1:
+        raise ValueError("rows must be a 1-D int32 tensor")
+
+
 def safe_gather_rows(state, rows, packed, stream=None):
     B, H, N, d = state.shape
+    _rows_arg(rows)
+    _need(packed, (B, H, rows.numel(), d), state.dtype, "packed", optional=False)
     _check(load().safe_gather_rows(_ptr(state), _ptr(rows), rows.numel(), B, H, N, d, _dtype_code(state),
                                    _ptr(packed), _stream(stream)), "safe_gather_rows")
     return packed
@@ -262,6 +321,8 @@ def safe_gather_rows(state, rows, packed, stream=None):
 
 def safe_scatter_rows(packed, rows, state, stream=None):
     B, H, N, d = state.shape
+    _rows_arg(rows)
+    _need(packed, (B, H, rows.numel(), d), state.dtype, "packed", optional=False)
     _check(load().safe_scatter_rows(_ptr(packed), _ptr(rows), rows.numel(), B, H, N, d, _dtype_code(state),
                                     _ptr(state), _stream(stream)), "safe_scatter_rows")
     return state
@@ -270,9 +331,12 @@ def safe_scatter_rows(packed, rows, state, stream=None):
 def safe_affinity_accumulate(x, lse_img, Tv: int, sel, scores, accumulate: bool, stream=None):
     """scores (+)= per-token attention mass on the selected text slots, summed over heads
     (safe_affinity_accumulate).  sel: device u8 [T]."""
+    torch = _torch()
     H, N, T = x.shape
-    if sel.numel() != T:
-        raise ValueError("sel must have one entry per text slot")
+    _need(x, (H, N, T), torch.float32, "x")
+    _need(lse_img, (H, N), torch.float32, "lse_img")
+    _need(sel, T, torch.uint8, "sel", optional=False)
+    _need(scores, N, torch.float32, "scores", optional=False)
     _check(load().safe_affinity_accumulate(_ptr(x), _ptr(lse_img), H, N, T, Tv, _ptr(sel), _ptr(scores),
                                            1 if accumulate else 0, _stream(stream)), "safe_affinity_accumulate")
     return scores
@@ -287,9 +351,10 @@ def safe_percentile_count(N: int, pct_bp: int) -> int:
 
 def safe_stepcache_extrapolate(eps_a, eps_b, w: float, out, stream=None):
     """out = eps_b + w (eps_b - eps_a), elementwise over fp32 tensors (safe_stepcache_extrapolate)."""
+    torch = _torch()
     n = out.numel()
-    if eps_a.numel() != n or eps_b.numel() != n:
-        raise ValueError("eps_a, eps_b and out must have the same number of elements")
+    for t, name in ((eps_a, "eps_a"), (eps_b, "eps_b"), (out, "out")):
+        _need(t, n, torch.float32, name, optional=False)
     _check(load().safe_stepcache_extrapolate(_ptr(eps_a), _ptr(eps_b), n, float(w), _ptr(out), _stream(stream)),
            "safe_stepcache_extrapolate")
     return out
@@ -313,11 +378,25 @@ def safe_rows_ffn_workspace_bytes(B: int, k: int, F: int) -> int:
     return int(load().safe_rows_ffn_workspace_bytes(int(B), int(k), int(F)))
 
 
+def _ffn_args(x, rows, w1, b1, w2, b2, cache):
+    torch = _torch()
+    B, N, D = x.shape
+    F = w1.shape[0]
+    _rows_arg(rows)
+    _need(x, (B, N, D), torch.bfloat16, "x")
+    _need(w1, (F, D), torch.bfloat16, "w1")
+    _need(w2, (D, F), torch.bfloat16, "w2", optional=False)
+    _need(b1, F, torch.float32, "b1")
+    _need(b2, D, torch.float32, "b2")
+    _need(cache, (B, N, D), torch.bfloat16, "cache", optional=False)
+
+
 def safe_rows_ffn(x, rows, w1, b1, w2, b2, cache, ws, stream=None):
     """cache[:, rows] = FFN(x[:, rows]) (safe_rows_ffn).  x, cache: bf16 [B, N, D]; w1 [F, D], w2 [D, F]
     bf16; b1 / b2 fp32 or None; ws: device workspace tensor of at least safe_rows_ffn_workspace_bytes."""
     B, N, D = x.shape
     F = w1.shape[0]
+    _ffn_args(x, rows, w1, b1, w2, b2, cache)
     _check(load().safe_rows_ffn(_ptr(x), _ptr(rows), rows.numel(), B, N, D, F, _ptr(w1), _ptr(b1), _ptr(w2),
                                 _ptr(b2), _ptr(cache), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
            "safe_rows_ffn")
@@ -329,6 +408,7 @@ def safe_rows_ffn_noalloc(x, rows, w1, b1, w2, b2, cache, stream=None):
     (safe_rows_ffn_noalloc; at most safe_rows_ffn_noalloc_max_bytes() bytes)."""
     B, N, D = x.shape
     F = w1.shape[0]
+    _ffn_args(x, rows, w1, b1, w2, b2, cache)
     _check(load().safe_rows_ffn_noalloc(_ptr(x), _ptr(rows), rows.numel(), B, N, D, F, _ptr(w1), _ptr(b1), _ptr(w2),
                                         _ptr(b2), _ptr(cache), _stream(stream)), "safe_rows_ffn_noalloc")
     return cache
@@ -340,8 +420,17 @@ def safe_rows_ffn_noalloc_max_bytes() -> int:
 
 def safe_rows_qkv(x, rows, wqkv, bqkv, q, k_cache, v_cache, stream=None):
     """Rows S of q / k_cache / v_cache [B, H, N, d] from the projection of x[:, rows] (safe_rows_qkv)."""
-    B, N, _ = x.shape
+    torch = _torch()
+    B, N, D = x.shape
     _, H, _, d = q.shape
+    _rows_arg(rows)
+    _need(x, (B, N, D), torch.bfloat16, "x")
+    if H * d != D:
+        raise ValueError("q must be [B, H, N, d] with H * d equal to the hidden width of x")
+    _need(wqkv, (3 * D, D), torch.bfloat16, "wqkv", optional=False)
+    _need(bqkv, 3 * D, torch.float32, "bqkv")
+    for t, name in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _need(t, (B, H, N, d), torch.bfloat16, name, optional=False)
     _check(load().safe_rows_qkv(_ptr(x), _ptr(rows), rows.numel(), B, N, H, d, _ptr(wqkv), _ptr(bqkv), _ptr(q),
                                 _ptr(k_cache), _ptr(v_cache), _stream(stream)), "safe_rows_qkv")
     return q, k_cache, v_cache

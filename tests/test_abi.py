@@ -313,3 +313,58 @@ def test_mask_scan_reads_stay_inside_the_mask_buffer(tmp_path):
                    capture_output=True)
     out = subprocess.run([str(exe)], capture_output=True, text=True)
     assert out.returncode == 0 and out.stdout.startswith("ok"), out.stdout
+
+
+# ------------------------------------------------------------------ binding: sizes of the tensors it hands over
+def test_binding_rejects_mis_sized_tensors_before_any_call():
+    """The C ABI sees only addresses, so the binding checks every tensor's shape and dtype first: a wrong one
+    raises a ValueError naming it, before anything reaches the library (host tensors suffice: the checks run
+    before the device check)."""
+    import torch
+    bf, f32, i32, u8 = torch.bfloat16, torch.float32, torch.int32, torch.uint8
+    z = lambda *s, dt=bf: torch.zeros(s, dtype=dt)
+    B, H, N, T, d = 2, 3, 64, 16, 64
+    q, kt = z(B, H, N, d), z(B, H, T, d)
+    with pytest.raises(ValueError, match="lse"):
+        dts.safe_attn_dense(q, q, q, kt, kt, (4, 5), q, lse=z(B, H, N - 1, dt=f32))
+    with pytest.raises(ValueError, match="xattn_out"):
+        dts.safe_attn_dense(q, q, q, kt, kt, (4, 5), q, xattn_out=z(H, N, T + 1, dt=f32))
+    with pytest.raises(ValueError, match="lse_img_out"):
+        dts.safe_attn_dense(q, q, q, kt, kt, (4, 5), q, lse_img_out=z(H, N, dt=bf))
+    with pytest.raises(ValueError, match="mask"):
+        dts.safe_attn_dense(q, q, q, kt, kt, (4, 5), q, mask=z(1, 1, N, N, dt=u8))
+    with pytest.raises(ValueError, match="c_out"):
+        dts.safe_mask_is_row_constant(z(1, 1, N, N, dt=torch.bool), N, T, (4, 5), z(1, dt=i32), c_out=z(N - 1, dt=f32))
+    with pytest.raises(ValueError, match="flag_ws"):
+        dts.safe_mask_check_launch(z(1, 1, N, N, dt=torch.bool), N, T, (4, 5), z(1, dt=f32))
+    with pytest.raises(ValueError, match="scores"):
+        dts.safe_pcsp_accumulate(z(H, N, T, dt=f32), None, 10, 0, 10, z(N + 1, dt=f32), False)
+    with pytest.raises(ValueError, match="lse_img"):
+        dts.safe_pcsp_accumulate(z(H, N, T, dt=f32), z(H, N - 2, dt=f32), 10, 0, 10, z(N, dt=f32), False)
+    with pytest.raises(ValueError, match="S must"):
+        dts.safe_pcsp_partition(z(N, dt=f32), 10, z(9, dt=i32), z(N - 10, dt=i32), z(N, dt=u8))
+    with pytest.raises(ValueError, match="is_sens"):
+        dts.safe_pcsp_partition(z(N, dt=f32), 10, z(10, dt=i32), z(N - 10, dt=i32), z(N, dt=torch.bool))
+    with pytest.raises(ValueError, match="out"):
+        dts.safe_swcfg_combine(z(2, 4, 16, 16, dt=f32), z(64, dt=f32), 8, 1.0, 2.0, z(4, 16, 8, dt=f32))
+    rows = torch.arange(5, dtype=i32)
+    with pytest.raises(ValueError, match="packed"):
+        dts.safe_gather_rows(q, rows, z(B, H, 4, d))
+    with pytest.raises(ValueError, match="rows"):
+        dts.safe_scatter_rows(z(B, H, 5, d), rows.long(), q)
+    with pytest.raises(ValueError, match="sel"):
+        dts.safe_affinity_accumulate(z(H, N, T, dt=f32), None, 10, z(T - 1, dt=u8), z(N, dt=f32), False)
+    with pytest.raises(ValueError, match="eps_b"):
+        dts.safe_stepcache_extrapolate(z(100, dt=f32), z(100, dt=torch.float16), 0.5, z(100, dt=f32))
+    D, F = H * d, 4 * H * d
+    x = z(B, N, D)
+    with pytest.raises(ValueError, match="w2"):
+        dts.safe_rows_ffn(x, rows, z(F, D), None, z(D, F - 8), None, z(B, N, D), z(10))
+    with pytest.raises(ValueError, match="cache"):
+        dts.safe_rows_ffn_noalloc(x, rows, z(F, D), None, z(D, F), None, z(B, N, D, dt=f32))
+    with pytest.raises(ValueError, match="b1"):
+        dts.safe_rows_ffn(x, rows, z(F, D), z(F - 1, dt=f32), z(D, F), None, z(B, N, D), z(10))
+    with pytest.raises(ValueError, match="hidden width"):
+        dts.safe_rows_qkv(x, rows, z(3 * D, D), None, z(B, H + 1, N, d), z(B, H + 1, N, d), z(B, H + 1, N, d))
+    with pytest.raises(ValueError, match="v_cache"):
+        dts.safe_rows_qkv(x, rows, z(3 * D, D), None, z(B, H, N, d), z(B, H, N, d), z(B, H, N - 1, d))
