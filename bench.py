@@ -53,6 +53,8 @@ def parse():
                     help="run only the sensitive-row block products (FFN, QKV) and print them; for profiling them")
     ap.add_argument("--trajectory-only", action="store_true",
                     help="run only the 3072^2 trajectory line and print it; for profiling it")
+    ap.add_argument("--variants-only", action="store_true",
+                    help="run only the head-dim-128 and fp8 attention lines (1024^2) and print them; for profiling them")
     return ap.parse_args()
 
 
@@ -82,6 +84,15 @@ def main():
         return
     if args.trajectory_only:
         print(json.dumps({"trajectory_3072": trajectory_3072(dts, torch, np, syn, dev)}), flush=True)
+        return
+    if args.variants_only:
+        out = {"attention_d128_1024": attention_large(dts, torch, syn, dev, syn.WORKLOADS["dense_1024_d128"],
+                                                      torch.cuda.current_stream(), reps=10)[-1],
+               "attention_fp8_1024": attention_fp8(dts, torch, syn, dev, syn.WORKLOADS["srsu_1024"]),
+               "attention_fp8_d128_1024": attention_fp8(dts, torch, syn, dev, syn.WORKLOADS["dense_1024_d128"])}
+        if args.copy_calibration:
+            out["copy_calibration_bytes"] = copy_calibration(torch, dev)
+        print(json.dumps(out), flush=True)
         return
     if args.block_only:
         out = {"srsu_block": srsu_block(dts, torch, np, syn, dev)}
