@@ -910,6 +910,31 @@ def cpu_baseline(w, inp, rows_S, budget_s: float, large: bool):
     fr, er, dr = _oracle_heads(w, inp, np.asarray(rows_S, dtype=np.int64), budget_s / 3)
     legs["rows_1024"] = {"value": fr / er / 1e12, "unit": "TFLOP/s", "s": er,
                          "sample": f"sensitive rows (|S| = {len(rows_S)}) of {dr} of the {w.B * w.H} heads"}
+    # head dim 128 (n4): the same dense attention on its own inputs, heads in order within a third of the budget
+    w128 = syn.WORKLOADS["dense_1024_d128"]
+    f128, e128, d128 = _oracle_heads(w128, syn.attention_inputs(w128), None, budget_s / 3)
+    legs["dense_1024_d128"] = {"value": f128 / e128 / 1e12, "unit": "TFLOP/s", "s": e128,
+                               "sample": f"dense_1024_d128: all {w128.N} query rows of {d128} of the {w128.B * w128.H} heads"}
+    # the sensitive-row block products (n3): FFN and QKV of every 16th row of S, scaled to the whole launch
+    from oracle import srsu_block as SB
+    x = syn.hidden_states(w)
+    bw = syn.block_weights(w)
+    sub = np.asarray(rows_S, dtype=np.int64)[::16]
+    D, F = w.H * w.d, bw["w1"].shape[0]
+    t0 = time.perf_counter()
+    SB.rows_ffn(x, sub, bw["w1"], bw["b1"], bw["w2"], bw["b2"], np.zeros_like(x))
+    e_ffn = time.perf_counter() - t0
+    zq = np.zeros((w.B, w.H, w.N, w.d), dtype=np.float32)
+    t0 = time.perf_counter()
+    SB.rows_qkv(x, sub, bw["wqkv"], bw["bqkv"], zq, zq, zq, w.H, w.d)
+    e_qkv = time.perf_counter() - t0
+    f_blk = w.B * len(sub) * (4.0 * D * F + 6.0 * D * D)
+    legs["block_1024_rows_1_in_16"] = {
+        "value": f_blk / (e_ffn + e_qkv) / 1e12, "unit": "TFLOP/s", "sample_s": e_ffn + e_qkv,
+        "scaled_full_launch_s": (e_ffn + e_qkv) * len(rows_S) / len(sub),
+        "sample": f"srsu_1024 block products (FFN D->F->D with GELU, QKV) of every 16th row of S ({len(sub)} of "
+                  f"{len(rows_S)} rows per batch entry); the scaled figure is the time the full FFN + QKV would take"}
+    del x, zq
     if large:
         for name in ("srsu_2560", "traj_3072"):
             wl = syn.WORKLOADS[name]
