@@ -16,10 +16,12 @@ CFG_REL = 1e-5
 # max-abs bound cannot fail, and one zeroed row-head among 59k adds only ~4e-3 to the relative L2).
 # Bounds from the measured distribution of the worst row over every parity case on MI355X (bf16: 121
 # assertions, worst 5.2e-3 on the logit-std-3 stress rows, 2.8-3.3e-3 on the full-size 1024^2 / 2560^2 /
-# 3072^2 launches, 2.5-2.6e-3 on the block products; fp32: worst 8.9e-7), about twice the worst case.
+# 3072^2 launches, 2.5-2.6e-3 on the block products), about twice the worst case.  fp32 rows take the fp32
+# figure above (about 1e-6 per output from fp32 accumulation, with the 10x margin): a wider seeded sweep put a
+# row with about 1000 keys, logits four times the workload's and an fp32 mask at 2.2e-6.
 # A row with a missing key tile, a wrong row index or a zero output lands between 1e-1 and 1.
 BF16_ROW_REL = 1e-2
-F32_ROW_REL = 2e-6
+F32_ROW_REL = 1e-5
 ROW_STATS = []  # (what, dtype, worst row, rel-L2) of every assert_close call, for the run's summary
 
 
