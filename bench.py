@@ -442,31 +442,35 @@ def gpu_busy(torch, ms=1.0):
 def cold_launch_ms(torch, fn, flush, reps=10):
     """Duration (ms) of one launch that finds none of its data in L2 or the 256 MB MALL: before each launch
     a 1 GiB write and then a 1 GiB read sweep both caches (the read leaves them holding clean lines, so the
-    timed launch does not pay for writing back the sweep's dirty ones); a HIP event pair brackets the
-    launch alone.  The median of an event pair bracketing nothing after the same sweep (the event packets'
-    own cost, about 2-4 us) is subtracted.  Returns (corrected, raw, empty-pair) medians."""
+    timed launch does not pay for writing back the sweep's dirty ones).  Differential timing: one HIP event
+    pair brackets a short spin kernel followed by the launch, another pair (after the same sweep) the spin
+    alone; the difference of the medians is the launch's duration plus one kernel-to-kernel dispatch gap, so
+    the event packets' own cost and the spin cancel.  Returns (duration, raw, spin-only) medians."""
     import statistics
     fn()
     torch.cuda.synchronize()
-    raw, empty = [], []
+    gpu_busy(torch, 0.01)  # calibrates the spin rate outside the timed pairs
+    spin = max(int(0.01 * _SLEEP_CYCLES_PER_MS[0]), 1)  # about 10 us
+    raw, anchor = [], []
     for r in range(2 * reps):
         flush.fill_(float(r))
         flush.sum()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
+        torch.cuda._sleep(spin)
         if r % 2 == 0:
             fn()
         e1.record()
         torch.cuda.synchronize()
-        (raw if r % 2 == 0 else empty).append(e0.elapsed_time(e1))
-    raw_ms, empty_ms = statistics.median(raw), statistics.median(empty)
-    return max(raw_ms - empty_ms, 1e-6), raw_ms, empty_ms
+        (raw if r % 2 == 0 else anchor).append(e0.elapsed_time(e1))
+    raw_ms, anchor_ms = statistics.median(raw), statistics.median(anchor)
+    return max(raw_ms - anchor_ms, 1e-6), raw_ms, anchor_ms
 
 
 def cold_line(hbm, bytes_, timed):
-    ms, raw, empty = timed
+    ms, raw, anchor = timed
     line = hbm(bytes_, ms)
-    line.update({"ms_raw": raw, "event_pair_ms": empty})
+    line.update({"ms_raw": raw, "spin_only_ms": anchor})
     return line
 
 
@@ -573,8 +577,9 @@ def hbm_stages(dts, torch, np, syn, dev, hbm):
                3072^2 shape in one launch where one instance is smaller), alternating over two such buffer
                sets, 8 back-to-back launches between one event pair: every launch reads and writes HBM;
       cold:    one launch of the single-instance 2560^2 / 3072^2 shape after a 1 GiB write + 1 GiB read sweep
-               of L2 and the MALL, with its own event pair minus the median of an empty pair after the same
-               sweep (about 2 us of event uncertainty remains);
+               of L2 and the MALL, timed differentially: an event pair around a short spin and the launch,
+               minus the median of a pair around the spin alone after the same sweep (the launch plus one
+               dispatch gap);
       cache_resident: 20 back-to-back launches of the single-instance shape between one event pair, whose
                working set stays in the MALL from launch to launch -- a cache figure, not an HBM one.
     frac_hbm is reported for the first two modes only."""
@@ -676,7 +681,8 @@ def hbm_stages(dts, torch, np, syn, dev, hbm):
                       "[2,C,384,384] / [C,384,384] fp32 (x10: C=160; single: C=16); mask [1,1,25600,25600]",
             "note": "batched: 8 back-to-back launches alternating over two buffer sets larger than the MALL, one "
                     "event pair; cold: one launch after a 1 GiB write + 1 GiB read "
-                    "sweep, its own event pair minus the empty pair (ms_raw, event_pair_ms); the kernel trace of "
+                    "sweep, timed as (spin + launch) minus (spin alone) between event pairs (ms_raw, spin_only_ms): the "
+                    "launch plus one dispatch gap; the kernel trace of "
                     "the same launches is in profiles/hbm_stages_large.md"}
 
 
@@ -801,7 +807,8 @@ def next_rows(dts, torch, np, syn, dev, hbm, large: bool):
             "cold": cold_line(hbm, 12.0 * n, cold_launch_ms(torch, ex, sweep)),
             "workload": f"{name}: prediction [{C_},{Hl},{Wl}] fp32, w = 1/3"}
     out["note"] = ("cache_resident: 20 back-to-back launches between one event pair; cold: each launch after a 1 GiB write "
-                   "and a 1 GiB read, its own event pair minus an empty pair; mask_ms: affinity + partition")
+                   "and a 1 GiB read, timed as (spin + launch) minus (spin alone) between event pairs; mask_ms: "
+                   "affinity + partition")
     del sweep
     return out
 
